@@ -1,0 +1,256 @@
+/*
+ * da.h -- decode attention over a large KV cache on AMD Instinct MI355X
+ * (gfx950).  C ABI of libda.so.
+ *
+ * What is computed
+ * ----------------
+ * One decode step of attention: for each batch row b and query head j, with
+ * KV head h = floor(j / G), G = n_q_heads / n_kv_heads (contiguous groups),
+ *
+ *     o[b][j] = sum_i softmax_i(scale * q[b][j] . k[b][h][i]) * v[b][h][i]
+ *
+ * over the cached tokens i (HeadInfer, section "核心 idea", per-head equation;
+ * TinyServe, section "方法细节", standard decode step).  Variants:
+ *
+ *   - da_decode_attention        all N cached tokens (dense).
+ *   - da_build_page_meta,        TinyServe's query-aware page selection:
+ *     da_select_pages,           per-page per-channel key min/max, the
+ *     da_decode_attention_paged  directional bound score, top-K pages, and
+ *                                attention over the kept pages only
+ *                                (TinyServe, section "方法细节", Algorithm 1).
+ *   - da_quantize_kv4,           FlexGen's 4-bit min/max quantization in
+ *     da_dequantize_kv4,         groups of 64 channels, and attention that
+ *     da_decode_attention_kv4    dequantizes while loading (FlexGen digest,
+ *                                section "方法细节").
+ *   - da_stream_*                HeadInfer's head-wise offload: the cache of
+ *                                each (layer, KV head) lives in pinned host
+ *                                memory and is copied into one of two
+ *                                ping-pong device buffers while attention runs
+ *                                on the other (HeadInfer, section "方法：
+ *                                ping-pong memory 与异步重叠").
+ *
+ * Conventions (all entry points)
+ * ------------------------------
+ *   - Memory: every pointer is owned by the caller.  The library allocates no
+ *     device or host memory; the split-K workspace is passed in, sized by the
+ *     matching *_workspace() call.  da_stream_create allocates only hipEvents.
+ *   - Device pointers must be 16-byte aligned; arrays are dense (row-major,
+ *     last index fastest) in the layouts given below.
+ *   - dtypes: q and K/V are fp32, fp16 or bf16 (DA_F32/DA_F16/DA_BF16); the
+ *     output is always fp32.  q must be fp32 or the KV dtype.
+ *   - Errors: every argument is checked on the host before anything is
+ *     enqueued.  On an error nothing is launched, a da_status is returned and
+ *     da_last_error() holds a message (thread-local).  DA_OK means enqueued:
+ *     the work is asynchronous on the given stream, and device faults surface
+ *     at the caller's next synchronisation.
+ *   - Streams: hipStream_t values (0 = the null stream).  Calls on one stream
+ *     run in order; calls that share a workspace must not overlap.
+ *   - Reentrancy: entry points keep no state between calls except
+ *     da_stream_ctx objects, which must not be shared by concurrent calls.
+ */
+#ifndef DA_H
+#define DA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef DA_HIP_STREAM_DEFINED
+#define DA_HIP_STREAM_DEFINED
+typedef struct ihipStream_t *hipStream_t;
+#endif
+
+#define DA_VERSION_MAJOR 0
+#define DA_VERSION_MINOR 1
+#define DA_VERSION_PATCH 0
+
+typedef enum da_status {
+    DA_OK = 0,
+    DA_E_INVALID = 1,      /* null/misaligned pointer, bad size or index  */
+    DA_E_UNSUPPORTED = 2,  /* valid but not built: head_dim, dtype, G ... */
+    DA_E_WORKSPACE = 3,    /* ws_bytes smaller than the *_workspace size  */
+    DA_E_NOT_PINNED = 4,   /* host pointer not in page-locked memory      */
+    DA_E_HIP = 5           /* a HIP runtime call failed (see last_error)  */
+} da_status;
+
+typedef enum da_dtype { DA_F32 = 0, DA_F16 = 1, DA_BF16 = 2 } da_dtype;
+
+/* Shape of one decode-attention call.
+ *   batch >= 1; n_kv_heads >= 1; n_q_heads = G * n_kv_heads with
+ *   G in {1, 2, 4, 8}; head_dim in {64, 128}; n_ctx >= 1 tokens per (batch
+ *   row, KV head); scale > 0 (normally 1/sqrt(head_dim)); q_dtype is DA_F32
+ *   or kv_dtype; split_tokens is the number of tokens (dense) or selected
+ *   token positions (paged) one workgroup reduces before the cross-split
+ *   merge: 0 selects the default (512); otherwise a multiple of 16 in
+ *   [16, 65536].  It depends only on this field, never on batch or heads, so
+ *   a call over one head and a call over all heads give bitwise-equal
+ *   results for that head. */
+typedef struct da_attn_shape {
+    int32_t batch;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int64_t n_ctx;
+    float   scale;
+    int32_t q_dtype;       /* da_dtype */
+    int32_t kv_dtype;      /* da_dtype */
+    int32_t split_tokens;
+} da_attn_shape;
+
+/* (DA_VERSION_MAJOR << 16) | (DA_VERSION_MINOR << 8) | DA_VERSION_PATCH */
+int da_version(void);
+const char *da_status_string(int status);
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *da_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Dense decode attention (HeadInfer per-head equation; TinyServe Attn(q,K,V))
+ *   q  [batch][n_q_heads][head_dim]          q_dtype, device
+ *   k  [batch][n_kv_heads][n_ctx][head_dim]  kv_dtype, device
+ *   v  same layout as k
+ *   o  [batch][n_q_heads][head_dim]          fp32, device (written)
+ *   ws >= da_decode_attention_workspace(s) bytes, device scratch holding the
+ *      per-split (max, sum, unnormalised output) partials; contents on entry
+ *      are ignored.
+ * Two kernels on `stream`: a split-K partial pass and a cross-split merge.
+ * ------------------------------------------------------------------------ */
+size_t da_decode_attention_workspace(const da_attn_shape *s);
+da_status da_decode_attention(const da_attn_shape *s, const void *q,
+                              const void *k, const void *v, float *o,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Page metadata (TinyServe phi(K_j) = (m_j, M_j)): per page of page_size
+ * tokens, the per-channel minimum and maximum of the keys.  Page j covers
+ * tokens [j*page_size, min((j+1)*page_size, n_ctx)); P = ceil(n_ctx/page_size).
+ *   k     [batch][n_kv_heads][n_ctx][head_dim] kv_dtype, device
+ *   kmin, kmax [batch][n_kv_heads][P][head_dim] kv_dtype, device (written)
+ * page_size: a power of two in [1, 1024].  Exact (no rounding).
+ * ------------------------------------------------------------------------ */
+da_status da_build_page_meta(const da_attn_shape *s, int32_t page_size,
+                             const void *k, void *kmin, void *kmax,
+                             hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Query-aware page selection (TinyServe relevance score and S_t = TopK):
+ *   r_j = sum_d (q_d * kmax[j][d] if q_d >= 0 else q_d * kmin[j][d])
+ * accumulated in fp32 (products of fp16/bf16 values are exact in fp32), then
+ * the top_k largest r_j per (batch row, head); equal scores keep the lower
+ * page index; the kept indices are written in ascending order.
+ *   q          [batch][n_q_heads][head_dim]   q_dtype, device
+ *   kmin, kmax as written by da_build_page_meta
+ *   page_idx   [batch][n_q_heads][top_k] int32, device (written)
+ *   page_score [batch][n_q_heads][P] fp32, device, or NULL (written if given)
+ * Requires n_q_heads == n_kv_heads (one selection per head), 1 <= top_k <= P,
+ * P <= 8192, page_size a power of two in [1, 1024].
+ * ------------------------------------------------------------------------ */
+da_status da_select_pages(const da_attn_shape *s, int32_t page_size,
+                          int32_t top_k, const void *q, const void *kmin,
+                          const void *kmax, int32_t *page_idx,
+                          float *page_score, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse attention over the selected pages only (TinyServe SparseAttn):
+ * softmax normalised over the tokens of the listed pages; positions at or
+ * beyond n_ctx in a partial last page are skipped, and so is any listed page
+ * index outside [0, P).
+ *   page_idx [batch][n_q_heads][top_k] int32, device
+ *   q, k, v, o as for da_decode_attention (n_q_heads == n_kv_heads)
+ *   ws >= da_decode_attention_paged_workspace(s, page_size, top_k) bytes
+ * ------------------------------------------------------------------------ */
+size_t da_decode_attention_paged_workspace(const da_attn_shape *s,
+                                           int32_t page_size, int32_t top_k);
+da_status da_decode_attention_paged(const da_attn_shape *s, int32_t page_size,
+                                    int32_t top_k, const int32_t *page_idx,
+                                    const void *q, const void *k, const void *v,
+                                    float *o, void *ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * uint4 group quantization (FlexGen 4-bit, groups of 64 along the hidden
+ * dimension).  For each row and each group of 64 contiguous fp16 values:
+ *   min = minimum, max = maximum,
+ *   scale = fp16((max - min) / 15)     exact quotient rounded once (RNE),
+ *   code  = clamp(round_half_even((x - min) / scale), 0, 15), 0 if scale == 0,
+ * two codes per byte, even channel in the low nibble.  Bit-exact.
+ *   x      [n_rows][row_len] fp16, device (row_len a multiple of 64)
+ *   codes  [n_rows][row_len/2] uint8, device (written)
+ *   gmin, gscale [n_rows][row_len/64] fp16, device (written)
+ * da_dequantize_kv4 writes x_hat = fp16(min + code * scale), rounded once.
+ * ------------------------------------------------------------------------ */
+da_status da_quantize_kv4(int64_t n_rows, int32_t row_len, const void *x,
+                          uint8_t *codes, void *gmin, void *gscale,
+                          hipStream_t stream);
+da_status da_dequantize_kv4(int64_t n_rows, int32_t row_len,
+                            const uint8_t *codes, const void *gmin,
+                            const void *gscale, void *x, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Decode attention over a uint4 cache, dequantizing while loading.
+ * The dequantization is folded into the fp32 arithmetic
+ * (q . (min + c*scale) = min * sum(q) + scale * sum(q*c) per group, and the
+ * same for the value side), which differs from rounding each dequantized
+ * element to fp16 first by at most half an fp16 ulp per element.
+ *   q                 [batch][n_q_heads][head_dim]  fp16 or fp32, device
+ *   k_codes, v_codes  [batch][n_kv_heads][n_ctx][head_dim/2] uint8, device
+ *   k_min, k_scale, v_min, v_scale
+ *                     [batch][n_kv_heads][n_ctx][head_dim/64] fp16, device
+ *   o                 [batch][n_q_heads][head_dim] fp32, device (written)
+ * head_dim must be 128; kv_dtype is ignored; ws as reported.
+ * ------------------------------------------------------------------------ */
+size_t da_decode_attention_kv4_workspace(const da_attn_shape *s);
+da_status da_decode_attention_kv4(const da_attn_shape *s, const void *q,
+                                  const uint8_t *k_codes, const void *k_min,
+                                  const void *k_scale, const uint8_t *v_codes,
+                                  const void *v_min, const void *v_scale,
+                                  float *o, void *ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Head-wise streamed decode (HeadInfer).
+ * `per_layer` describes one layer (batch, heads, head_dim, n_ctx, dtypes).
+ * heads_per_chunk (1, 2, 4 or 8, dividing n_kv_heads) KV heads are copied
+ * per transfer (HeadInfer's adaptive head grouping; n_kv_heads = layer-wise).
+ *
+ * da_headwise_buffer_bytes: bytes of ONE ping-pong buffer, i.e. K and V of
+ *   heads_per_chunk heads: 2 * heads_per_chunk * batch * n_ctx * head_dim *
+ *   sizeof(kv).  Pure host arithmetic.
+ * da_stream_headwise: for each layer l and chunk c (in order), on `copy`:
+ *   wait until the buffer's previous attention finished, copy K then V of
+ *   the chunk's heads from pinned host memory into buffer (chunk index % 2);
+ *   on `compute`: wait for the copy, run attention for those heads.
+ *   k_host[l * n_kv_heads + h], v_host[...]: [batch][n_ctx][head_dim]
+ *     kv_dtype in page-locked host memory (hipHostMalloc), one per
+ *     (layer, KV head);
+ *   buf0, buf1: device buffers of da_stream_buffer_bytes each;
+ *   q [n_layers][batch][n_q_heads][head_dim] q_dtype, device;
+ *   o [n_layers][batch][n_q_heads][head_dim] fp32, device (written);
+ *   ws >= da_stream_workspace(ctx) bytes, device;
+ *   compute != copy.  The output is complete when `compute` drains.
+ * Each head's result is bitwise equal to da_decode_attention on the same
+ * data with the same split_tokens.
+ * ------------------------------------------------------------------------ */
+typedef struct da_stream_ctx da_stream_ctx;
+
+size_t da_headwise_buffer_bytes(const da_attn_shape *per_layer,
+                                int32_t heads_per_chunk);
+da_status da_stream_create(const da_attn_shape *per_layer,
+                           int32_t heads_per_chunk, da_stream_ctx **out);
+size_t da_stream_buffer_bytes(const da_stream_ctx *c);
+size_t da_stream_workspace(const da_stream_ctx *c);
+da_status da_stream_headwise(da_stream_ctx *c, int32_t n_layers,
+                             const void *const *k_host,
+                             const void *const *v_host, void *buf0, void *buf1,
+                             const void *q, float *o, void *ws,
+                             size_t ws_bytes, hipStream_t compute,
+                             hipStream_t copy);
+void da_stream_destroy(da_stream_ctx *c);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DA_H */

@@ -1,0 +1,278 @@
+"""Python binding of libda.so: the same entry points, taking torch tensors.
+
+Argument marshalling only: shapes and dtypes are read from the tensors, the
+output and the workspace are allocated with torch (device memory plumbing),
+and the raw pointers plus the current HIP stream go to the C ABI.  Every step
+of the computation runs in the library's kernels; if libda.so is missing the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from ._lib import (DA_BF16, DA_F16, DA_F32, DaAttnShape, check, load)
+
+_DT = {torch.float32: DA_F32, torch.float16: DA_F16, torch.bfloat16: DA_BF16}
+
+
+def _vp(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous GPU tensors")
+
+
+def attn_shape(batch, n_q_heads, n_kv_heads, head_dim, n_ctx, scale=None, q_dtype=DA_F32,
+               kv_dtype=DA_BF16, split_tokens=0) -> DaAttnShape:
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return DaAttnShape(batch, n_q_heads, n_kv_heads, head_dim, n_ctx, scale, q_dtype, kv_dtype,
+                       split_tokens)
+
+
+def _dense_shape(q, k, scale, split_tokens, kv_dtype=None):
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [B][Hq][D] and k [B][Hkv][N][D]")
+    B, Hq, D = q.shape
+    Bk, Hkv, N, Dk = k.shape
+    if Bk != B or (kv_dtype is None and Dk != D):
+        raise ValueError("q and k disagree on batch or head_dim")
+    kvd = _DT[k.dtype] if kv_dtype is None else kv_dtype
+    return attn_shape(B, Hq, Hkv, D, N, scale, _DT[q.dtype], kvd, split_tokens)
+
+
+def _expect(t, shape, dtype, name):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name}: expected {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+
+
+def _ws(nbytes: int, device):
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+def da_decode_attention(q, k, v, scale=None, split_tokens=0, out=None, ws=None, stream=None):
+    """o[b, j] = softmax(scale q[b,j] . K[b, j//G]^T) V[b, j//G]; fp32 [B][Hq][D]."""
+    lib = load()
+    _dev(q, k, v, out, ws)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must have the same shape and dtype")
+    s = _dense_shape(q, k, scale, split_tokens)
+    need = lib.da_decode_attention_workspace(ctypes.byref(s))
+    _expect(out, q.shape, torch.float32, "out")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = _ws(need, q.device)
+    check(lib.da_decode_attention(ctypes.byref(s), _vp(q), _vp(k), _vp(v), _vp(out), _vp(ws),
+                                  ws.numel(), _stream(stream)))
+    return out
+
+
+def da_build_page_meta(k, page_size, kmin=None, kmax=None, stream=None):
+    """Per-page per-channel key min and max: ([B][H][P][D], [B][H][P][D])."""
+    lib = load()
+    _dev(k, kmin, kmax)
+    B, H, N, D = k.shape
+    P = -(-N // page_size)
+    s = attn_shape(B, H, H, D, N, None, _DT[k.dtype], _DT[k.dtype])
+    _expect(kmin, (B, H, P, D), k.dtype, "kmin")
+    _expect(kmax, (B, H, P, D), k.dtype, "kmax")
+    if kmin is None:
+        kmin = torch.empty((B, H, P, D), dtype=k.dtype, device=k.device)
+    if kmax is None:
+        kmax = torch.empty((B, H, P, D), dtype=k.dtype, device=k.device)
+    check(lib.da_build_page_meta(ctypes.byref(s), page_size, _vp(k), _vp(kmin), _vp(kmax),
+                                 _stream(stream)))
+    return kmin, kmax
+
+
+def da_select_pages(q, kmin, kmax, page_size, top_k, n_ctx, page_idx=None, page_score=None,
+                    want_scores=False, stream=None):
+    """Top-k pages by the bound score per (b, h), ascending int32 [B][H][top_k]."""
+    lib = load()
+    _dev(q, kmin, kmax, page_idx, page_score)
+    B, H, D = q.shape
+    P = -(-n_ctx // page_size)
+    _expect(kmin, (B, H, P, D), kmin.dtype, "kmin")
+    _expect(kmax, (B, H, P, D), kmin.dtype, "kmax")
+    _expect(page_idx, (B, H, top_k), torch.int32, "page_idx")
+    _expect(page_score, (B, H, P), torch.float32, "page_score")
+    s = attn_shape(B, H, H, D, n_ctx, None, _DT[q.dtype], _DT[kmin.dtype])
+    if page_idx is None:
+        page_idx = torch.empty((B, H, top_k), dtype=torch.int32, device=q.device)
+    if want_scores and page_score is None:
+        page_score = torch.empty((B, H, P), dtype=torch.float32, device=q.device)
+    check(lib.da_select_pages(ctypes.byref(s), page_size, top_k, _vp(q), _vp(kmin), _vp(kmax),
+                              _vp(page_idx), _vp(page_score), _stream(stream)))
+    return (page_idx, page_score) if want_scores else page_idx
+
+
+def da_decode_attention_paged(q, k, v, page_idx, page_size, scale=None, split_tokens=0, out=None,
+                              ws=None, stream=None):
+    """Attention over the tokens of the listed pages only; fp32 [B][H][D]."""
+    lib = load()
+    _dev(q, k, v, page_idx, out, ws)
+    s = _dense_shape(q, k, scale, split_tokens)
+    top_k = page_idx.shape[-1]
+    _expect(page_idx, (q.shape[0], q.shape[1], top_k), torch.int32, "page_idx")
+    _expect(out, q.shape, torch.float32, "out")
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must have the same shape and dtype")
+    need = lib.da_decode_attention_paged_workspace(ctypes.byref(s), page_size, top_k)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = _ws(need, q.device)
+    check(lib.da_decode_attention_paged(ctypes.byref(s), page_size, top_k, _vp(page_idx), _vp(q),
+                                        _vp(k), _vp(v), _vp(out), _vp(ws), ws.numel(),
+                                        _stream(stream)))
+    return out
+
+
+def da_quantize_kv4(x, codes=None, gmin=None, gscale=None, stream=None):
+    """fp16 [..., R] -> (codes uint8 [..., R/2], min fp16 [..., R/64], scale fp16 [..., R/64])."""
+    lib = load()
+    _dev(x, codes, gmin, gscale)
+    if x.dtype != torch.float16:
+        raise ValueError("x must be float16")
+    R = x.shape[-1]
+    lead = tuple(x.shape[:-1])
+    n_rows = x.numel() // R if R else 0
+    _expect(codes, lead + (R // 2,), torch.uint8, "codes")
+    _expect(gmin, lead + (R // 64,), torch.float16, "gmin")
+    _expect(gscale, lead + (R // 64,), torch.float16, "gscale")
+    if codes is None:
+        codes = torch.empty(lead + (R // 2,), dtype=torch.uint8, device=x.device)
+    if gmin is None:
+        gmin = torch.empty(lead + (R // 64,), dtype=torch.float16, device=x.device)
+    if gscale is None:
+        gscale = torch.empty(lead + (R // 64,), dtype=torch.float16, device=x.device)
+    check(lib.da_quantize_kv4(n_rows, R, _vp(x), _vp(codes), _vp(gmin), _vp(gscale),
+                              _stream(stream)))
+    return codes, gmin, gscale
+
+
+def da_dequantize_kv4(codes, gmin, gscale, out=None, stream=None):
+    """(codes, min, scale) -> fp16 fp16(min + code * scale)."""
+    lib = load()
+    _dev(codes, gmin, gscale, out)
+    R = codes.shape[-1] * 2
+    lead = tuple(codes.shape[:-1])
+    n_rows = codes.numel() * 2 // R if R else 0
+    if codes.dtype != torch.uint8:
+        raise ValueError("codes must be uint8")
+    _expect(gmin, lead + (R // 64,), torch.float16, "gmin")
+    _expect(gscale, lead + (R // 64,), torch.float16, "gscale")
+    _expect(out, lead + (R,), torch.float16, "out")
+    if out is None:
+        out = torch.empty(lead + (R,), dtype=torch.float16, device=codes.device)
+    check(lib.da_dequantize_kv4(n_rows, R, _vp(codes), _vp(gmin), _vp(gscale), _vp(out),
+                                _stream(stream)))
+    return out
+
+
+def da_decode_attention_kv4(q, k_codes, k_min, k_scale, v_codes, v_min, v_scale, scale=None,
+                            split_tokens=0, out=None, ws=None, stream=None):
+    """Decode attention over a uint4 cache; fp32 [B][Hq][D]."""
+    lib = load()
+    _dev(q, k_codes, k_min, k_scale, v_codes, v_min, v_scale, out, ws)
+    B, Hq, D = q.shape
+    if k_codes.dim() != 4 or k_codes.shape[-1] * 2 != D:
+        raise ValueError("codes must be [B][Hkv][N][D/2]")
+    Hkv, N = k_codes.shape[1], k_codes.shape[2]
+    for t, name in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        _expect(t, (B, Hkv, N, D // 2), torch.uint8, name)
+    for t, name in ((k_min, "k_min"), (k_scale, "k_scale"), (v_min, "v_min"), (v_scale, "v_scale")):
+        _expect(t, (B, Hkv, N, D // 64), torch.float16, name)
+    _expect(out, q.shape, torch.float32, "out")
+    s = attn_shape(B, Hq, Hkv, D, N, scale, _DT[q.dtype], DA_F16, split_tokens)
+    need = lib.da_decode_attention_kv4_workspace(ctypes.byref(s))
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = _ws(need, q.device)
+    check(lib.da_decode_attention_kv4(ctypes.byref(s), _vp(q), _vp(k_codes), _vp(k_min),
+                                      _vp(k_scale), _vp(v_codes), _vp(v_min), _vp(v_scale),
+                                      _vp(out), _vp(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def da_headwise_buffer_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_ctx, kv_dtype=DA_BF16,
+                             q_dtype=DA_F32, heads_per_chunk=1) -> int:
+    s = attn_shape(batch, n_q_heads, n_kv_heads, head_dim, n_ctx, None, q_dtype, kv_dtype)
+    return int(load().da_headwise_buffer_bytes(ctypes.byref(s), heads_per_chunk))
+
+
+class HeadwiseStream:
+    """da_stream_* context: head-wise streamed decode over pinned host KV."""
+
+    def __init__(self, batch, n_q_heads, n_kv_heads, head_dim, n_ctx, q_dtype=DA_F32,
+                 kv_dtype=DA_BF16, heads_per_chunk=1, scale=None, split_tokens=0):
+        self._lib = load()
+        self.shape = attn_shape(batch, n_q_heads, n_kv_heads, head_dim, n_ctx, scale, q_dtype,
+                                kv_dtype, split_tokens)
+        self.heads_per_chunk = heads_per_chunk
+        self._ctx = ctypes.c_void_p()
+        check(self._lib.da_stream_create(ctypes.byref(self.shape), heads_per_chunk,
+                                         ctypes.byref(self._ctx)))
+
+    @property
+    def buffer_bytes(self) -> int:
+        return int(self._lib.da_stream_buffer_bytes(self._ctx))
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(self._lib.da_stream_workspace(self._ctx))
+
+    def da_stream_headwise(self, k_host, v_host, buf0, buf1, q, out, ws, compute, copy):
+        """k_host/v_host: lists (layer-major) of pinned host tensors [B][N][D]."""
+        _dev(buf0, buf1, q, out, ws)
+        n = len(k_host)
+        if n % self.shape.n_kv_heads or len(v_host) != n:
+            raise ValueError("need n_layers * n_kv_heads host tensors for K and for V")
+        for t in list(k_host) + list(v_host):
+            if t.is_cuda or not t.is_contiguous():
+                raise ValueError("host KV tensors must be contiguous CPU tensors")
+        hb = self.buffer_bytes // (2 * self.heads_per_chunk)
+        for t in list(k_host) + list(v_host):
+            if t.numel() * t.element_size() != hb:
+                raise ValueError(f"each host head must hold {hb} bytes")
+        for b in (buf0, buf1):
+            if b.numel() * b.element_size() < self.buffer_bytes:
+                raise ValueError(f"ping-pong buffers need {self.buffer_bytes} bytes")
+        L = n // self.shape.n_kv_heads
+        qshape = (L, self.shape.batch, self.shape.n_q_heads, self.shape.head_dim)
+        if tuple(q.shape) != qshape or tuple(out.shape) != qshape or out.dtype != torch.float32:
+            raise ValueError(f"q and out must be {qshape} (out fp32)")
+        kp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in k_host])
+        vp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in v_host])
+        check(self._lib.da_stream_headwise(self._ctx, n // self.shape.n_kv_heads, kp, vp,
+                                           _vp(buf0), _vp(buf1), _vp(q), _vp(out), _vp(ws),
+                                           ws.numel(), _stream(compute), _stream(copy)))
+        return out
+
+    def close(self):
+        if self._ctx:
+            self._lib.da_stream_destroy(self._ctx)
+            self._ctx = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,72 @@
+// Internal interface between the C-ABI layer (api.cpp, stream.cpp) and the
+// HIP kernels.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace da {
+
+// Storage formats of q and of the KV cache.  Values 0..2 equal da_dtype.
+enum Fmt : int { FMT_F32 = 0, FMT_F16 = 1, FMT_BF16 = 2, FMT_U4 = 3 };
+
+constexpr int kDefaultSplitTokens = 512;
+
+// One attention launch (split-K partial pass + cross-split merge).
+// The KV cache is addressed by rows (tokens): row r of (batch b, KV head h)
+// starts at base + ((b * kv_bstride + h * kv_hstride) + r) * row_bytes.
+struct AttnLaunch {
+    int32_t B = 0, Hkv = 0, G = 0, D = 0;
+    int64_t N = 0;                 // valid tokens per (b, h)
+    float scale_log2 = 0.f;        // softmax scale * log2(e)
+    int32_t q_fmt = 0, kv_fmt = 0;
+
+    const void *q = nullptr;       // head (h*G + g) of row b at q + b*q_bstride + (h*G+g)*D
+    int64_t q_bstride = 0;         // elements
+    float *o = nullptr;            // same indexing as q, fp32
+    int64_t o_bstride = 0;         // floats
+
+    const void *k = nullptr, *v = nullptr;
+    int64_t kv_bstride = 0, kv_hstride = 0;   // rows
+    // uint4 cache: per-row fp16 min and scale arrays, D/64 per row
+    const void *kmin = nullptr, *kscale = nullptr, *vmin = nullptr, *vscale = nullptr;
+
+    // page-sparse: page list [B][Hkv][top_k] (Hq == Hkv), page = 2^log2_page tokens
+    const int32_t *page_idx = nullptr;
+    int32_t top_k = 0, log2_page = 0;
+
+    int32_t split_tokens = kDefaultSplitTokens;
+    int32_t n_split = 0;
+    float *ws = nullptr;           // [B*Hkv*G][n_split][D+2]
+};
+
+// Number of splits and workspace bytes for a launch description.
+int32_t attn_n_split(int64_t n_ctx, int32_t split_tokens, bool paged,
+                     int32_t top_k, int32_t log2_page);
+size_t attn_ws_bytes(int64_t rows, int32_t n_split, int32_t D);
+
+// True if a kernel is built for this combination.
+bool attn_supported(int kv_fmt, int q_fmt, int D, int G, bool paged);
+
+hipError_t launch_attention(const AttnLaunch &a, hipStream_t stream);
+
+// Page metadata: kmin/kmax [B*H][P][D] from k [B*H][N][D].
+hipError_t launch_page_meta(int kv_fmt, int64_t BH, int64_t N, int D,
+                            int log2_page, const void *k, void *kmin, void *kmax,
+                            hipStream_t stream);
+
+// Bound score + top-K per (b, h).
+bool select_supported(int kv_fmt, int q_fmt, int D);
+hipError_t launch_select(int kv_fmt, int q_fmt, int64_t BH, int64_t P, int D,
+                         int top_k, const void *q, const void *kmin,
+                         const void *kmax, int32_t *page_idx, float *page_score,
+                         hipStream_t stream);
+
+// uint4 group quantization.
+hipError_t launch_quantize_kv4(int64_t n_groups, const void *x, uint8_t *codes,
+                               void *gmin, void *gscale, hipStream_t stream);
+hipError_t launch_dequantize_kv4(int64_t n_groups, const uint8_t *codes,
+                                 const void *gmin, const void *gscale, void *x,
+                                 hipStream_t stream);
+
+}  // namespace da

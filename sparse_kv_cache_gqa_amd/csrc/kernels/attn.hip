@@ -1,0 +1,591 @@
+// Split-K decode attention for gfx950 (CDNA4).
+//
+// Computes, per (batch row b, KV head h) and each of its G query heads, the
+// decode-attention output softmax(scale * q . k_i) v_i over a token range
+// (HeadInfer, section "核心 idea", per-head equation; TinyServe, section
+// "方法细节", Attn and SparseAttn).  One workgroup reduces one split of the
+// range to a partial (running max, running sum, unnormalised output); a second
+// kernel merges the splits.
+//
+// Mapping to the hardware
+//   * q.K^T runs on the matrix cores.  A 16x16x32 MFMA takes 16 tokens as its
+//     N dimension; every lane loads 16 bytes of one token's key row straight
+//     from HBM into the B operand (no LDS round trip).  The 16 rows of the A
+//     operand hold the G query heads, each split into several bf16/fp16 terms
+//     (hi + mid + lo) when q is fp32, so the products are exact and the sum is
+//     fp32-accurate; for a uint4 cache the rows also separate the two
+//     64-channel quantization groups so their scales can be applied after.
+//   * P.V runs on the VALU in fp32: each lane owns a fixed set of channels and
+//     accumulates them over the tokens it loads (16-byte coalesced loads).
+//   * Online softmax per 32-token tile in base 2 (exp2 with log2(e) folded
+//     into the scale); the per-head tile max is reduced with lane shuffles
+//     and broadcast with readlane; accumulators are rescaled only when a max
+//     changes.
+//   * The four waves of a workgroup merge through LDS; the partial goes to the
+//     workspace, and attn_reduce combines the splits of each query head.
+#include "common.h"
+
+#include <math.h>
+
+namespace da {
+namespace {
+
+using namespace dev;
+
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSub = 16;               // tokens per MFMA (its N dimension)
+constexpr int kTS = 2;                 // MFMA sub-tiles per wave iteration
+constexpr int kTile = kSub * kTS;      // tokens per wave iteration
+constexpr int kMaxPagesPerSplit = 1024;
+
+// Compile-time layout of one kernel instance.
+template <int KF, int QF, int D, int G>
+struct Cfg {
+    static constexpr bool U4 = KF == FMT_U4;
+    static constexpr int R = KF == FMT_F32 ? 4 * D : (U4 ? D / 2 : 2 * D);   // row bytes
+    static constexpr int NGRP = U4 ? D / 64 : 1;        // quantization groups per row
+    // number of terms q is split into for the MFMA input type
+    static constexpr int SPL = (KF == FMT_F32) ? 1
+                             : (QF == KF || (U4 && QF == FMT_F16)) ? 1
+                             : (KF == FMT_BF16 ? (G <= 4 ? 3 : 2) : 2);
+    static constexpr int RPH0 = SPL * NGRP;            // A rows used per head
+    static constexpr int RPH = RPH0 <= 1 ? 1 : (RPH0 <= 2 ? 2 : 4);
+    static constexpr int HPL = 4 / RPH;                 // heads per 16-lane group
+    static constexpr int NCH = R / 64;                  // 16-byte K chunks per lane per sub-tile
+    static constexpr int NMF = KF == FMT_F32 ? 4 * NCH : (U4 ? 4 * NCH : NCH);
+    static constexpr int VP = R / 64;                   // 16-byte V pieces per lane per sub-tile
+    static constexpr int TPP = 1024 / R;                // token stride between V pieces
+    static constexpr int CPL = KF == FMT_F32 ? 4 : (U4 ? 32 : 8);   // V channels per lane
+    static constexpr int CH_LANES = R / 16;             // lanes covering one row (V side)
+    // 16 MFMA rows must hold every (head, group, split term); rows fit 64..1024 bytes
+    static constexpr bool ok = RPH0 <= 4 && G * RPH <= 16 && R >= 64 && R <= 1024;
+};
+
+// One dword of 8 codes -> 8 fp16 values 0..15 in the order of qk_dim().
+__device__ __forceinline__ u32x4 u4_to_f16x8(uint32_t x) {
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t m = ((x >> (4 * k)) & 0x000F000Fu) | 0x64006400u;   // 1024 + c
+        f16x2 h = __builtin_bit_cast(f16x2, m) - (f16x2){(_Float16)1024.0f, (_Float16)1024.0f};
+        r[k] = __builtin_bit_cast(uint32_t, h);
+    }
+    return r;
+}
+
+template <int KF, int QF, int D, int G, bool PAGED>
+__global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnLaunch a) {
+    using C = Cfg<KF, QF, D, G>;
+    static_assert(C::ok, "unsupported layout");
+    constexpr int R = C::R, RPH = C::RPH, HPL = C::HPL, SPL = C::SPL, NGRP = C::NGRP;
+    constexpr int NCH = C::NCH, NMF = C::NMF, VP = C::VP, TPP = C::TPP, CPL = C::CPL;
+    constexpr int MT = C::U4 ? FMT_F16 : KF;
+
+    __shared__ float p_lds[kWaves][kTile][G];
+    __shared__ float mrg_o[kWaves][G][D];
+    __shared__ float mrg_m[kWaves][G];
+    __shared__ float mrg_l[kWaves][G];
+    __shared__ int32_t pg_lds[PAGED ? kMaxPagesPerSplit : 1];
+    __shared__ float qsum_lds[G][NGRP];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int g4 = lane >> 4;          // lane group (MFMA k-chunk / C row block)
+    const int n16 = lane & 15;         // token within sub-tile (K side)
+    const int split = blockIdx.x;
+    const int unit = blockIdx.y;       // b * Hkv + h
+    const int b = unit / a.Hkv;
+    const int hkv = unit - b * a.Hkv;
+
+    // ---- token range of this split --------------------------------------
+    int64_t s0 = 0;
+    int ntok;
+    int pg_mask = 0;
+    if constexpr (PAGED) {
+        const int pps = min(kMaxPagesPerSplit, max(1, a.split_tokens >> a.log2_page));
+        const int p0 = split * pps;
+        const int np = min(pps, a.top_k - p0);
+        const int32_t *lst = a.page_idx + (int64_t)unit * a.top_k + p0;
+        for (int i = tid; i < np; i += kThreads) pg_lds[i] = lst[i];
+        ntok = np << a.log2_page;
+        pg_mask = (1 << a.log2_page) - 1;
+    } else {
+        s0 = (int64_t)split * a.split_tokens;
+        ntok = (int)min((int64_t)a.split_tokens, a.N - s0);
+    }
+
+    const int64_t kvoff = (int64_t)b * a.kv_bstride + (int64_t)hkv * a.kv_hstride;
+    const char *kbase = (const char *)a.k + kvoff * R;
+    const char *vbase = (const char *)a.v + kvoff * R;
+    const uint16_t *kmn = nullptr, *ksc = nullptr, *vmn = nullptr, *vsc = nullptr;
+    if constexpr (C::U4) {
+        kmn = (const uint16_t *)a.kmin + kvoff * NGRP;
+        ksc = (const uint16_t *)a.kscale + kvoff * NGRP;
+        vmn = (const uint16_t *)a.vmin + kvoff * NGRP;
+        vsc = (const uint16_t *)a.vscale + kvoff * NGRP;
+    }
+    const int64_t qoff = (int64_t)b * a.q_bstride + (int64_t)hkv * G * D;
+
+    if constexpr (C::U4) {
+        if (tid < G * NGRP) {
+            const int h = tid / NGRP, gr = tid % NGRP;
+            float s = 0.f;
+            for (int d = 0; d < 64; ++d) s += load_scalar<QF>(a.q, qoff + h * D + gr * 64 + d);
+            qsum_lds[h][gr] = s;
+        }
+    }
+
+    // ---- A operand: query rows, split into MFMA-type terms -------------------
+    u32x4 Aq[KF == FMT_F32 ? 1 : NMF];
+    float Af[KF == FMT_F32 ? NMF : 1];
+    {
+        const int m = n16;
+        const int h = m / RPH, within = m % RPH;
+        const int grp = within / SPL, s = within % SPL;
+        const bool rowok = h < G && within < SPL * NGRP;
+#pragma unroll
+        for (int mf = 0; mf < NMF; ++mf) {
+            if constexpr (KF == FMT_F32) {
+                const int d = qk_dim<KF>(mf, g4, 0);
+                Af[mf] = rowok ? load_scalar<QF>(a.q, qoff + h * D + d) : 0.f;
+            } else {
+                uint32_t hv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int d = qk_dim<KF>(mf, g4, e);
+                    float x = 0.f;
+                    if (rowok && (!C::U4 || d / 64 == grp)) x = load_scalar<QF>(a.q, qoff + h * D + d);
+                    hv[e] = split_term<MT>(x, s);
+                }
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) Aq[mf][e2] = hv[2 * e2] | (hv[2 * e2 + 1] << 16);
+            }
+        }
+    }
+    if constexpr (C::U4) __syncthreads();   // qsum_lds
+    if constexpr (PAGED) { if constexpr (!C::U4) __syncthreads(); }   // pg_lds
+
+    float qs[HPL][NGRP];
+    if constexpr (C::U4) {
+#pragma unroll
+        for (int hh = 0; hh < HPL; ++hh)
+#pragma unroll
+            for (int gr = 0; gr < NGRP; ++gr) {
+                const int h = g4 * HPL + hh;
+                qs[hh][gr] = h < G ? qsum_lds[h][gr] : 0.f;
+            }
+    }
+
+    // ---- running state ----------------------------------------------------
+    float m_run[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) m_run[h] = neg_inf();
+    float l_part[HPL];
+#pragma unroll
+    for (int hh = 0; hh < HPL; ++hh) l_part[hh] = 0.f;
+    float acc[G][CPL];
+    float amin[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        amin[h] = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[h][c] = 0.f;
+    }
+
+    const int vcol = (lane * 16) % R;            // V byte column of this lane
+    const int vtok = (lane * 16) / R;            // V token within a piece
+    const float sl2 = a.scale_log2;
+
+    auto row_of = [&](int pos, bool &ok) -> int64_t {
+        if constexpr (PAGED) {
+            ok = pos < ntok;
+            if (!ok) return 0;
+            const int32_t pg = pg_lds[pos >> a.log2_page];
+            const int64_t r = ((int64_t)pg << a.log2_page) + (pos & pg_mask);
+            ok = pg >= 0 && r < a.N;
+            return ok ? r : 0;
+        } else {
+            ok = pos < ntok;
+            return ok ? s0 + pos : 0;
+        }
+    };
+
+    for (int t0 = w * kTile; t0 < ntok; t0 += kWaves * kTile) {
+        // ---- issue loads: K (B operand), then V ---------------------------
+        u32x4 Kr[kTS][NCH];
+        u32x4 Vr[kTS][VP];
+        bool kok[kTS];
+        uint32_t kmn_r[kTS], ksc_r[kTS];
+        float vmn_r[kTS], vsc_r[kTS];
+#pragma unroll
+        for (int ts = 0; ts < kTS; ++ts) {
+            bool ok;
+            const int64_t r = row_of(t0 + ts * kSub + n16, ok);
+            kok[ts] = ok;
+            const char *p = kbase + r * R + 16 * g4;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+                Kr[ts][c] = ok ? *(const u32x4 *)(p + 64 * c) : (u32x4){0u, 0u, 0u, 0u};
+            if constexpr (C::U4) {
+                kmn_r[ts] = ok ? *(const uint32_t *)(kmn + r * NGRP) : 0u;
+                ksc_r[ts] = ok ? *(const uint32_t *)(ksc + r * NGRP) : 0u;
+            }
+        }
+#pragma unroll
+        for (int ts = 0; ts < kTS; ++ts) {
+#pragma unroll
+            for (int p = 0; p < VP; ++p) {
+                bool ok;
+                const int64_t r = row_of(t0 + ts * kSub + p * TPP + vtok, ok);
+                Vr[ts][p] = ok ? *(const u32x4 *)(vbase + r * R + vcol) : (u32x4){0u, 0u, 0u, 0u};
+                if constexpr (C::U4) {
+                    const int gr = vcol / 32;
+                    vmn_r[ts] = ok ? f16_to_f32(vmn[r * NGRP + gr]) : 0.f;
+                    vsc_r[ts] = ok ? f16_to_f32(vsc[r * NGRP + gr]) : 0.f;
+                }
+            }
+        }
+
+        // ---- scores on the matrix cores -------------------------------------
+        float sc[kTS][HPL];
+#pragma unroll
+        for (int ts = 0; ts < kTS; ++ts) {
+            f32x4 cc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                if constexpr (KF == FMT_F32) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        cc = __builtin_amdgcn_mfma_f32_16x16x4f32(Af[4 * c + e], __uint_as_float(Kr[ts][c][e]), cc, 0, 0, 0);
+                } else if constexpr (KF == FMT_BF16) {
+                    cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Aq[c]),
+                                                                 __builtin_bit_cast(bf16x8, Kr[ts][c]), cc, 0, 0, 0);
+                } else if constexpr (KF == FMT_F16) {
+                    cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, Aq[c]),
+                                                                __builtin_bit_cast(f16x8, Kr[ts][c]), cc, 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, Aq[4 * c + u]),
+                                                                    __builtin_bit_cast(f16x8, u4_to_f16x8(Kr[ts][c][u])), cc, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int hh = 0; hh < HPL; ++hh) {
+                const int h = g4 * HPL + hh;
+                float raw = 0.f;
+                if constexpr (C::U4) {
+#pragma unroll
+                    for (int gr = 0; gr < NGRP; ++gr) {
+                        float dot = 0.f;
+#pragma unroll
+                        for (int s = 0; s < SPL; ++s) dot += cc[hh * RPH + gr * SPL + s];
+                        const float mn = f16_to_f32((kmn_r[ts] >> (16 * gr)) & 0xFFFFu);
+                        const float sg = f16_to_f32((ksc_r[ts] >> (16 * gr)) & 0xFFFFu);
+                        raw += mn * qs[hh][gr] + sg * dot;
+                    }
+                } else {
+#pragma unroll
+                    for (int s = 0; s < SPL; ++s) raw += cc[hh * RPH + s];
+                }
+                sc[ts][hh] = (h < G && kok[ts]) ? raw * sl2 : neg_inf();
+            }
+        }
+
+        // ---- online softmax (base 2) ------------------------------------
+        float mt[HPL];
+#pragma unroll
+        for (int hh = 0; hh < HPL; ++hh) {
+            float x = sc[0][hh];
+#pragma unroll
+            for (int ts = 1; ts < kTS; ++ts) x = fmaxf(x, sc[ts][hh]);
+            x = fmaxf(x, shfl_xor(x, 1));
+            x = fmaxf(x, shfl_xor(x, 2));
+            x = fmaxf(x, shfl_xor(x, 4));
+            x = fmaxf(x, shfl_xor(x, 8));
+            mt[hh] = x;
+        }
+        float alpha[G];
+        bool changed = false;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float tmax = readlane_f(mt[h % HPL], (h / HPL) * 16);
+            const float mn = fmaxf(m_run[h], tmax);
+            alpha[h] = (mn == m_run[h]) ? 1.f : fast_exp2(m_run[h] - mn);
+            changed |= (mn != m_run[h]);
+            m_run[h] = mn;
+        }
+        if (changed) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                amin[h] *= alpha[h];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) acc[h][c] *= alpha[h];
+            }
+#pragma unroll
+            for (int hh = 0; hh < HPL; ++hh) {
+                const int h = g4 * HPL + hh;
+                float al = 1.f;
+#pragma unroll
+                for (int h2 = 0; h2 < G; ++h2) if (h2 == h) al = alpha[h2];
+                l_part[hh] *= al;
+            }
+        }
+#pragma unroll
+        for (int hh = 0; hh < HPL; ++hh) {
+            const int h = g4 * HPL + hh;
+            float mh = 0.f;
+#pragma unroll
+            for (int h2 = 0; h2 < G; ++h2) if (h2 == h) mh = m_run[h2];
+#pragma unroll
+            for (int ts = 0; ts < kTS; ++ts) {
+                const float p = (sc[ts][hh] == neg_inf()) ? 0.f : fast_exp2(sc[ts][hh] - mh);
+                l_part[hh] += p;
+                if (h < G) p_lds[w][ts * kSub + n16][h] = p;
+            }
+        }
+        wave_lds_sync();
+
+        // ---- P.V on the VALU ------------------------------------------------
+#pragma unroll
+        for (int ts = 0; ts < kTS; ++ts) {
+#pragma unroll
+            for (int p = 0; p < VP; ++p) {
+                const int t = ts * kSub + p * TPP + vtok;
+                float pv[G];
+#pragma unroll
+                for (int h = 0; h < G; ++h) pv[h] = p_lds[w][t][h];
+                const u32x4 x = Vr[ts][p];
+                if constexpr (KF == FMT_F32) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float xv = __uint_as_float(x[e]);
+#pragma unroll
+                        for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pv[h], xv, acc[h][e]);
+                    }
+                } else if constexpr (C::U4) {
+                    float wv[G];
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        wv[h] = pv[h] * vsc_r[ts];
+                        amin[h] = fmaf(pv[h], vmn_r[ts], amin[h]);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint32_t lo = x[u] & 0x0F0F0F0Fu;
+                        const uint32_t hi = (x[u] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                        for (int bb = 0; bb < 4; ++bb) {
+                            const float c0 = (float)((lo >> (8 * bb)) & 0xFFu);
+                            const float c1 = (float)((hi >> (8 * bb)) & 0xFFu);
+#pragma unroll
+                            for (int h = 0; h < G; ++h) {
+                                acc[h][8 * u + 2 * bb] = fmaf(wv[h], c0, acc[h][8 * u + 2 * bb]);
+                                acc[h][8 * u + 2 * bb + 1] = fmaf(wv[h], c1, acc[h][8 * u + 2 * bb + 1]);
+                            }
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        float x0, x1;
+                        if constexpr (KF == FMT_BF16) {
+                            x0 = __uint_as_float(x[e2] << 16);
+                            x1 = __uint_as_float(x[e2] & 0xFFFF0000u);
+                        } else {
+                            x0 = f16_to_f32(x[e2] & 0xFFFFu);
+                            x1 = f16_to_f32(x[e2] >> 16);
+                        }
+#pragma unroll
+                        for (int h = 0; h < G; ++h) {
+                            acc[h][2 * e2] = fmaf(pv[h], x0, acc[h][2 * e2]);
+                            acc[h][2 * e2 + 1] = fmaf(pv[h], x1, acc[h][2 * e2 + 1]);
+                        }
+                    }
+                }
+            }
+        }
+        wave_lds_sync();
+    }
+
+    // ---- merge lanes, then waves ----------------------------------------
+#pragma unroll
+    for (int hh = 0; hh < HPL; ++hh) {
+        float x = l_part[hh];
+        x += shfl_xor(x, 1);
+        x += shfl_xor(x, 2);
+        x += shfl_xor(x, 4);
+        x += shfl_xor(x, 8);
+        l_part[hh] = x;
+    }
+#pragma unroll
+    for (int mask = C::CH_LANES; mask < 64; mask <<= 1) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            amin[h] += shfl_xor(amin[h], mask);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[h][c] += shfl_xor(acc[h][c], mask);
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) mrg_m[w][h] = m_run[h];
+    }
+    if (n16 == 0) {
+#pragma unroll
+        for (int hh = 0; hh < HPL; ++hh) {
+            const int h = g4 * HPL + hh;
+            if (h < G) mrg_l[w][h] = l_part[hh];
+        }
+    }
+    if (lane < C::CH_LANES) {
+        const int c0 = KF == FMT_F32 ? vcol / 4 : (C::U4 ? vcol * 2 : vcol / 2);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) mrg_o[w][h][c0 + c] = acc[h][c] + (C::U4 ? amin[h] : 0.f);
+    }
+    __syncthreads();
+
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+        const int h = idx / D, d = idx - h * D;
+        float M = mrg_m[0][h];
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, mrg_m[ww][h]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            const float mw = mrg_m[ww][h];
+            const float f = (mw == neg_inf()) ? 0.f : fast_exp2(mw - M);
+            L = fmaf(f, mrg_l[ww][h], L);
+            O = fmaf(f, mrg_o[ww][h][d], O);
+        }
+        float *dst = a.ws + ((int64_t)(unit * G + h) * a.n_split + split) * (D + 2);
+        dst[2 + d] = O;
+        if (d == 0) { dst[0] = M; dst[1] = L; }
+    }
+}
+
+// Merge of the split partials of one query head (one block per head row).
+__global__ __launch_bounds__(128) void attn_reduce_kernel(const float *__restrict__ ws, float *__restrict__ o,
+                                                          int n_split, int D, int HG, int64_t o_bstride) {
+    const int row = blockIdx.x;                 // (b * Hkv + h) * G + g = b * HG + hq
+    const int b = row / HG, hq = row - b * HG;
+    const float *p = ws + (int64_t)row * n_split * (D + 2);
+    float M = neg_inf();
+    for (int s = 0; s < n_split; ++s) M = fmaxf(M, p[(int64_t)s * (D + 2)]);
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        float L = 0.f, O = 0.f;
+        for (int s = 0; s < n_split; ++s) {
+            const float *q = p + (int64_t)s * (D + 2);
+            const float f = (q[0] == neg_inf()) ? 0.f : fast_exp2(q[0] - M);
+            L = fmaf(f, q[1], L);
+            O = fmaf(f, q[2 + d], O);
+        }
+        o[(int64_t)b * o_bstride + (int64_t)hq * D + d] = O / L;
+    }
+}
+
+using SplitFn = void (*)(AttnLaunch);
+
+template <int KF, int QF, int D, int G, bool PAGED>
+SplitFn pick_one() {
+    if constexpr (Cfg<KF, QF, D, G>::ok) return attn_split_kernel<KF, QF, D, G, PAGED>;
+    else return nullptr;
+}
+
+template <int KF, int QF, int D, bool PAGED>
+SplitFn pick_g(int G) {
+    if constexpr (PAGED) return G == 1 ? pick_one<KF, QF, D, 1, PAGED>() : nullptr;
+    switch (G) {
+    case 1: return pick_one<KF, QF, D, 1, PAGED>();
+    case 2: return pick_one<KF, QF, D, 2, PAGED>();
+    case 4: return pick_one<KF, QF, D, 4, PAGED>();
+    case 8: return pick_one<KF, QF, D, 8, PAGED>();
+    default: return nullptr;
+    }
+}
+
+template <int KF, int QF, bool PAGED>
+SplitFn pick_d(int D, int G) {
+    if constexpr (KF == FMT_U4) {
+        return D == 128 ? pick_g<KF, QF, 128, PAGED>(G) : nullptr;
+    } else {
+        if (D == 64) return pick_g<KF, QF, 64, PAGED>(G);
+        if (D == 128) return pick_g<KF, QF, 128, PAGED>(G);
+        return nullptr;
+    }
+}
+
+SplitFn pick(int kv, int qf, int D, int G, bool paged) {
+    if (paged) {
+        if (G != 1) return nullptr;
+        switch (kv) {
+        case FMT_F32: return qf == FMT_F32 ? pick_d<FMT_F32, FMT_F32, true>(D, G) : nullptr;
+        case FMT_F16:
+            if (qf == FMT_F16) return pick_d<FMT_F16, FMT_F16, true>(D, G);
+            if (qf == FMT_F32) return pick_d<FMT_F16, FMT_F32, true>(D, G);
+            return nullptr;
+        case FMT_BF16:
+            if (qf == FMT_BF16) return pick_d<FMT_BF16, FMT_BF16, true>(D, G);
+            if (qf == FMT_F32) return pick_d<FMT_BF16, FMT_F32, true>(D, G);
+            return nullptr;
+        default: return nullptr;
+        }
+    }
+    switch (kv) {
+    case FMT_F32: return qf == FMT_F32 ? pick_d<FMT_F32, FMT_F32, false>(D, G) : nullptr;
+    case FMT_F16:
+        if (qf == FMT_F16) return pick_d<FMT_F16, FMT_F16, false>(D, G);
+        if (qf == FMT_F32) return pick_d<FMT_F16, FMT_F32, false>(D, G);
+        return nullptr;
+    case FMT_BF16:
+        if (qf == FMT_BF16) return pick_d<FMT_BF16, FMT_BF16, false>(D, G);
+        if (qf == FMT_F32) return pick_d<FMT_BF16, FMT_F32, false>(D, G);
+        return nullptr;
+    case FMT_U4:
+        if (qf == FMT_F16) return pick_d<FMT_U4, FMT_F16, false>(D, G);
+        if (qf == FMT_F32) return pick_d<FMT_U4, FMT_F32, false>(D, G);
+        return nullptr;
+    default: return nullptr;
+    }
+}
+
+}  // namespace
+
+int32_t attn_n_split(int64_t n_ctx, int32_t split_tokens, bool paged, int32_t top_k, int32_t log2_page) {
+    if (split_tokens <= 0) split_tokens = kDefaultSplitTokens;
+    if (paged) {
+        int pps = split_tokens >> log2_page;
+        if (pps < 1) pps = 1;
+        if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;
+        return (top_k + pps - 1) / pps;
+    }
+    return (int32_t)((n_ctx + split_tokens - 1) / split_tokens);
+}
+
+size_t attn_ws_bytes(int64_t rows, int32_t n_split, int32_t D) {
+    return (size_t)rows * (size_t)n_split * (size_t)(D + 2) * sizeof(float);
+}
+
+bool attn_supported(int kv_fmt, int q_fmt, int D, int G, bool paged) {
+    return pick(kv_fmt, q_fmt, D, G, paged) != nullptr;
+}
+
+hipError_t launch_attention(const AttnLaunch &a, hipStream_t stream) {
+    SplitFn fn = pick(a.kv_fmt, a.q_fmt, a.D, a.G, a.page_idx != nullptr);
+    if (!fn) return hipErrorInvalidValue;
+    dim3 grid(a.n_split, a.B * a.Hkv);
+    hipLaunchKernelGGL(fn, grid, dim3(kThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int rows = a.B * a.Hkv * a.G;
+    hipLaunchKernelGGL(attn_reduce_kernel, dim3(rows), dim3(a.D), 0, stream,
+                       (const float *)a.ws, a.o, a.n_split, a.D, a.Hkv * a.G, a.o_bstride);
+    return hipGetLastError();
+}
+
+}  // namespace da

@@ -1,0 +1,87 @@
+// Device helpers shared by the gfx950 kernels: vector types, exact storage
+// conversions, wave-level shuffles.
+#pragma once
+
+#include "../internal.h"
+
+namespace da {
+namespace dev {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+    uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;     // nearest, ties to even
+}
+__device__ __forceinline__ float f16_to_f32(uint32_t b) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+__device__ __forceinline__ uint32_t f32_to_f16(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);  // nearest, ties to even
+}
+
+template <int F>
+__device__ __forceinline__ float load_scalar(const void *p, int64_t i) {
+    if constexpr (F == FMT_F32) return ((const float *)p)[i];
+    else if constexpr (F == FMT_F16) return f16_to_f32(((const uint16_t *)p)[i]);
+    else return bf16_to_f32(((const uint16_t *)p)[i]);
+}
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int mask) {
+    return __shfl_xor(v, mask, 64);
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+
+// Physical channel fed by MFMA `mf`, lane group g (lane / 16), element e, when
+// a lane loads 16 bytes at byte offset 64 * chunk + 16 * g of a row:
+//   fp32:  16x16x4 MFMA per element  -> channel 16 * chunk + 4 * g + e (mf = 4 * chunk + e)
+//   16-bit: 16x16x32 MFMA per chunk  -> channel 32 * chunk + 8 * g + e (mf = chunk)
+//   uint4: 16x16x32 MFMA per dword u of the lane's 16 bytes; the codes of a dword
+//          come out as channels {0,4,1,5,2,6,3,7} -> 32 * g + 8 * u + pos(e)
+template <int KF>
+__device__ __forceinline__ int qk_dim(int mf, int g, int e) {
+    if constexpr (KF == FMT_F32) {
+        return 16 * (mf >> 2) + 4 * g + (mf & 3);
+    } else if constexpr (KF == FMT_U4) {
+        const int pos = (e >> 1) + 4 * (e & 1);
+        return 32 * g + 8 * mf + pos;
+    } else {
+        return 32 * mf + 8 * g + e;
+    }
+}
+
+// x split into its `s`-th term of the 16-bit MFMA type MT (0 = nearest value,
+// then nearest value of the remainder, ...).  The terms sum to x within the
+// last term's rounding.
+template <int MT>
+__device__ __forceinline__ uint32_t split_term(float x, int s) {
+    uint32_t bits = 0;
+    for (int i = 0; i <= s; ++i) {
+        if constexpr (MT == FMT_BF16) { bits = f32_to_bf16(x); x -= bf16_to_f32(bits); }
+        else { bits = f32_to_f16(x); x -= f16_to_f32(bits); }
+    }
+    return bits;
+}
+
+}  // namespace dev
+}  // namespace da

@@ -1,0 +1,182 @@
+"""The C ABI without a GPU: libda.so loads, exports every function declared in
+include/da.h, and its host-side argument checks return the documented status
+codes before anything is enqueued (the fake device pointers used here are
+never dereferenced, and no call here reaches the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_kv_cache_gqa_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "da.h")
+
+FAKE = ctypes.c_void_p(0x10000)          # 16-byte aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x10008)
+NULL = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libda.so is not built (run __graft_entry__.build())")
+    return L.load()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(da_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert len(names) >= 19
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.SIGNATURES), "binding and header disagree"
+
+
+def test_version_matches_header(lib):
+    src = open(HEADER).read()
+    maj, mi, pa = (int(re.search(rf"#define DA_VERSION_{k} (\d+)", src).group(1))
+                   for k in ("MAJOR", "MINOR", "PATCH"))
+    assert lib.da_version() == (maj << 16) | (mi << 8) | pa
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["DA_OK", "DA_E_INVALID", "DA_E_UNSUPPORTED", "DA_E_WORKSPACE",
+                                 "DA_E_NOT_PINNED", "DA_E_HIP"]):
+        assert lib.da_status_string(code).decode() == name
+
+
+def shape(**kw):
+    d = dict(batch=8, n_q_heads=32, n_kv_heads=8, head_dim=128, n_ctx=32768, scale=128 ** -0.5,
+             q_dtype=L.DA_F32, kv_dtype=L.DA_BF16, split_tokens=0)
+    d.update(kw)
+    return L.DaAttnShape(**d)
+
+
+def dense(lib, s, q=FAKE, k=FAKE, v=FAKE, o=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return lib.da_decode_attention(ctypes.byref(s) if s is not None else None, q, k, v, o, ws,
+                                   ws_bytes, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_q_heads=30), L.DA_E_INVALID),           # not a multiple of n_kv_heads
+    (dict(n_q_heads=24), L.DA_E_UNSUPPORTED),       # G = 3
+    (dict(n_q_heads=128), L.DA_E_UNSUPPORTED),      # G = 16
+    (dict(n_kv_heads=0), L.DA_E_INVALID),
+    (dict(head_dim=96), L.DA_E_UNSUPPORTED),
+    (dict(head_dim=0), L.DA_E_INVALID),
+    (dict(n_ctx=0), L.DA_E_INVALID),
+    (dict(n_ctx=-5), L.DA_E_INVALID),
+    (dict(scale=0.0), L.DA_E_INVALID),
+    (dict(scale=float("nan")), L.DA_E_INVALID),
+    (dict(scale=float("inf")), L.DA_E_INVALID),
+    (dict(q_dtype=L.DA_F16), L.DA_E_UNSUPPORTED),   # fp16 q with bf16 KV
+    (dict(kv_dtype=7), L.DA_E_INVALID),
+    (dict(split_tokens=17), L.DA_E_INVALID),
+    (dict(split_tokens=8), L.DA_E_INVALID),
+    (dict(split_tokens=1 << 20), L.DA_E_INVALID),
+    (dict(batch=-1), L.DA_E_INVALID),
+    (dict(batch=20000), L.DA_E_UNSUPPORTED),        # batch * kv heads > 65535
+])
+def test_dense_shape_checks(lib, kw, code):
+    assert dense(lib, shape(**kw)) == code
+    assert lib.da_last_error().decode()
+
+
+def test_dense_pointer_and_workspace_checks(lib):
+    s = shape()
+    assert dense(lib, None) == L.DA_E_INVALID
+    assert dense(lib, s, q=NULL) == L.DA_E_INVALID
+    assert dense(lib, s, k=MISALIGNED) == L.DA_E_INVALID
+    assert dense(lib, s, o=NULL) == L.DA_E_INVALID
+    assert dense(lib, s, ws=NULL) == L.DA_E_INVALID
+    need = lib.da_decode_attention_workspace(ctypes.byref(s))
+    assert need == 8 * 32 * 64 * 130 * 4          # B*Hq rows x 64 splits x (D+2) fp32
+    assert dense(lib, s, ws_bytes=need - 1) == L.DA_E_WORKSPACE
+
+
+def test_empty_batch_is_a_no_op(lib):
+    s = shape(batch=0)
+    assert dense(lib, s, q=NULL, k=NULL, v=NULL, o=NULL, ws=NULL, ws_bytes=0) == L.DA_OK
+    assert lib.da_quantize_kv4(0, 128, NULL, NULL, NULL, NULL, NULL) == L.DA_OK
+
+
+def test_workspace_depends_on_split_size(lib):
+    s1 = shape(split_tokens=1024)
+    s2 = shape(split_tokens=256)
+    assert lib.da_decode_attention_workspace(ctypes.byref(s1)) == 8 * 32 * 32 * 130 * 4
+    assert lib.da_decode_attention_workspace(ctypes.byref(s2)) == 8 * 32 * 128 * 130 * 4
+    assert lib.da_decode_attention_workspace(ctypes.byref(shape(head_dim=96))) == 0
+
+
+def mha(**kw):
+    d = dict(batch=32, n_q_heads=16, n_kv_heads=16, head_dim=64, n_ctx=32768, q_dtype=L.DA_F16,
+             kv_dtype=L.DA_F16)
+    d.update(kw)
+    return shape(**d)
+
+
+def test_page_checks(lib):
+    s = mha()
+    meta = lambda ps: lib.da_build_page_meta(ctypes.byref(s), ps, FAKE, FAKE, FAKE, NULL)
+    assert meta(3) == L.DA_E_INVALID
+    assert meta(0) == L.DA_E_INVALID
+    assert meta(2048) == L.DA_E_INVALID
+    sel = lambda sh, ps, k: lib.da_select_pages(ctypes.byref(sh), ps, k, FAKE, FAKE, FAKE, FAKE,
+                                                NULL, NULL)
+    assert sel(s, 16, 0) == L.DA_E_INVALID
+    assert sel(s, 16, 2049) == L.DA_E_INVALID
+    assert sel(mha(n_q_heads=32), 16, 128) == L.DA_E_UNSUPPORTED     # GQA
+    assert sel(mha(n_ctx=16 * 8193), 16, 128) == L.DA_E_UNSUPPORTED   # > 8192 pages
+    assert lib.da_select_pages(ctypes.byref(s), 16, 128, FAKE, FAKE, FAKE, MISALIGNED, NULL,
+                               NULL) == L.DA_E_INVALID
+    paged = lambda sh, k, ws_bytes=1 << 40: lib.da_decode_attention_paged(
+        ctypes.byref(sh), 16, k, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, NULL)
+    assert paged(s, 0) == L.DA_E_INVALID
+    assert paged(mha(n_q_heads=32), 128) == L.DA_E_UNSUPPORTED
+    need = lib.da_decode_attention_paged_workspace(ctypes.byref(s), 16, 128)
+    assert need == 32 * 16 * 4 * 66 * 4           # 128 pages of 16 = 2048 positions / 512
+    assert paged(s, 128, need - 4) == L.DA_E_WORKSPACE
+
+
+def test_kv4_checks(lib):
+    q = lambda **kw: lib.da_quantize_kv4(kw.get("n", 4), kw.get("r", 128), FAKE, FAKE, FAKE, FAKE,
+                                          NULL)
+    assert q(r=96) == L.DA_E_INVALID
+    assert q(r=0) == L.DA_E_INVALID
+    assert q(n=-1) == L.DA_E_INVALID
+    assert lib.da_quantize_kv4(4, 128, MISALIGNED, FAKE, FAKE, FAKE, NULL) == L.DA_E_INVALID
+    assert lib.da_dequantize_kv4(4, 100, FAKE, FAKE, FAKE, FAKE, NULL) == L.DA_E_INVALID
+    s = shape(batch=64, n_q_heads=56, n_kv_heads=56, head_dim=128, n_ctx=1024, q_dtype=L.DA_F16)
+    att = lambda sh: lib.da_decode_attention_kv4(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                 FAKE, FAKE, FAKE, FAKE, 1 << 40, NULL)
+    s64 = shape(batch=64, n_q_heads=56, n_kv_heads=56, head_dim=64, n_ctx=1024, q_dtype=L.DA_F16)
+    assert att(s64) == L.DA_E_UNSUPPORTED
+    sbf = shape(batch=64, n_q_heads=56, n_kv_heads=56, head_dim=128, n_ctx=1024, q_dtype=L.DA_BF16)
+    assert att(sbf) == L.DA_E_UNSUPPORTED
+    assert lib.da_decode_attention_kv4_workspace(ctypes.byref(s)) == 64 * 56 * 2 * 130 * 4
+
+
+def test_headwise_sizes_match_the_pages_and_checks(lib):
+    # Llama-3-8B, 1M tokens, bf16: one head's K+V is 512 MiB; a layer is 4 GiB
+    s = shape(batch=1, n_ctx=1 << 20)
+    assert lib.da_headwise_buffer_bytes(ctypes.byref(s), 1) == 512 << 20
+    assert 2 * lib.da_headwise_buffer_bytes(ctypes.byref(s), 1) == 1 << 30     # "1 GB" on GPU
+    assert 2 * lib.da_headwise_buffer_bytes(ctypes.byref(s), 8) == 8 << 30     # layer-wise "8 GB"
+    assert lib.da_headwise_buffer_bytes(ctypes.byref(s), 3) == 0
+    ctx = ctypes.c_void_p()
+    assert lib.da_stream_create(ctypes.byref(s), 3, ctypes.byref(ctx)) == L.DA_E_INVALID
+    assert lib.da_stream_create(ctypes.byref(s), 16, ctypes.byref(ctx)) == L.DA_E_INVALID
+    assert lib.da_stream_create(ctypes.byref(s), 1, None) == L.DA_E_INVALID
+    arr = (ctypes.c_void_p * 1)(FAKE)
+    assert lib.da_stream_headwise(None, 1, arr, arr, FAKE, FAKE, FAKE, FAKE, FAKE, 1, NULL,
+                                  ctypes.c_void_p(1)) == L.DA_E_INVALID
+    assert lib.da_stream_buffer_bytes(None) == 0
+    assert lib.da_stream_workspace(None) == 0
+    lib.da_stream_destroy(None)

@@ -1,0 +1,110 @@
+"""Dense / GQA decode attention on the GPU against the fp64 oracle.
+
+Tolerances: the spec bar is |err| <= 1e-3 absolute on the fp32 output;
+on top of it these tests hold max|err| / rms(reference) <= 1e-4 (outputs of
+N(0,1) data are small, rms ~ sqrt(e/N)), and small shapes hold 1e-5 absolute.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import decode_attention
+from oracle.numerics import as_f64
+from gpu_util import assert_close, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run(da, c: synth.DenseCase, split_tokens=0):
+    import torch
+    q = to_dev(c.q, c.q_dtype)
+    k = to_dev(c.k, c.kv_dtype)
+    v = to_dev(c.v, c.kv_dtype)
+    o = da.da_decode_attention(q, k, v, scale=c.scale, split_tokens=split_tokens)
+    torch.cuda.synchronize()
+    return o.cpu().numpy()
+
+
+def oracle_of(c: synth.DenseCase):
+    return decode_attention(as_f64(c.q, c.q_dtype), as_f64(c.k, c.kv_dtype),
+                            as_f64(c.v, c.kv_dtype), c.scale)
+
+
+def test_workload1_tiny_fp32(da):
+    c = synth.workload1()
+    assert_close(run(da, c), oracle_of(c), atol=1e-5, rel_rms=1e-4, what="tiny fp32")
+
+
+CASES = [
+    # B, Hq, Hkv, D, N, q, kv, split_tokens
+    (2, 8, 2, 128, 1000, "f32", "bf16", 0),     # ragged tail, 2 splits
+    (1, 4, 1, 64, 1, "f32", "f32", 0),          # a single token
+    (3, 16, 2, 64, 777, "f16", "f16", 128),     # G = 8, fp16 q
+    (2, 4, 4, 128, 300, "f32", "f16", 16),      # MHA, 19 splits of 16
+    (2, 8, 8, 64, 2049, "bf16", "bf16", 0),     # bf16 q, one token past a split
+    (1, 8, 1, 128, 5000, "f32", "bf16", 1024),  # G = 8 with fp32 q split in two terms
+    (2, 2, 1, 64, 129, "f32", "f32", 32),
+    (1, 32, 8, 128, 4096, "f32", "bf16", 512),  # the Llama-3-8B layer, short context
+    (2, 16, 8, 128, 333, "f32", "f32", 0),      # fp32 cache, G = 2
+    (1, 8, 2, 64, 70, "f32", "f16", 64),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,N,qd,kd,st", CASES)
+def test_small_shapes(da, B, Hq, Hkv, D, N, qd, kd, st):
+    c = synth.dense_case([100, B, Hq, Hkv, D, N], B, Hq, Hkv, D, N, qd, kd)
+    assert_close(run(da, c, st), oracle_of(c), atol=1e-5, rel_rms=1e-4,
+                 what=f"B{B} Hq{Hq} Hkv{Hkv} D{D} N{N} {qd}/{kd} split{st}")
+
+
+def test_peaked_softmax_and_large_scores(da):
+    # one token per head scores ~ +60 above the rest: every other weight
+    # underflows; exercise the -inf / rescale paths
+    c = synth.dense_case([101], 2, 8, 2, 128, 900, "f32", "f32")
+    q64 = as_f64(c.q, "f32")
+    for b in range(2):
+        for h in range(2):
+            u = q64[b, h * 4] / np.linalg.norm(q64[b, h * 4])
+            c.k[b, h, 613] = (60.0 * u).astype(np.float32)     # score ~ +60 for head h*4
+    assert_close(run(da, c, 64), oracle_of(c), atol=1e-5, rel_rms=1e-4, what="peaked")
+
+
+def test_constant_values_and_zero_query(da):
+    c = synth.dense_case([102], 1, 4, 2, 64, 500, "f32", "bf16")
+    c.q[0, 0] = 0.0
+    c.v[0, 1] = c.v[0, 1, 7]                     # KV head 1: every value row equal
+    got = run(da, c)
+    ref = oracle_of(c)
+    assert_close(got, ref, atol=1e-5, rel_rms=1e-4, what="const")
+    np.testing.assert_allclose(got[0, 2], as_f64(c.v[0, 1, 7], "bf16"), atol=1e-6)
+
+
+def test_deterministic(da):
+    c = synth.dense_case([103], 2, 8, 2, 128, 3000, "f32", "bf16")
+    a = run(da, c)
+    b = run(da, c)
+    assert np.array_equal(a, b)
+
+
+def test_split_sizes_agree(da):
+    c = synth.dense_case([104], 1, 8, 2, 128, 2500, "f32", "bf16")
+    ref = oracle_of(c)
+    for st in (16, 48, 512, 4096):
+        assert_close(run(da, c, st), ref, atol=1e-5, rel_rms=1e-4, what=f"split {st}")
+
+
+def test_workload2_full_size_sampled(da):
+    """The Llama-3-8B layer at 32K context, in the benchmark's launch
+    configuration (default split), checked on sampled (row, head) pairs."""
+    c = synth.workload2()
+    got = run(da, c)
+    rng = np.random.default_rng(2)
+    picks = [(int(b), int(j)) for b, j in zip(rng.integers(0, 8, 6), rng.integers(0, 32, 6))]
+    picks += [(0, 0), (7, 31)]
+    for b, j in picks:
+        h = j // 4
+        q = as_f64(c.q[b:b + 1, j:j + 1], "f32")
+        k = as_f64(c.k[b:b + 1, h:h + 1], "bf16")
+        v = as_f64(c.v[b:b + 1, h:h + 1], "bf16")
+        ref = decode_attention(q, k, v, c.scale)[0, 0]
+        assert_close(got[b, j], ref, atol=1e-3, rel_rms=1e-4, what=f"w2 b{b} j{j}")
