@@ -1,0 +1,420 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+Headline (one JSON line on stdout): the Llama-3-8B-shaped decode-attention
+layer -- batch 8, 32 query / 8 KV heads, head_dim 128, 32768 cached tokens,
+bf16 K/V, fp32 q -- one step = da_decode_attention over the whole cache
+(split-K partial pass + merge).  `value` is algorithmic KV bytes moved per
+second (K + V + q + o per step / step time) with the inputs resident in HBM.
+
+Also reported, in "extra": the page-sparse step (bound-score selection + sparse
+attention, TinyServe shape), the uint4 step (FlexGen shape) and the head-wise
+streamed step (HeadInfer shape, 32 layers x 8 KV heads at 1M tokens streamed
+from pinned host memory), each with its own bytes/s and roofline fraction.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-extra] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+PCIE_GEN5_X16_GBS = 64.0       # nominal per direction
+
+METRIC = "decode-attention KV bytes/s (fraction of HBM/PCIe peak); tokens/s at 32K ctx"
+
+
+def cpu_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    return min(n, int(env)) if env and env.isdigit() and int(env) > 0 else n
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def up(arr, dtype, torch, np):
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr))
+    return t.cuda()
+
+
+def time_events(torch, fn, steps: int, warmup: int, stream=None) -> float:
+    """Average ms per call of fn(i), with HIP events on `stream` around all calls."""
+    stream = stream or torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(steps):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def time_each(torch, fn, steps: int, stream=None) -> float:
+    """Mean of per-launch event durations (events recorded on `stream`)."""
+    stream = stream or torch.cuda.current_stream()
+    evs = []
+    for i in range(steps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return statistics.fmean(x.elapsed_time(y) for x, y in evs)
+
+
+# ---------------------------------------------------------------------------
+# headline: dense GQA decode attention, Llama-3-8B layer at 32K
+# ---------------------------------------------------------------------------
+def bench_dense(args, torch, np, da, synth):
+    log("workload: llama3-8b layer decode, B8 Hq32 Hkv8 D128 N32768 bf16 KV")
+    t0 = time.time()
+    c = synth.workload2()
+    log(f"generated inputs in {time.time() - t0:.1f}s")
+    B, Hq, Hkv, D, N = c.shape
+    q = up(c.q, "f32", torch, np)
+    ks = [up(c.k, "bf16", torch, np)]
+    vs = [up(c.v, "bf16", torch, np)]
+    # second resident copy: consecutive steps alternate, so the 256 MB
+    # last-level cache cannot serve a repeated cache
+    ks.append(ks[0].clone())
+    vs.append(vs[0].clone())
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    ns = da.da_decode_attention_n_split(B, Hq, Hkv, D, N)
+    ws = torch.empty((B, Hq, ns, D + 4), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        da.da_decode_attention(q, ks[i & 1], vs[i & 1], scale=c.scale, out=out, ws=ws)
+
+    ms = time_events(torch, step, args.steps, args.warmup)
+
+    def partial(i):
+        da.da_decode_attention_partials(q, ks[i & 1], vs[i & 1], scale=c.scale, ws=ws)
+
+    for i in range(3):
+        partial(i)
+    ms_partial = time_each(torch, partial, args.steps)
+
+    def merge(i):
+        da.da_merge_partials(ws, out=out)
+
+    ms_merge = time_each(torch, merge, args.steps)
+
+    kv_bytes = 2 * B * Hkv * N * D * 2
+    q_bytes = B * Hq * D * 4
+    o_bytes = B * Hq * D * 4
+    step_bytes = kv_bytes + q_bytes + o_bytes
+    part_bytes = kv_bytes + q_bytes
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    part_gbs = part_bytes / (ms_partial * 1e-3) / 1e9
+    res = {
+        "ms_per_step": ms, "gbs": gbs, "tokens_per_s": B / (ms * 1e-3),
+        "step_bytes": step_bytes, "partial_ms": ms_partial, "partial_bytes": part_bytes,
+        "partial_gbs": part_gbs, "merge_ms": ms_merge, "n_split": ns,
+    }
+    log(f"dense: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s); "
+        f"partial pass {ms_partial * 1e3:.1f} us ({part_gbs:.0f} GB/s), merge {ms_merge * 1e3:.1f} us")
+    return c, res
+
+
+def cpu_baseline_dense(c, np):
+    """The fp64 oracle on batch row 0 of the same workload (all 32 query heads)."""
+    from oracle import decode_attention
+    from oracle.numerics import as_f64
+
+    def once():
+        t = time.perf_counter()
+        decode_attention(as_f64(c.q[0:1], "f32"), as_f64(c.k[0:1], "bf16"),
+                         as_f64(c.v[0:1], "bf16"), c.scale)
+        return time.perf_counter() - t
+
+    once()
+    runs = [once() for _ in range(3)]
+    sec = statistics.median(runs)
+    B, Hq, Hkv, D, N = c.shape
+    sample_bytes = 2 * Hkv * N * D * 2 + Hq * D * 4 * 2
+    return {
+        "value": sample_bytes / sec / 1e9, "unit": "GB/s", "cores": cpu_threads(), "kind": "oracle",
+        "sample": f"batch row 0 of {B} (all {Hq} query heads over {N} tokens), median of 3 runs "
+                  f"after 1 warm-up, {sec:.2f} s per run",
+        "tokens_per_s": 1.0 / sec,
+    }
+
+
+# ---------------------------------------------------------------------------
+# extra: page-sparse (TinyServe shape)
+# ---------------------------------------------------------------------------
+def bench_sparse(args, torch, np, da, synth):
+    log("extra: page-sparse decode, B32 H16 D64 N32768 fp16, page 16, top-128")
+    t0 = time.time()
+    c = synth.workload3()
+    log(f"generated inputs in {time.time() - t0:.1f}s")
+    B, H, _, D, N = c.shape
+    S, K = c.page_size, c.top_k
+    q = up(c.q, "f16", torch, np)
+    k0 = up(c.k, "f16", torch, np)
+    v0 = up(c.v, "f16", torch, np)
+    del c
+    copies = [(k0, v0), (k0.clone(), v0.clone())]
+    metas = []
+    for kk, _ in copies:
+        metas.append(da.da_build_page_meta(kk, S))
+    ms_meta = time_events(torch, lambda i: da.da_build_page_meta(copies[0][0], S, *metas[0]), 5, 1)
+    P = -(-N // S)
+    idx = torch.empty((B, H, K), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+    wsz = 4 * B * H * D
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        kk, vv = copies[i & 1]
+        mn, mx = metas[i & 1]
+        da.da_select_pages(q, mn, mx, S, K, N, page_idx=idx)
+        da.da_decode_attention_paged(q, kk, vv, idx, S, out=out, ws=ws)
+
+    ms = time_events(torch, step, args.steps, args.warmup)
+
+    def sel(i):
+        mn, mx = metas[i & 1]
+        da.da_select_pages(q, mn, mx, S, K, N, page_idx=idx)
+
+    ms_sel = time_each(torch, sel, args.steps)
+
+    def gather(i):
+        kk, vv = copies[i & 1]
+        da.da_decode_attention_paged(q, kk, vv, idx, S, out=out, ws=ws)
+
+    ms_gather = time_each(torch, gather, args.steps)
+    wsd = torch.empty(1 << 26, dtype=torch.uint8, device="cuda")
+
+    def dense(i):
+        kk, vv = copies[i & 1]
+        da.da_decode_attention(q, kk, vv, out=out, ws=wsd)
+
+    ms_dense = time_events(torch, dense, max(5, args.steps // 4), 2)
+    meta_bytes = 2 * B * H * P * D * 2
+    sel_kv_bytes = 2 * B * H * K * S * D * 2
+    step_bytes = meta_bytes + sel_kv_bytes + B * H * D * 2 + wsz + 2 * B * H * K * 4
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    res = {
+        "workload": "tinyserve-page-sparse B32 H16 D64 N32768 fp16 page16 top128",
+        "ms_per_step": ms, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "step_bytes": step_bytes,
+        "tokens_per_s": B / (ms * 1e-3),
+        "select_ms": ms_sel, "select_gbs": (meta_bytes + B * H * D * 2) / (ms_sel * 1e-3) / 1e9,
+        "gather_attention_ms": ms_gather,
+        "gather_gbs": (sel_kv_bytes + B * H * D * 6) / (ms_gather * 1e-3) / 1e9,
+        "page_meta_ms": ms_meta, "dense_same_cache_ms": ms_dense,
+        "speedup_vs_dense": ms_dense / ms,
+    }
+    log(f"sparse: {ms * 1e3:.1f} us/step ({gbs:.0f} GB/s), select {ms_sel * 1e3:.1f} us, "
+        f"gather {ms_gather * 1e3:.1f} us, dense on same cache {ms_dense * 1e3:.1f} us")
+    return res
+
+
+# ---------------------------------------------------------------------------
+# extra: uint4 KV (FlexGen shape)
+# ---------------------------------------------------------------------------
+def bench_kv4(args, torch, np, da, synth):
+    log("extra: uint4 KV decode, B64 H56 D128 N1024")
+    t0 = time.time()
+    c = synth.workload4()
+    log(f"generated inputs in {time.time() - t0:.1f}s")
+    B, H, _, D, N = c.shape
+    q = up(c.q, "f16", torch, np)
+    k = up(c.k, "f16", torch, np)
+    v = up(c.v, "f16", torch, np)
+    del c
+    ms_quant = time_events(torch, lambda i: da.da_quantize_kv4(k), 5, 1)
+    copies = [da.da_quantize_kv4(k) + da.da_quantize_kv4(v) for _ in range(2)]
+    out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(1 << 26, dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        kc, kmn, ksc, vc, vmn, vsc = copies[i & 1]
+        da.da_decode_attention_kv4(q, kc, kmn, ksc, vc, vmn, vsc, out=out, ws=ws)
+
+    ms = time_events(torch, step, args.steps, args.warmup)
+    code_bytes = 2 * B * H * N * D // 2
+    ms_bytes = 2 * 2 * B * H * N * (D // 64) * 2
+    step_bytes = code_bytes + ms_bytes + B * H * D * 2 + B * H * D * 4
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    del k, v
+    res = {"workload": "flexgen-uint4 B64 H56 D128 N1024 groups of 64", "ms_per_step": ms,
+           "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "step_bytes": step_bytes,
+           "tokens_per_s": B / (ms * 1e-3), "quantize_k_ms": ms_quant}
+    log(f"kv4: {ms * 1e3:.1f} us/step ({gbs:.0f} GB/s)")
+    return res
+
+
+# ---------------------------------------------------------------------------
+# extra: head-wise streamed (HeadInfer shape)
+# ---------------------------------------------------------------------------
+def bench_stream(args, torch, np, da, synth):
+    spec = synth.workload5()
+    pool_heads = args.stream_pool_heads
+    log(f"extra: head-wise streamed decode, 32 layers x 8 KV heads, N {spec.n_ctx}, bf16; "
+        f"pinned pool of {pool_heads} layer-heads")
+    hb = spec.head_bytes
+    t0 = time.time()
+    kh, vh = [], []
+    for i in range(pool_heads):
+        kh.append(torch.empty((spec.batch, spec.n_ctx, spec.head_dim), dtype=torch.bfloat16,
+                              pin_memory=True))
+        vh.append(torch.empty_like(kh[-1], pin_memory=True))
+    log(f"pinned {2 * pool_heads * hb / 2**30:.1f} GiB in {time.time() - t0:.1f}s")
+    t0 = time.time()
+
+    import concurrent.futures as cf
+
+    def fill(i):
+        l, h = divmod(i, spec.n_kv_heads)
+        spec.head(l, h, kh[i].view(torch.int16).numpy().view(np.uint16),
+                  vh[i].view(torch.int16).numpy().view(np.uint16))
+
+    with cf.ThreadPoolExecutor(min(16, cpu_threads())) as ex:
+        list(ex.map(fill, range(pool_heads)))
+    log(f"filled pool in {time.time() - t0:.1f}s")
+
+    # measured pinned H2D peak: one 512 MiB copy per call on a copy stream
+    dev = torch.empty((hb // 2,), dtype=torch.bfloat16, device="cuda")
+    cs = torch.cuda.Stream()
+    src = kh[0].view(-1)
+
+    def h2d(i):
+        with torch.cuda.stream(cs):
+            dev.copy_(src, non_blocking=True)
+
+    h2d_ms = time_events(torch, h2d, 6, 2, stream=cs)
+    h2d_gbs = hb / (h2d_ms * 1e-3) / 1e9
+
+    hs = da.HeadwiseStream(spec.batch, spec.n_q_heads, spec.n_kv_heads, spec.head_dim, spec.n_ctx,
+                           da.DA_F32, da.DA_BF16, heads_per_chunk=1)
+    nb = hs.buffer_bytes
+    buf0 = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    buf1 = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    q = up(spec.q(), "f32", torch, np)
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(16, hs.workspace_bytes), dtype=torch.uint8, device="cuda")
+    L, H = spec.n_layers, spec.n_kv_heads
+    k_list = [kh[(i) % pool_heads] for i in range(L * H)]
+    v_list = [vh[(i) % pool_heads] for i in range(L * H)]
+    comp = torch.cuda.current_stream()
+    cpy = torch.cuda.Stream()
+
+    def step(i):
+        cpy.wait_stream(comp)
+        hs.da_stream_headwise(k_list, v_list, buf0, buf1, q, out, ws, comp, cpy)
+
+    steps = args.stream_steps
+    ms = time_events(torch, step, steps, 1)
+    total = 2 * L * H * hb
+    gbs = total / (ms * 1e-3) / 1e9
+    hs.close()
+    res = {"workload": "headinfer-headwise L32 Hkv8 Hq32 D128 N1048576 bf16 B1",
+           "ms_per_step": ms, "h2d_bytes_per_step": total, "h2d_gbs": gbs,
+           "measured_h2d_peak_gbs": h2d_gbs, "frac_measured_h2d": gbs / h2d_gbs,
+           "frac_pcie_gen5_nominal": gbs / PCIE_GEN5_X16_GBS, "tokens_per_s": 1.0 / (ms * 1e-3),
+           "steps": steps,
+           "pool": f"{pool_heads} distinct pinned layer-heads ({2 * pool_heads * hb / 2**30:.0f} GiB) "
+                   f"reused cyclically for the 256 layer-heads of a step; every layer-head is a real "
+                   f"512 MiB H2D copy"}
+    log(f"stream: {ms:.0f} ms/step, {gbs:.1f} GB/s H2D vs measured peak {h2d_gbs:.1f} GB/s")
+    return res
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-stream", action="store_true", help="skip the head-wise streamed workload")
+    ap.add_argument("--stream-pool-heads", type=int, default=16)
+    ap.add_argument("--stream-steps", type=int, default=2)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding is a design note only)"}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    import sparse_kv_cache_gqa_amd as da
+    import synth
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 1
+    da.load()
+    torch.cuda.set_device(0)
+
+    c, dense = bench_dense(args, torch, np, da, synth)
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle on a sample")
+        cpu = cpu_baseline_dense(c, np)
+        log(f"cpu oracle: {cpu['value']:.2f} GB/s on {cpu['cores']} threads")
+    del c
+    extra = {}
+    if not args.no_extra:
+        for name, fn in (("page_sparse", bench_sparse), ("uint4", bench_kv4)):
+            torch.cuda.empty_cache()
+            extra[name] = fn(args, torch, np, da, synth)
+        if not args.no_stream:
+            torch.cuda.empty_cache()
+            extra["headwise_stream"] = bench_stream(args, torch, np, da, synth)
+
+    line = {
+        "metric": METRIC,
+        "value": dense["gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dense["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3-8b-layer-decode-32k", "batch": 8, "n_q_heads": 32,
+                   "n_kv_heads": 8, "head_dim": 128, "n_ctx": 32768, "kv_dtype": "bf16",
+                   "q_dtype": "f32", "accumulate": "f32", "parallelism": "single-gpu"},
+        "tokens_per_s": dense["tokens_per_s"],
+        "roofline": {"bound": "hbm", "achieved": dense["partial_gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": dense["partial_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "attn_split_kernel (split-K partial pass)",
+                     "bytes_per_launch": dense["partial_bytes"], "avg_launch_ms": dense["partial_ms"]},
+        "cpu_baseline": cpu,
+        "detail": {k: v for k, v in dense.items() if k not in ("gbs",)},
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -84,10 +84,11 @@ typedef enum da_dtype { DA_F32 = 0, DA_F16 = 1, DA_BF16 = 2 } da_dtype;
  *   row, KV head); scale > 0 (normally 1/sqrt(head_dim)); q_dtype is DA_F32
  *   or kv_dtype; split_tokens is the number of tokens (dense) or selected
  *   token positions (paged) one workgroup reduces before the cross-split
- *   merge: 0 selects the default (512); otherwise a multiple of 16 in
- *   [16, 65536].  It depends only on this field, never on batch or heads, so
- *   a call over one head and a call over all heads give bitwise-equal
- *   results for that head. */
+ *   merge: 0 selects the entry point's default (dense and head-wise: the
+ *   power of two nearest above n_ctx/16 within [256, 2048]; uint4 512;
+ *   paged 256); otherwise a multiple of 16 in [16, 65536].  The
+ *   split never depends on batch or head counts, so a call over one head and
+ *   a call over all heads give bitwise-equal results for that head. */
 typedef struct da_attn_shape {
     int32_t batch;
     int32_t n_q_heads;
@@ -121,6 +122,30 @@ size_t da_decode_attention_workspace(const da_attn_shape *s);
 da_status da_decode_attention(const da_attn_shape *s, const void *q,
                               const void *k, const void *v, float *o,
                               void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * The two halves of da_decode_attention, for callers that merge partials
+ * themselves (for example partials computed over different token ranges, on
+ * different devices, of one sequence) or time the passes apart.
+ *
+ * da_decode_attention_partials: the split-K pass only.  Writes, for every
+ *   query-head row r = b * n_q_heads + j and split i (tokens
+ *   [i * split, min((i+1) * split, n_ctx)), split = split_tokens or 512),
+ *   ws[r][i][0..head_dim+3] fp32 = (u[0..head_dim-1], m, l, pad, pad)
+ *   with m = max_t x_t, l = sum_t 2^(x_t - m), u = sum_t 2^(x_t - m) v_t and
+ *   x_t = scale * log2(e) * q . k_t (base-2 logits).  n_split is
+ *   da_decode_attention_n_split(s); ws as for da_decode_attention.
+ * da_merge_partials: o[r] = sum_i 2^(m_i - M) u_i / sum_i 2^(m_i - M) l_i,
+ *   M = max_i m_i, for rows r < rows, partials [rows][n_split][head_dim+4]
+ *   fp32 (device), o [rows][head_dim] fp32 (device).  A split with
+ *   m = -inf contributes nothing.  head_dim in {64, 128}.
+ * ------------------------------------------------------------------------ */
+int32_t da_decode_attention_n_split(const da_attn_shape *s);
+da_status da_decode_attention_partials(const da_attn_shape *s, const void *q,
+                                       const void *k, const void *v, void *ws,
+                                       size_t ws_bytes, hipStream_t stream);
+da_status da_merge_partials(int64_t rows, int32_t n_split, int32_t head_dim,
+                            const void *partials, float *o, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Page metadata (TinyServe phi(K_j) = (m_j, M_j)): per page of page_size

@@ -42,6 +42,9 @@ SIGNATURES = {
     "da_last_error": (ctypes.c_char_p, []),
     "da_decode_attention_workspace": (c_sz, [SHAPE]),
     "da_decode_attention": (ctypes.c_int, [SHAPE, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "da_decode_attention_n_split": (c_i32, [SHAPE]),
+    "da_decode_attention_partials": (ctypes.c_int, [SHAPE, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "da_merge_partials": (ctypes.c_int, [c_i64, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "da_build_page_meta": (ctypes.c_int, [SHAPE, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "da_select_pages": (ctypes.c_int, [SHAPE, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "da_decode_attention_paged_workspace": (c_sz, [SHAPE, c_i32, c_i32]),

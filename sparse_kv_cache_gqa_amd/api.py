@@ -60,6 +60,10 @@ def _expect(t, shape, dtype, name):
         raise ValueError(f"{name}: expected {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
 def _ws(nbytes: int, device):
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
@@ -79,7 +83,45 @@ def da_decode_attention(q, k, v, scale=None, split_tokens=0, out=None, ws=None, 
     if ws is None:
         ws = _ws(need, q.device)
     check(lib.da_decode_attention(ctypes.byref(s), _vp(q), _vp(k), _vp(v), _vp(out), _vp(ws),
-                                  ws.numel(), _stream(stream)))
+                                  _nbytes(ws), _stream(stream)))
+    return out
+
+
+def da_decode_attention_n_split(batch, n_q_heads, n_kv_heads, head_dim, n_ctx, split_tokens=0) -> int:
+    s = attn_shape(batch, n_q_heads, n_kv_heads, head_dim, n_ctx, None, DA_F32, DA_BF16, split_tokens)
+    return int(load().da_decode_attention_n_split(ctypes.byref(s)))
+
+
+def da_decode_attention_partials(q, k, v, scale=None, split_tokens=0, ws=None, stream=None):
+    """Split-K pass only: fp32 partials [B][Hq][n_split][D+4] = (u[D], m, l, pad, pad)."""
+    lib = load()
+    _dev(q, k, v, ws)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must have the same shape and dtype")
+    s = _dense_shape(q, k, scale, split_tokens)
+    ns = int(lib.da_decode_attention_n_split(ctypes.byref(s)))
+    shape = (q.shape[0], q.shape[1], ns, q.shape[2] + 4)
+    _expect(ws, shape, torch.float32, "ws")
+    if ws is None:
+        ws = torch.empty(shape, dtype=torch.float32, device=q.device)
+    check(lib.da_decode_attention_partials(ctypes.byref(s), _vp(q), _vp(k), _vp(v), _vp(ws),
+                                           _nbytes(ws), _stream(stream)))
+    return ws
+
+
+def da_merge_partials(partials, out=None, stream=None):
+    """partials [..., n_split, D+4] fp32 -> o [..., D] fp32."""
+    lib = load()
+    _dev(partials, out)
+    if partials.dtype != torch.float32:
+        raise ValueError("partials must be float32")
+    ns, D = partials.shape[-2], partials.shape[-1] - 4
+    lead = tuple(partials.shape[:-2])
+    rows = partials.numel() // (ns * (D + 4))
+    _expect(out, lead + (D,), torch.float32, "out")
+    if out is None:
+        out = torch.empty(lead + (D,), dtype=torch.float32, device=partials.device)
+    check(lib.da_merge_partials(rows, ns, D, _vp(partials), _vp(out), _stream(stream)))
     return out
 
 
@@ -139,7 +181,7 @@ def da_decode_attention_paged(q, k, v, page_idx, page_size, scale=None, split_to
     if ws is None:
         ws = _ws(need, q.device)
     check(lib.da_decode_attention_paged(ctypes.byref(s), page_size, top_k, _vp(page_idx), _vp(q),
-                                        _vp(k), _vp(v), _vp(out), _vp(ws), ws.numel(),
+                                        _vp(k), _vp(v), _vp(out), _vp(ws), _nbytes(ws),
                                         _stream(stream)))
     return out
 
@@ -208,7 +250,7 @@ def da_decode_attention_kv4(q, k_codes, k_min, k_scale, v_codes, v_min, v_scale,
         ws = _ws(need, q.device)
     check(lib.da_decode_attention_kv4(ctypes.byref(s), _vp(q), _vp(k_codes), _vp(k_min),
                                       _vp(k_scale), _vp(v_codes), _vp(v_min), _vp(v_scale),
-                                      _vp(out), _vp(ws), ws.numel(), _stream(stream)))
+                                      _vp(out), _vp(ws), _nbytes(ws), _stream(stream)))
     return out
 
 
@@ -263,7 +305,7 @@ class HeadwiseStream:
         vp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in v_host])
         check(self._lib.da_stream_headwise(self._ctx, n // self.shape.n_kv_heads, kp, vp,
                                            _vp(buf0), _vp(buf1), _vp(q), _vp(out), _vp(ws),
-                                           ws.numel(), _stream(compute), _stream(copy)))
+                                           _nbytes(ws), _stream(compute), _stream(copy)))
         return out
 
     def close(self):

@@ -78,8 +78,10 @@ da_status check_shape(const da_attn_shape *s, bool kv4) {
     return DA_OK;
 }
 
-int32_t split_tokens_of(const da_attn_shape *s) {
-    return s->split_tokens ? s->split_tokens : kDefaultSplitTokens;
+int32_t split_tokens_of(const da_attn_shape *s, int mode) {
+    if (s->split_tokens) return s->split_tokens;
+    return mode == SPLIT_PAGED ? kDefaultSplitPaged
+                               : (mode == SPLIT_U4 ? kDefaultSplitU4 : default_split_dense(s->n_ctx));
 }
 
 da_status check_ptr(const void *p, const char *name) {
@@ -96,7 +98,7 @@ da_status check_page(int32_t page_size) {
 
 int64_t n_pages(const da_attn_shape *s, int32_t page_size) { return (s->n_ctx + page_size - 1) / page_size; }
 
-AttnLaunch dense_launch(const da_attn_shape *s, int kv_fmt) {
+AttnLaunch dense_launch(const da_attn_shape *s, int kv_fmt, int mode) {
     AttnLaunch a;
     a.B = s->batch;
     a.Hkv = s->n_kv_heads;
@@ -110,7 +112,7 @@ AttnLaunch dense_launch(const da_attn_shape *s, int kv_fmt) {
     a.o_bstride = (int64_t)s->n_q_heads * s->head_dim;
     a.kv_bstride = (int64_t)s->n_kv_heads * s->n_ctx;
     a.kv_hstride = s->n_ctx;
-    a.split_tokens = split_tokens_of(s);
+    a.split_tokens = split_tokens_of(s, mode);
     a.n_split = attn_n_split(s->n_ctx, a.split_tokens, false, 0, 0);
     return a;
 }
@@ -139,8 +141,8 @@ const char *da_last_error(void) { return g_err; }
 
 size_t da_decode_attention_workspace(const da_attn_shape *s) {
     if (check_shape(s, false) != DA_OK) return 0;
-    return attn_ws_bytes((int64_t)s->batch * s->n_q_heads, attn_n_split(s->n_ctx, split_tokens_of(s), false, 0, 0),
-                         s->head_dim);
+    return attn_ws_bytes((int64_t)s->batch * s->n_q_heads,
+                         attn_n_split(s->n_ctx, split_tokens_of(s, SPLIT_DENSE), false, 0, 0), s->head_dim);
 }
 
 da_status da_decode_attention(const da_attn_shape *s, const void *q, const void *k, const void *v, float *o,
@@ -154,7 +156,7 @@ da_status da_decode_attention(const da_attn_shape *s, const void *q, const void 
     DA_TRY(check_ptr(ws, "ws"));
     const size_t need = da_decode_attention_workspace(s);
     if (ws_bytes < need) return fail(DA_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-    AttnLaunch a = dense_launch(s, s->kv_dtype);
+    AttnLaunch a = dense_launch(s, s->kv_dtype, SPLIT_DENSE);
     if (!attn_supported(a.kv_fmt, a.q_fmt, a.D, a.G, false))
         return fail(DA_E_UNSUPPORTED, "no kernel for this dtype / head_dim / group combination");
     a.q = q;
@@ -164,6 +166,47 @@ da_status da_decode_attention(const da_attn_shape *s, const void *q, const void 
     a.ws = (float *)ws;
     hipError_t e = launch_attention(a, stream);
     if (e != hipSuccess) return hip_fail(e, "decode attention launch");
+    return ok();
+}
+
+da_status da_decode_attention_partials(const da_attn_shape *s, const void *q, const void *k, const void *v,
+                                       void *ws, size_t ws_bytes, hipStream_t stream) {
+    DA_TRY(check_shape(s, false));
+    if (s->batch == 0) return ok();
+    DA_TRY(check_ptr(q, "q"));
+    DA_TRY(check_ptr(k, "k"));
+    DA_TRY(check_ptr(v, "v"));
+    DA_TRY(check_ptr(ws, "ws"));
+    const size_t need = da_decode_attention_workspace(s);
+    if (ws_bytes < need) return fail(DA_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    AttnLaunch a = dense_launch(s, s->kv_dtype, SPLIT_DENSE);
+    if (!attn_supported(a.kv_fmt, a.q_fmt, a.D, a.G, false))
+        return fail(DA_E_UNSUPPORTED, "no kernel for this dtype / head_dim / group combination");
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.ws = (float *)ws;
+    hipError_t e = launch_split(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "partial pass launch");
+    return ok();
+}
+
+int32_t da_decode_attention_n_split(const da_attn_shape *s) {
+    if (check_shape(s, false) != DA_OK) return 0;
+    return attn_n_split(s->n_ctx, split_tokens_of(s, SPLIT_DENSE), false, 0, 0);
+}
+
+da_status da_merge_partials(int64_t rows, int32_t n_split, int32_t head_dim, const void *partials, float *o,
+                            hipStream_t stream) {
+    if (rows < 0) return fail(DA_E_INVALID, "rows %lld < 0", (long long)rows);
+    if (n_split < 1) return fail(DA_E_INVALID, "n_split %d < 1", n_split);
+    if (head_dim != 64 && head_dim != 128) return fail(DA_E_UNSUPPORTED, "head_dim %d not supported", head_dim);
+    if (rows > 0x7FFFFFFF) return fail(DA_E_UNSUPPORTED, "rows %lld too many", (long long)rows);
+    if (rows == 0) return ok();
+    DA_TRY(check_ptr(partials, "partials"));
+    DA_TRY(check_ptr(o, "o"));
+    hipError_t e = launch_merge(rows, 1, n_split, head_dim, (const float *)partials, o, head_dim, stream);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
     return ok();
 }
 
@@ -208,7 +251,7 @@ da_status da_select_pages(const da_attn_shape *s, int32_t page_size, int32_t top
 size_t da_decode_attention_paged_workspace(const da_attn_shape *s, int32_t page_size, int32_t top_k) {
     if (check_shape(s, false) != DA_OK || check_page(page_size) != DA_OK) return 0;
     if (top_k < 1 || top_k > n_pages(s, page_size)) return 0;
-    const int32_t ns = attn_n_split(s->n_ctx, split_tokens_of(s), true, top_k, ilog2(page_size));
+    const int32_t ns = attn_n_split(s->n_ctx, split_tokens_of(s, SPLIT_PAGED), true, top_k, ilog2(page_size));
     return attn_ws_bytes((int64_t)s->batch * s->n_q_heads, ns, s->head_dim);
 }
 
@@ -230,7 +273,7 @@ da_status da_decode_attention_paged(const da_attn_shape *s, int32_t page_size, i
     DA_TRY(check_ptr(ws, "ws"));
     const size_t need = da_decode_attention_paged_workspace(s, page_size, top_k);
     if (ws_bytes < need) return fail(DA_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-    AttnLaunch a = dense_launch(s, s->kv_dtype);
+    AttnLaunch a = dense_launch(s, s->kv_dtype, SPLIT_PAGED);
     if (!attn_supported(a.kv_fmt, a.q_fmt, a.D, a.G, true))
         return fail(DA_E_UNSUPPORTED, "no paged kernel for this dtype / head_dim");
     a.page_idx = page_idx;
@@ -277,8 +320,8 @@ da_status da_dequantize_kv4(int64_t n_rows, int32_t row_len, const uint8_t *code
 
 size_t da_decode_attention_kv4_workspace(const da_attn_shape *s) {
     if (check_shape(s, true) != DA_OK) return 0;
-    return attn_ws_bytes((int64_t)s->batch * s->n_q_heads, attn_n_split(s->n_ctx, split_tokens_of(s), false, 0, 0),
-                         s->head_dim);
+    return attn_ws_bytes((int64_t)s->batch * s->n_q_heads,
+                         attn_n_split(s->n_ctx, split_tokens_of(s, SPLIT_U4), false, 0, 0), s->head_dim);
 }
 
 da_status da_decode_attention_kv4(const da_attn_shape *s, const void *q, const uint8_t *k_codes, const void *k_min,
@@ -297,7 +340,7 @@ da_status da_decode_attention_kv4(const da_attn_shape *s, const void *q, const u
     DA_TRY(check_ptr(ws, "ws"));
     const size_t need = da_decode_attention_kv4_workspace(s);
     if (ws_bytes < need) return fail(DA_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-    AttnLaunch a = dense_launch(s, FMT_U4);
+    AttnLaunch a = dense_launch(s, FMT_U4, SPLIT_U4);
     if (!attn_supported(a.kv_fmt, a.q_fmt, a.D, a.G, false))
         return fail(DA_E_UNSUPPORTED, "no uint4 kernel for this q dtype / group size");
     a.q = q;

@@ -16,8 +16,9 @@ da_status hip_fail(hipError_t e, const char *what);
 da_status check_shape(const da_attn_shape *s, bool kv4);
 da_status check_ptr(const void *p, const char *name);
 int esize(int dtype);
-int32_t split_tokens_of(const da_attn_shape *s);
-AttnLaunch dense_launch(const da_attn_shape *s, int kv_fmt);
+enum SplitMode { SPLIT_DENSE = 0, SPLIT_U4 = 1, SPLIT_PAGED = 2 };
+int32_t split_tokens_of(const da_attn_shape *s, int mode);
+AttnLaunch dense_launch(const da_attn_shape *s, int kv_fmt, int mode);
 
 }  // namespace da
 

@@ -10,7 +10,15 @@ namespace da {
 // Storage formats of q and of the KV cache.  Values 0..2 equal da_dtype.
 enum Fmt : int { FMT_F32 = 0, FMT_F16 = 1, FMT_BF16 = 2, FMT_U4 = 3 };
 
-constexpr int kDefaultSplitTokens = 512;
+// Default tokens (dense) or selected positions (paged) per split.  They depend
+// only on the entry point and the context length, never on batch or head
+// counts.  Dense: the power of two nearest above n_ctx / 16, within
+// [256, 2048] (long splits amortise each wave's set-up and keep the partials
+// small); uint4 and paged: fixed.
+constexpr int kDefaultSplitDenseMin = 256;
+constexpr int kDefaultSplitDense = 2048;
+constexpr int kDefaultSplitU4 = 512;
+constexpr int kDefaultSplitPaged = 256;
 
 // One attention launch (split-K partial pass + cross-split merge).
 // The KV cache is addressed by rows (tokens): row r of (batch b, KV head h)
@@ -35,10 +43,12 @@ struct AttnLaunch {
     const int32_t *page_idx = nullptr;
     int32_t top_k = 0, log2_page = 0;
 
-    int32_t split_tokens = kDefaultSplitTokens;
+    int32_t split_tokens = kDefaultSplitDense;
     int32_t n_split = 0;
-    float *ws = nullptr;           // [B*Hkv*G][n_split][D+2]
+    float *ws = nullptr;           // [B*Hkv*G][n_split][D+4]
 };
+
+int32_t default_split_dense(int64_t n_ctx);
 
 // Number of splits and workspace bytes for a launch description.
 int32_t attn_n_split(int64_t n_ctx, int32_t split_tokens, bool paged,
@@ -48,7 +58,15 @@ size_t attn_ws_bytes(int64_t rows, int32_t n_split, int32_t D);
 // True if a kernel is built for this combination.
 bool attn_supported(int kv_fmt, int q_fmt, int D, int G, bool paged);
 
+// Split-K partial pass + cross-split merge.
 hipError_t launch_attention(const AttnLaunch &a, hipStream_t stream);
+// The two halves on their own.  Partials: [rows][n_split][D + 4] fp32 holding
+// (unnormalised output u[D], max m of the base-2 logits, sum l of
+// 2^(logit - m), two pad words).
+// Merge: row r = b * heads_per_row + j goes to o + b * o_bstride + j * D.
+hipError_t launch_split(const AttnLaunch &a, hipStream_t stream);
+hipError_t launch_merge(int64_t rows, int32_t heads_per_row, int32_t n_split, int32_t D, const float *ws, float *o,
+                        int64_t o_bstride, hipStream_t stream);
 
 // Page metadata: kmin/kmax [B*H][P][D] from k [B*H][N][D].
 hipError_t launch_page_meta(int kv_fmt, int64_t BH, int64_t N, int D,

@@ -33,8 +33,6 @@ namespace {
 using namespace dev;
 
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kSub = 16;               // tokens per MFMA (its N dimension)
 constexpr int kTS = 2;                 // MFMA sub-tiles per wave iteration
 constexpr int kTile = kSub * kTS;      // tokens per wave iteration
@@ -63,6 +61,17 @@ struct Cfg {
     static constexpr bool ok = RPH0 <= 4 && G * RPH <= 16 && R >= 64 && R <= 1024;
 };
 
+// K/V rows are read once per call: load them non-temporally (streaming).
+__device__ __forceinline__ u32x4 ld_stream(const char *p) {
+    return __builtin_nontemporal_load((const u32x4 *)p);
+}
+__device__ __forceinline__ uint32_t ld_stream32(const void *p) {
+    return __builtin_nontemporal_load((const uint32_t *)p);
+}
+__device__ __forceinline__ uint16_t ld_stream16(const uint16_t *p) {
+    return __builtin_nontemporal_load(p);
+}
+
 // One dword of 8 codes -> 8 fp16 values 0..15 in the order of qk_dim().
 __device__ __forceinline__ u32x4 u4_to_f16x8(uint32_t x) {
     u32x4 r;
@@ -75,24 +84,34 @@ __device__ __forceinline__ u32x4 u4_to_f16x8(uint32_t x) {
     return r;
 }
 
+// Registers of one pipeline stage: the K and V of kTS sub-tiles of 16 tokens.
+template <int KF, int QF, int D, int G>
+struct Stage {
+    using C = Cfg<KF, QF, D, G>;
+    u32x4 K[kTS][C::NCH];
+    u32x4 V[kTS][C::VP];
+    bool kok[kTS];
+    uint32_t kmn[kTS], ksc[kTS];       // uint4: fp16 min/scale pairs of the K row (both groups)
+    float vmn[kTS], vsc[kTS];          // uint4: min/scale of the V row's group
+};
+
+// One wave per workgroup; the wave reduces one split of one (batch row, KV
+// head) to a partial per query head.  Loads of the next 32-token tile are
+// issued before the current tile is computed (two register stages).
 template <int KF, int QF, int D, int G, bool PAGED>
-__global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnLaunch a) {
+__global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a) {
     using C = Cfg<KF, QF, D, G>;
     static_assert(C::ok, "unsupported layout");
+    using St = Stage<KF, QF, D, G>;
     constexpr int R = C::R, RPH = C::RPH, HPL = C::HPL, SPL = C::SPL, NGRP = C::NGRP;
     constexpr int NCH = C::NCH, NMF = C::NMF, VP = C::VP, TPP = C::TPP, CPL = C::CPL;
     constexpr int MT = C::U4 ? FMT_F16 : KF;
+    constexpr int PSTR = D + 4;        // floats per partial row: u[D], m, l, pad, pad
 
-    __shared__ float p_lds[kWaves][kTile][G];
-    __shared__ float mrg_o[kWaves][G][D];
-    __shared__ float mrg_m[kWaves][G];
-    __shared__ float mrg_l[kWaves][G];
+    __shared__ float p_lds[kTile][G];
     __shared__ int32_t pg_lds[PAGED ? kMaxPagesPerSplit : 1];
-    __shared__ float qsum_lds[G][NGRP];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int lane = threadIdx.x;
     const int g4 = lane >> 4;          // lane group (MFMA k-chunk / C row block)
     const int n16 = lane & 15;         // token within sub-tile (K side)
     const int split = blockIdx.x;
@@ -109,9 +128,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnLaunch a) {
         const int p0 = split * pps;
         const int np = min(pps, a.top_k - p0);
         const int32_t *lst = a.page_idx + (int64_t)unit * a.top_k + p0;
-        for (int i = tid; i < np; i += kThreads) pg_lds[i] = lst[i];
+        for (int i = lane; i < np; i += 64) pg_lds[i] = lst[i];
         ntok = np << a.log2_page;
         pg_mask = (1 << a.log2_page) - 1;
+        wave_lds_sync();
     } else {
         s0 = (int64_t)split * a.split_tokens;
         ntok = (int)min((int64_t)a.split_tokens, a.N - s0);
@@ -129,14 +149,80 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnLaunch a) {
     }
     const int64_t qoff = (int64_t)b * a.q_bstride + (int64_t)hkv * G * D;
 
-    if constexpr (C::U4) {
-        if (tid < G * NGRP) {
-            const int h = tid / NGRP, gr = tid % NGRP;
-            float s = 0.f;
-            for (int d = 0; d < 64; ++d) s += load_scalar<QF>(a.q, qoff + h * D + gr * 64 + d);
-            qsum_lds[h][gr] = s;
+    const int vcol = (lane * 16) % R;            // V byte column of this lane
+    const int vtok = (lane * 16) / R;            // V token within a piece
+
+    auto row_of = [&](int pos, bool &ok) -> int64_t {
+        if constexpr (PAGED) {
+            ok = pos < ntok;
+            if (!ok) return 0;
+            const int32_t pg = pg_lds[pos >> a.log2_page];
+            const int64_t r = ((int64_t)pg << a.log2_page) + (pos & pg_mask);
+            ok = pg >= 0 && r < a.N;
+            return ok ? r : 0;
+        } else {
+            ok = pos < ntok;
+            return ok ? s0 + pos : 0;
         }
-    }
+    };
+
+    // ---- issue the loads of one tile ---------------------------------------
+    auto load_tile = [&](St &st, int t0) {
+        if (!PAGED && t0 + kTile <= ntok) {
+            // full dense tile: rows s0 + t0 .. s0 + t0 + 31, no masks
+            const char *kb = kbase + (s0 + t0) * R + 16 * g4;
+            const char *vb = vbase + (s0 + t0) * R + vcol;
+#pragma unroll
+            for (int ts = 0; ts < kTS; ++ts) {
+                st.kok[ts] = true;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c)
+                    st.K[ts][c] = ld_stream(kb + (ts * kSub + n16) * R + 64 * c);
+#pragma unroll
+                for (int p = 0; p < VP; ++p)
+                    st.V[ts][p] = ld_stream(vb + (ts * kSub + p * TPP + vtok) * R);
+                if constexpr (C::U4) {
+                    const int64_t rk = s0 + t0 + ts * kSub + n16;
+                    st.kmn[ts] = ld_stream32(kmn + rk * NGRP);
+                    st.ksc[ts] = ld_stream32(ksc + rk * NGRP);
+                    const int64_t rv = s0 + t0 + ts * kSub + vtok;     // VP == 1 for uint4
+                    const int gr = vcol / 32;
+                    st.vmn[ts] = f16_to_f32(ld_stream16(vmn + rv * NGRP + gr));
+                    st.vsc[ts] = f16_to_f32(ld_stream16(vsc + rv * NGRP + gr));
+                }
+            }
+            return;
+        }
+#pragma unroll
+        for (int ts = 0; ts < kTS; ++ts) {
+            bool ok;
+            const int64_t r = row_of(t0 + ts * kSub + n16, ok);
+            st.kok[ts] = ok;
+            const char *p = kbase + r * R + 16 * g4;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+                st.K[ts][c] = ok ? ld_stream(p + 64 * c) : (u32x4){0u, 0u, 0u, 0u};
+            if constexpr (C::U4) {
+                st.kmn[ts] = ok ? ld_stream32(kmn + r * NGRP) : 0u;
+                st.ksc[ts] = ok ? ld_stream32(ksc + r * NGRP) : 0u;
+            }
+#pragma unroll
+            for (int p2 = 0; p2 < VP; ++p2) {
+                bool okv;
+                const int64_t rv = row_of(t0 + ts * kSub + p2 * TPP + vtok, okv);
+                st.V[ts][p2] = okv ? ld_stream(vbase + rv * R + vcol) : (u32x4){0u, 0u, 0u, 0u};
+                if constexpr (C::U4) {
+                    const int gr = vcol / 32;
+                    st.vmn[ts] = okv ? f16_to_f32(ld_stream16(vmn + rv * NGRP + gr)) : 0.f;
+                    st.vsc[ts] = okv ? f16_to_f32(ld_stream16(vsc + rv * NGRP + gr)) : 0.f;
+                }
+            }
+        }
+    };
+
+    // issue the first tile before the q set-up below, so its latency overlaps
+    St sa, sb;
+    if (ntok > 0) load_tile(sa, 0);
 
     // ---- A operand: query rows, split into MFMA-type terms -------------------
     u32x4 Aq[KF == FMT_F32 ? 1 : NMF];
@@ -165,17 +251,22 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnLaunch a) {
             }
         }
     }
-    if constexpr (C::U4) __syncthreads();   // qsum_lds
-    if constexpr (PAGED) { if constexpr (!C::U4) __syncthreads(); }   // pg_lds
 
+    // uint4: per (head, group) sum of q, for the min term of the folded dequantization
     float qs[HPL][NGRP];
+#pragma unroll
+    for (int hh = 0; hh < HPL; ++hh)
+#pragma unroll
+        for (int gr = 0; gr < NGRP; ++gr) qs[hh][gr] = 0.f;
     if constexpr (C::U4) {
 #pragma unroll
-        for (int hh = 0; hh < HPL; ++hh)
+        for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int gr = 0; gr < NGRP; ++gr) {
-                const int h = g4 * HPL + hh;
-                qs[hh][gr] = h < G ? qsum_lds[h][gr] : 0.f;
+                float x = load_scalar<QF>(a.q, qoff + h * D + gr * 64 + lane);
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) x += shfl_xor(x, o);
+                if (h / HPL == g4) qs[h % HPL][gr] = x;
             }
     }
 
@@ -195,61 +286,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnLaunch a) {
         for (int c = 0; c < CPL; ++c) acc[h][c] = 0.f;
     }
 
-    const int vcol = (lane * 16) % R;            // V byte column of this lane
-    const int vtok = (lane * 16) / R;            // V token within a piece
     const float sl2 = a.scale_log2;
 
-    auto row_of = [&](int pos, bool &ok) -> int64_t {
-        if constexpr (PAGED) {
-            ok = pos < ntok;
-            if (!ok) return 0;
-            const int32_t pg = pg_lds[pos >> a.log2_page];
-            const int64_t r = ((int64_t)pg << a.log2_page) + (pos & pg_mask);
-            ok = pg >= 0 && r < a.N;
-            return ok ? r : 0;
-        } else {
-            ok = pos < ntok;
-            return ok ? s0 + pos : 0;
-        }
-    };
-
-    for (int t0 = w * kTile; t0 < ntok; t0 += kWaves * kTile) {
-        // ---- issue loads: K (B operand), then V ---------------------------
-        u32x4 Kr[kTS][NCH];
-        u32x4 Vr[kTS][VP];
-        bool kok[kTS];
-        uint32_t kmn_r[kTS], ksc_r[kTS];
-        float vmn_r[kTS], vsc_r[kTS];
-#pragma unroll
-        for (int ts = 0; ts < kTS; ++ts) {
-            bool ok;
-            const int64_t r = row_of(t0 + ts * kSub + n16, ok);
-            kok[ts] = ok;
-            const char *p = kbase + r * R + 16 * g4;
-#pragma unroll
-            for (int c = 0; c < NCH; ++c)
-                Kr[ts][c] = ok ? *(const u32x4 *)(p + 64 * c) : (u32x4){0u, 0u, 0u, 0u};
-            if constexpr (C::U4) {
-                kmn_r[ts] = ok ? *(const uint32_t *)(kmn + r * NGRP) : 0u;
-                ksc_r[ts] = ok ? *(const uint32_t *)(ksc + r * NGRP) : 0u;
-            }
-        }
-#pragma unroll
-        for (int ts = 0; ts < kTS; ++ts) {
-#pragma unroll
-            for (int p = 0; p < VP; ++p) {
-                bool ok;
-                const int64_t r = row_of(t0 + ts * kSub + p * TPP + vtok, ok);
-                Vr[ts][p] = ok ? *(const u32x4 *)(vbase + r * R + vcol) : (u32x4){0u, 0u, 0u, 0u};
-                if constexpr (C::U4) {
-                    const int gr = vcol / 32;
-                    vmn_r[ts] = ok ? f16_to_f32(vmn[r * NGRP + gr]) : 0.f;
-                    vsc_r[ts] = ok ? f16_to_f32(vsc[r * NGRP + gr]) : 0.f;
-                }
-            }
-        }
-
-        // ---- scores on the matrix cores -------------------------------------
+    // ---- scores, online softmax and P.V of one loaded tile ---------------------
+    auto compute_tile = [&](St &st) {
         float sc[kTS][HPL];
 #pragma unroll
         for (int ts = 0; ts < kTS; ++ts) {
@@ -259,18 +299,18 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnLaunch a) {
                 if constexpr (KF == FMT_F32) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        cc = __builtin_amdgcn_mfma_f32_16x16x4f32(Af[4 * c + e], __uint_as_float(Kr[ts][c][e]), cc, 0, 0, 0);
+                        cc = __builtin_amdgcn_mfma_f32_16x16x4f32(Af[4 * c + e], __uint_as_float(st.K[ts][c][e]), cc, 0, 0, 0);
                 } else if constexpr (KF == FMT_BF16) {
                     cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Aq[c]),
-                                                                 __builtin_bit_cast(bf16x8, Kr[ts][c]), cc, 0, 0, 0);
+                                                                 __builtin_bit_cast(bf16x8, st.K[ts][c]), cc, 0, 0, 0);
                 } else if constexpr (KF == FMT_F16) {
                     cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, Aq[c]),
-                                                                __builtin_bit_cast(f16x8, Kr[ts][c]), cc, 0, 0, 0);
+                                                                __builtin_bit_cast(f16x8, st.K[ts][c]), cc, 0, 0, 0);
                 } else {
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
                         cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, Aq[4 * c + u]),
-                                                                    __builtin_bit_cast(f16x8, u4_to_f16x8(Kr[ts][c][u])), cc, 0, 0, 0);
+                                                                    __builtin_bit_cast(f16x8, u4_to_f16x8(st.K[ts][c][u])), cc, 0, 0, 0);
                 }
             }
 #pragma unroll
@@ -283,19 +323,19 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnLaunch a) {
                         float dot = 0.f;
 #pragma unroll
                         for (int s = 0; s < SPL; ++s) dot += cc[hh * RPH + gr * SPL + s];
-                        const float mn = f16_to_f32((kmn_r[ts] >> (16 * gr)) & 0xFFFFu);
-                        const float sg = f16_to_f32((ksc_r[ts] >> (16 * gr)) & 0xFFFFu);
+                        const float mn = f16_to_f32((st.kmn[ts] >> (16 * gr)) & 0xFFFFu);
+                        const float sg = f16_to_f32((st.ksc[ts] >> (16 * gr)) & 0xFFFFu);
                         raw += mn * qs[hh][gr] + sg * dot;
                     }
                 } else {
 #pragma unroll
                     for (int s = 0; s < SPL; ++s) raw += cc[hh * RPH + s];
                 }
-                sc[ts][hh] = (h < G && kok[ts]) ? raw * sl2 : neg_inf();
+                sc[ts][hh] = (h < G && st.kok[ts]) ? raw * sl2 : neg_inf();
             }
         }
 
-        // ---- online softmax (base 2) ------------------------------------
+        // online softmax (base 2): per-head tile max over the 16 lanes of a group
         float mt[HPL];
 #pragma unroll
         for (int hh = 0; hh < HPL; ++hh) {
@@ -344,12 +384,12 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnLaunch a) {
             for (int ts = 0; ts < kTS; ++ts) {
                 const float p = (sc[ts][hh] == neg_inf()) ? 0.f : fast_exp2(sc[ts][hh] - mh);
                 l_part[hh] += p;
-                if (h < G) p_lds[w][ts * kSub + n16][h] = p;
+                if (h < G) p_lds[ts * kSub + n16][h] = p;
             }
         }
         wave_lds_sync();
 
-        // ---- P.V on the VALU ------------------------------------------------
+        // P.V on the VALU
 #pragma unroll
         for (int ts = 0; ts < kTS; ++ts) {
 #pragma unroll
@@ -357,8 +397,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnLaunch a) {
                 const int t = ts * kSub + p * TPP + vtok;
                 float pv[G];
 #pragma unroll
-                for (int h = 0; h < G; ++h) pv[h] = p_lds[w][t][h];
-                const u32x4 x = Vr[ts][p];
+                for (int h = 0; h < G; ++h) pv[h] = p_lds[t][h];
+                const u32x4 x = st.V[ts][p];
                 if constexpr (KF == FMT_F32) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -370,8 +410,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnLaunch a) {
                     float wv[G];
 #pragma unroll
                     for (int h = 0; h < G; ++h) {
-                        wv[h] = pv[h] * vsc_r[ts];
-                        amin[h] = fmaf(pv[h], vmn_r[ts], amin[h]);
+                        wv[h] = pv[h] * st.vsc[ts];
+                        amin[h] = fmaf(pv[h], st.vmn[ts], amin[h]);
                     }
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
@@ -409,9 +449,19 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnLaunch a) {
             }
         }
         wave_lds_sync();
+    };
+
+    // ---- main loop: two register stages -------------------------------------
+    for (int t0 = 0; t0 < ntok; t0 += 2 * kTile) {
+        const bool more = t0 + kTile < ntok;
+        if (more) load_tile(sb, t0 + kTile);
+        compute_tile(sa);
+        if (!more) break;
+        if (t0 + 2 * kTile < ntok) load_tile(sa, t0 + 2 * kTile);
+        compute_tile(sb);
     }
 
-    // ---- merge lanes, then waves ----------------------------------------
+    // ---- partial of this split ------------------------------------------------
 #pragma unroll
     for (int hh = 0; hh < HPL; ++hh) {
         float x = l_part[hh];
@@ -425,67 +475,106 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnLaunch a) {
     for (int mask = C::CH_LANES; mask < 64; mask <<= 1) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            amin[h] += shfl_xor(amin[h], mask);
+            if constexpr (C::U4) amin[h] += shfl_xor(amin[h], mask);
 #pragma unroll
             for (int c = 0; c < CPL; ++c) acc[h][c] += shfl_xor(acc[h][c], mask);
         }
     }
+    float *dst0 = a.ws + ((int64_t)unit * G * a.n_split + split) * PSTR;
+    const int64_t hstride = (int64_t)a.n_split * PSTR;
     if (lane == 0) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) mrg_m[w][h] = m_run[h];
+        for (int h = 0; h < G; ++h) dst0[h * hstride + D] = m_run[h];
     }
     if (n16 == 0) {
 #pragma unroll
         for (int hh = 0; hh < HPL; ++hh) {
             const int h = g4 * HPL + hh;
-            if (h < G) mrg_l[w][h] = l_part[hh];
+            if (h < G) dst0[h * hstride + D + 1] = l_part[hh];
         }
     }
     if (lane < C::CH_LANES) {
         const int c0 = KF == FMT_F32 ? vcol / 4 : (C::U4 ? vcol * 2 : vcol / 2);
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+        for (int h = 0; h < G; ++h) {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) mrg_o[w][h][c0 + c] = acc[h][c] + (C::U4 ? amin[h] : 0.f);
-    }
-    __syncthreads();
-
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-        const int h = idx / D, d = idx - h * D;
-        float M = mrg_m[0][h];
+            for (int c = 0; c < CPL; c += 4) {
+                f32x4 v4;
 #pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, mrg_m[ww][h]);
-        float L = 0.f, O = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-            const float mw = mrg_m[ww][h];
-            const float f = (mw == neg_inf()) ? 0.f : fast_exp2(mw - M);
-            L = fmaf(f, mrg_l[ww][h], L);
-            O = fmaf(f, mrg_o[ww][h][d], O);
+                for (int e = 0; e < 4; ++e) v4[e] = acc[h][c + e] + (C::U4 ? amin[h] : 0.f);
+                *(f32x4 *)(dst0 + h * hstride + c0 + c) = v4;
+            }
         }
-        float *dst = a.ws + ((int64_t)(unit * G + h) * a.n_split + split) * (D + 2);
-        dst[2 + d] = O;
-        if (d == 0) { dst[0] = M; dst[1] = L; }
     }
 }
 
-// Merge of the split partials of one query head (one block per head row).
+// Merge of the split partials of one query-head row (one block per row).
+// Partial row: [u(D), m, l, pad, pad].  Weights 2^(m_s - M) are computed once
+// per split into LDS, then every thread sums its channel over the splits.
+constexpr int kMergeMaxLds = 8192;
+
 __global__ __launch_bounds__(128) void attn_reduce_kernel(const float *__restrict__ ws, float *__restrict__ o,
                                                           int n_split, int D, int HG, int64_t o_bstride) {
-    const int row = blockIdx.x;                 // (b * Hkv + h) * G + g = b * HG + hq
+    __shared__ float w_lds[kMergeMaxLds];
+    __shared__ float red[4];
+    const int row = blockIdx.x;                 // b * HG + hq
     const int b = row / HG, hq = row - b * HG;
-    const float *p = ws + (int64_t)row * n_split * (D + 2);
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int PSTR = D + 4;
+    const float *p = ws + (int64_t)row * n_split * PSTR;
+
     float M = neg_inf();
-    for (int s = 0; s < n_split; ++s) M = fmaxf(M, p[(int64_t)s * (D + 2)]);
-    for (int d = threadIdx.x; d < D; d += blockDim.x) {
-        float L = 0.f, O = 0.f;
-        for (int s = 0; s < n_split; ++s) {
-            const float *q = p + (int64_t)s * (D + 2);
-            const float f = (q[0] == neg_inf()) ? 0.f : fast_exp2(q[0] - M);
-            L = fmaf(f, q[1], L);
-            O = fmaf(f, q[2 + d], O);
+    for (int s = tid; s < n_split; s += nt) M = fmaxf(M, p[(int64_t)s * PSTR + D]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, shfl_xor(M, off));
+    if ((tid & 63) == 0) red[tid >> 6] = M;
+    __syncthreads();
+    M = red[0];
+    for (int w = 1; w < (nt + 63) / 64; ++w) M = fmaxf(M, red[w]);
+    __syncthreads();
+
+    const bool use_lds = n_split <= kMergeMaxLds;
+    float L = 0.f;
+    for (int s = tid; s < n_split; s += nt) {
+        const float m = p[(int64_t)s * PSTR + D];
+        const float f = (m == neg_inf()) ? 0.f : fast_exp2(m - M);
+        if (use_lds) w_lds[s] = f;
+        L = fmaf(f, p[(int64_t)s * PSTR + D + 1], L);
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) L += shfl_xor(L, off);
+    if ((tid & 63) == 0) red[tid >> 6] = L;
+    __syncthreads();
+    L = red[0];
+    for (int w = 1; w < (nt + 63) / 64; ++w) L += red[w];
+
+    __syncthreads();   // w_lds complete
+    for (int d = tid; d < D; d += nt) {
+        float O0 = 0.f, O1 = 0.f, O2 = 0.f, O3 = 0.f;
+        int s = 0;
+        if (use_lds) {
+            // 16 independent loads in flight per batch
+            for (; s + 16 <= n_split; s += 16) {
+                float x[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) x[j] = p[(int64_t)(s + j) * PSTR + d];
+#pragma unroll
+                for (int j = 0; j < 16; j += 4) {
+                    O0 = fmaf(w_lds[s + j], x[j], O0);
+                    O1 = fmaf(w_lds[s + j + 1], x[j + 1], O1);
+                    O2 = fmaf(w_lds[s + j + 2], x[j + 2], O2);
+                    O3 = fmaf(w_lds[s + j + 3], x[j + 3], O3);
+                }
+            }
+            for (; s < n_split; ++s) O0 = fmaf(w_lds[s], p[(int64_t)s * PSTR + d], O0);
+        } else {
+            for (; s < n_split; ++s) {
+                const float m = p[(int64_t)s * PSTR + D];
+                const float f = (m == neg_inf()) ? 0.f : fast_exp2(m - M);
+                O0 = fmaf(f, p[(int64_t)s * PSTR + d], O0);
+            }
         }
-        o[(int64_t)b * o_bstride + (int64_t)hq * D + d] = O / L;
+        o[(int64_t)b * o_bstride + (int64_t)hq * D + d] = ((O0 + O1) + (O2 + O3)) / L;
     }
 }
 
@@ -556,8 +645,15 @@ SplitFn pick(int kv, int qf, int D, int G, bool paged) {
 
 }  // namespace
 
+int32_t default_split_dense(int64_t n_ctx) {
+    int64_t want = (n_ctx + 15) / 16;
+    int32_t s = kDefaultSplitDenseMin;
+    while (s < kDefaultSplitDense && s < want) s <<= 1;
+    return s;
+}
+
 int32_t attn_n_split(int64_t n_ctx, int32_t split_tokens, bool paged, int32_t top_k, int32_t log2_page) {
-    if (split_tokens <= 0) split_tokens = kDefaultSplitTokens;
+    if (split_tokens <= 0) split_tokens = paged ? kDefaultSplitPaged : default_split_dense(n_ctx);
     if (paged) {
         int pps = split_tokens >> log2_page;
         if (pps < 1) pps = 1;
@@ -568,24 +664,34 @@ int32_t attn_n_split(int64_t n_ctx, int32_t split_tokens, bool paged, int32_t to
 }
 
 size_t attn_ws_bytes(int64_t rows, int32_t n_split, int32_t D) {
-    return (size_t)rows * (size_t)n_split * (size_t)(D + 2) * sizeof(float);
+    return (size_t)rows * (size_t)n_split * (size_t)(D + 4) * sizeof(float);
 }
 
 bool attn_supported(int kv_fmt, int q_fmt, int D, int G, bool paged) {
     return pick(kv_fmt, q_fmt, D, G, paged) != nullptr;
 }
 
-hipError_t launch_attention(const AttnLaunch &a, hipStream_t stream) {
+hipError_t launch_split(const AttnLaunch &a, hipStream_t stream) {
     SplitFn fn = pick(a.kv_fmt, a.q_fmt, a.D, a.G, a.page_idx != nullptr);
     if (!fn) return hipErrorInvalidValue;
     dim3 grid(a.n_split, a.B * a.Hkv);
-    hipLaunchKernelGGL(fn, grid, dim3(kThreads), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int rows = a.B * a.Hkv * a.G;
-    hipLaunchKernelGGL(attn_reduce_kernel, dim3(rows), dim3(a.D), 0, stream,
-                       (const float *)a.ws, a.o, a.n_split, a.D, a.Hkv * a.G, a.o_bstride);
+    hipLaunchKernelGGL(fn, grid, dim3(64), 0, stream, a);
     return hipGetLastError();
+}
+
+hipError_t launch_merge(int64_t rows, int32_t heads_per_row, int32_t n_split, int32_t D, const float *ws, float *o,
+                        int64_t o_bstride, hipStream_t stream) {
+    if (rows <= 0) return hipSuccess;
+    if (rows > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_reduce_kernel, dim3((unsigned)rows), dim3(D), 0, stream, ws, o, n_split, D,
+                       heads_per_row, o_bstride);
+    return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnLaunch &a, hipStream_t stream) {
+    hipError_t e = launch_split(a, stream);
+    if (e != hipSuccess) return e;
+    return launch_merge((int64_t)a.B * a.Hkv * a.G, a.Hkv * a.G, a.n_split, a.D, a.ws, a.o, a.o_bstride, stream);
 }
 
 }  // namespace da

@@ -99,7 +99,7 @@ size_t da_stream_workspace(const da_stream_ctx *c) {
     if (!c) return 0;
     const da_attn_shape *s = &c->shape;
     const int G = s->n_q_heads / s->n_kv_heads;
-    return attn_ws_bytes((int64_t)s->batch * c->hpc * G, attn_n_split(s->n_ctx, split_tokens_of(s), false, 0, 0),
+    return attn_ws_bytes((int64_t)s->batch * c->hpc * G, attn_n_split(s->n_ctx, split_tokens_of(s, SPLIT_DENSE), false, 0, 0),
                          s->head_dim);
 }
 
@@ -128,7 +128,7 @@ da_status da_stream_headwise(da_stream_ctx *c, int32_t n_layers, const void *con
     const size_t hb = head_bytes(s);
     const int n_chunks = s->n_kv_heads / c->hpc;
     const int qes = esize(s->q_dtype);
-    AttnLaunch a = dense_launch(s, s->kv_dtype);
+    AttnLaunch a = dense_launch(s, s->kv_dtype, SPLIT_DENSE);
     a.Hkv = c->hpc;
     a.kv_bstride = s->n_ctx;                      // buffer layout [hpc][B][N][D]
     a.kv_hstride = (int64_t)s->batch * s->n_ctx;

@@ -97,7 +97,7 @@ def test_dense_pointer_and_workspace_checks(lib):
     assert dense(lib, s, o=NULL) == L.DA_E_INVALID
     assert dense(lib, s, ws=NULL) == L.DA_E_INVALID
     need = lib.da_decode_attention_workspace(ctypes.byref(s))
-    assert need == 8 * 32 * 64 * 130 * 4          # B*Hq rows x 64 splits x (D+2) fp32
+    assert need == 8 * 32 * 16 * 132 * 4          # B*Hq rows x 16 splits of 2048 x (D+4) fp32
     assert dense(lib, s, ws_bytes=need - 1) == L.DA_E_WORKSPACE
 
 
@@ -110,8 +110,8 @@ def test_empty_batch_is_a_no_op(lib):
 def test_workspace_depends_on_split_size(lib):
     s1 = shape(split_tokens=1024)
     s2 = shape(split_tokens=256)
-    assert lib.da_decode_attention_workspace(ctypes.byref(s1)) == 8 * 32 * 32 * 130 * 4
-    assert lib.da_decode_attention_workspace(ctypes.byref(s2)) == 8 * 32 * 128 * 130 * 4
+    assert lib.da_decode_attention_workspace(ctypes.byref(s1)) == 8 * 32 * 32 * 132 * 4
+    assert lib.da_decode_attention_workspace(ctypes.byref(s2)) == 8 * 32 * 128 * 132 * 4
     assert lib.da_decode_attention_workspace(ctypes.byref(shape(head_dim=96))) == 0
 
 
@@ -141,7 +141,7 @@ def test_page_checks(lib):
     assert paged(s, 0) == L.DA_E_INVALID
     assert paged(mha(n_q_heads=32), 128) == L.DA_E_UNSUPPORTED
     need = lib.da_decode_attention_paged_workspace(ctypes.byref(s), 16, 128)
-    assert need == 32 * 16 * 4 * 66 * 4           # 128 pages of 16 = 2048 positions / 512
+    assert need == 32 * 16 * 8 * 68 * 4           # 128 pages of 16 = 2048 positions / 256
     assert paged(s, 128, need - 4) == L.DA_E_WORKSPACE
 
 
@@ -160,7 +160,7 @@ def test_kv4_checks(lib):
     assert att(s64) == L.DA_E_UNSUPPORTED
     sbf = shape(batch=64, n_q_heads=56, n_kv_heads=56, head_dim=128, n_ctx=1024, q_dtype=L.DA_BF16)
     assert att(sbf) == L.DA_E_UNSUPPORTED
-    assert lib.da_decode_attention_kv4_workspace(ctypes.byref(s)) == 64 * 56 * 2 * 130 * 4
+    assert lib.da_decode_attention_kv4_workspace(ctypes.byref(s)) == 64 * 56 * 2 * 132 * 4
 
 
 def test_headwise_sizes_match_the_pages_and_checks(lib):

@@ -1,0 +1,155 @@
+"""uint4 group quantization and dequant-fused attention on the GPU against
+the oracle (FlexGen's 4-bit groups of 64).
+
+Codes and scales are bit-exact; group minima equal by value (a -0 / +0 minimum
+may carry either sign).  Dequantization is bit-exact.  Attention folds the
+dequantization into fp32 arithmetic (min * sum(q) + scale * sum(q * code)),
+which differs from the oracle's fp16-rounded values by at most half an fp16
+ulp (2^-11 relative) per element.  Against the oracle the bar is the
+spec 1e-3 absolute and max|err|/rms <= 3e-3 (random per-element
+differences of up to 2^-11 |x| give a typical output error near
+2^-11 / sqrt(3) of rms, about 3e-4, and a maximum over a head a few times
+that; measured maxima are near 1.3e-3).  A second, tight check compares the
+kernel with attention over the exact unrounded values min + code * scale,
+which is what the fold computes, at 1e-5 absolute and 1e-4 of rms."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import dequantize_kv4, kv4_attention, quantize_kv4, decode_attention
+from oracle.kv4 import unpack_codes
+from oracle.numerics import as_f64
+from gpu_util import assert_close, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def special_rows():
+    rng = np.random.default_rng(21)
+    rows = [rng.standard_normal(128) for _ in range(6)]
+    rows.append(np.full(128, -1.25))                          # constant groups
+    rows.append(rng.standard_normal(128) * 1e-6)              # fp16 subnormals
+    rows.append(rng.standard_normal(128) * 3000)              # large values
+    ramp = np.concatenate([np.arange(16), np.arange(16) + 0.5, np.arange(16) * 0.25,
+                           np.arange(16) * 0.75])
+    rows.append(np.concatenate([ramp, -ramp]))                # exact ties
+    rows.append(np.concatenate([np.zeros(64), np.full(64, 7.0)]))
+    return np.stack(rows).astype(np.float16)
+
+
+def quant_gpu(da, x):
+    import torch
+    codes, mn, sc = da.da_quantize_kv4(to_dev(x, "f16"))
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), mn.cpu().numpy(), sc.cpu().numpy()
+
+
+def assert_quant_equal(got, want):
+    gc, gm, gs = got
+    wc, wm, ws = want
+    assert np.array_equal(gc, wc), f"codes differ at {np.argwhere(gc != wc)[:5]}"
+    assert np.array_equal(gs.view(np.uint16), ws.view(np.uint16)), "scales differ"
+    assert np.array_equal(gm.astype(np.float64), wm.astype(np.float64)), "minima differ"
+
+
+@pytest.mark.parametrize("shape", [(11, 128), (3, 5, 7, 128), (2, 64), (1, 4096)])
+def test_quantize_bit_exact(da, shape):
+    rng = np.random.default_rng(sum(shape))
+    x = rng.standard_normal(shape).astype(np.float16)
+    assert_quant_equal(quant_gpu(da, x), quantize_kv4(x))
+
+
+def test_quantize_special_values_bit_exact(da):
+    x = special_rows()
+    assert_quant_equal(quant_gpu(da, x), quantize_kv4(x))
+
+
+def test_dequantize_bit_exact(da):
+    import torch
+    x = np.concatenate([special_rows(), np.random.default_rng(5).standard_normal((20, 128))
+                        .astype(np.float16)])
+    codes, mn, sc = quantize_kv4(x)
+    xh = da.da_dequantize_kv4(torch.from_numpy(codes).cuda(), torch.from_numpy(mn).cuda(),
+                              torch.from_numpy(sc).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(xh.cpu().numpy().view(np.uint16),
+                          dequantize_kv4(codes, mn, sc).view(np.uint16))
+
+
+def unrounded(codes, gmin, gscale):
+    """min + code * scale in float64, not rounded to fp16 (what the fold uses)."""
+    c = unpack_codes(codes).astype(np.float64)
+    lead, R = c.shape[:-1], c.shape[-1]
+    c = c.reshape(*lead, R // 64, 64)
+    x = gmin.astype(np.float64)[..., None] + c * gscale.astype(np.float64)[..., None]
+    return x.reshape(*lead, R)
+
+
+def run_kv4(da, c, split_tokens=0):
+    import torch
+    q = to_dev(c.q, c.q_dtype)
+    kq = da.da_quantize_kv4(to_dev(c.k, "f16"))
+    vq = da.da_quantize_kv4(to_dev(c.v, "f16"))
+    o = da.da_decode_attention_kv4(q, *kq, *vq, scale=c.scale, split_tokens=split_tokens)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), [t.cpu().numpy() for t in kq], [t.cpu().numpy() for t in vq]
+
+
+KV4_CASES = [
+    # B, Hq, Hkv, N, q dtype, split
+    (2, 4, 4, 300, "f16", 0),
+    (1, 8, 4, 1000, "f16", 128),      # G = 2
+    (2, 2, 2, 77, "f32", 16),         # fp32 q (two fp16 terms)
+    (1, 4, 1, 513, "f32", 0),         # G = 4
+    (1, 8, 1, 200, "f16", 64),        # G = 8
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,qd,st", KV4_CASES)
+def test_kv4_attention(da, B, Hq, Hkv, N, qd, st):
+    c = synth.dense_case([300, B, Hq, Hkv, N], B, Hq, Hkv, 128, N, qd, "f16")
+    o, kq, vq = run_kv4(da, c, st)
+    assert_quant_equal(kq, quantize_kv4(c.k))
+    ref = kv4_attention(as_f64(c.q, qd), *kq, *vq, c.scale)
+    assert_close(o, ref, atol=1e-3, rel_rms=3e-3, what=f"kv4 B{B} Hq{Hq} Hkv{Hkv} N{N} {qd}")
+    fold = decode_attention(as_f64(c.q, qd), unrounded(*kq), unrounded(*vq), c.scale)
+    assert_close(o, fold, atol=1e-5, rel_rms=1e-4, what="  vs unrounded dequant")
+
+
+def test_kv4_integer_data_equals_dense(da):
+    rng = np.random.default_rng(22)
+    B, H, N, D = 2, 2, 150, 128
+    k = rng.integers(0, 16, size=(B, H, N, D)).astype(np.float16)
+    v = rng.integers(-7, 9, size=(B, H, N, D)).astype(np.float16)
+    k[..., 0::64] = 0
+    k[..., 1::64] = 15
+    v[..., 0::64] = -7
+    v[..., 1::64] = 8
+    q = rng.standard_normal((B, H, D)).astype(np.float16)
+    c = synth.DenseCase(q=q, k=k, v=v, q_dtype="f16", kv_dtype="f16", scale=0.05)
+    o, _, _ = run_kv4(da, c)
+    ref = decode_attention(as_f64(q, "f16"), k.astype(np.float64), v.astype(np.float64), 0.05)
+    assert_close(o, ref, atol=1e-5, rel_rms=1e-5, what="kv4 integer data")
+
+
+def test_workload4_full_size_sampled(da):
+    """FlexGen shape (B64 H56 D128 N1024): codes of sampled rows bit-exact,
+    attention of sampled heads, in the benchmark's launch configuration."""
+    c = synth.workload4()
+    o, kq, vq = run_kv4(da, c)
+    rng = np.random.default_rng(4)
+    picks = [(0, 0), (63, 55)] + [(int(b), int(h)) for b, h in
+                                  zip(rng.integers(0, 64, 6), rng.integers(0, 56, 6))]
+    for b, h in picks:
+        want_k = quantize_kv4(c.k[b, h])
+        want_v = quantize_kv4(c.v[b, h])
+        assert_quant_equal([t[b, h] for t in kq], want_k)
+        assert_quant_equal([t[b, h] for t in vq], want_v)
+        ref = kv4_attention(as_f64(c.q[b:b + 1, h:h + 1], "f16"),
+                            *[t[None, None] for t in want_k], *[t[None, None] for t in want_v],
+                            c.scale)
+        assert_close(o[b, h], ref[0, 0], atol=1e-3, rel_rms=3e-3, what=f"w4 b{b} h{h}")
+        fold = decode_attention(as_f64(c.q[b:b + 1, h:h + 1], "f16"),
+                                unrounded(*want_k)[None, None], unrounded(*want_v)[None, None],
+                                c.scale)
+        assert_close(o[b, h], fold[0, 0], atol=1e-5, rel_rms=1e-4, what="  vs unrounded dequant")

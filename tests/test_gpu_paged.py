@@ -1,0 +1,140 @@
+"""Page metadata, bound-score top-K selection and sparse attention on the GPU
+against the fp64 oracle (TinyServe's query-aware page selection).
+
+Metadata must equal the oracle's by value (min/max are exact).  Selected sets
+must equal the oracle's except pages within 1e-5 relative of the oracle's
+k-th score.  Sparse attention is checked against the oracle evaluated on the
+GPU's own selected set (so a tie decision cannot fail a correct kernel), at
+|err| <= 1e-5 on small shapes and 1e-3 at full size, and max|err|/rms <= 1e-4.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import bound_scores, decode_attention, page_meta, sparse_attention
+from oracle.numerics import as_f64
+from gpu_util import assert_close, check_selection, from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dt,S,N,D", [("f16", 16, 1000, 64), ("bf16", 4, 333, 128),
+                                      ("f32", 64, 130, 64), ("f16", 1, 50, 128),
+                                      ("f16", 1024, 3000, 64)])
+def test_page_meta_exact(da, dt, S, N, D):
+    c = synth.paged_case([200, S, N, D], 2, 3, D, N, S, 1, dtype=dt)
+    kmin, kmax = da.da_build_page_meta(to_dev(c.k, dt), S)
+    rmin, rmax = page_meta(as_f64(c.k, dt), S)
+    assert np.array_equal(as_f64(from_dev(kmin, dt), dt), rmin)
+    assert np.array_equal(as_f64(from_dev(kmax, dt), dt), rmax)
+
+
+def run_select(da, c, qdt, kdt, want_scores=True):
+    import torch
+    q = to_dev(c.q, qdt)
+    k = to_dev(c.k, kdt)
+    N = c.k.shape[2]
+    kmin, kmax = da.da_build_page_meta(k, c.page_size)
+    idx, score = da.da_select_pages(q, kmin, kmax, c.page_size, c.top_k, N, want_scores=True)
+    torch.cuda.synchronize()
+    return q, k, idx.cpu().numpy(), score.cpu().numpy()
+
+
+SEL_CASES = [
+    # B, H, D, N, S, top_k, dtype(q/kv)
+    (2, 3, 64, 1000, 16, 5, "f16"),       # partial last page
+    (1, 4, 128, 4096, 16, 128, "f16"),
+    (2, 2, 64, 777, 4, 37, "f16"),
+    (1, 2, 64, 333, 1, 40, "f16"),         # one-token pages: bound = q.k
+    (2, 2, 128, 2048, 64, 3, "bf16"),
+    (1, 2, 64, 640, 16, 40, "f32"),        # top_k = P: every page
+]
+
+
+@pytest.mark.parametrize("B,H,D,N,S,K,dt", SEL_CASES)
+def test_select_and_sparse_attention(da, B, H, D, N, S, K, dt):
+    c = synth.paged_case([201, B, H, D, N, S, K], B, H, D, N, S, K, dtype=dt)
+    q, k, idx, score = run_select(da, c, dt, dt)
+    q64, k64, v64 = as_f64(c.q, dt), as_f64(c.k, dt), as_f64(c.v, dt)
+    rmin, rmax = page_meta(k64, S)
+    r = bound_scores(q64, rmin, rmax)
+    mag = np.einsum("bhd,bhpd->bhp", np.abs(q64), np.maximum(np.abs(rmin), np.abs(rmax)))
+    assert np.all(np.abs(score - r) <= 1e-6 * mag + 1e-30), "bound scores"
+    check_selection(idx, r, K)
+    if S == 1:
+        np.testing.assert_allclose(r, np.einsum("bhd,bhnd->bhn", q64, k64), atol=1e-9)
+    o = da.da_decode_attention_paged(q, k, to_dev(c.v, dt), torch_idx(idx), S, scale=c.scale)
+    ref = sparse_attention(q64, k64, v64, idx, S, c.scale)
+    assert_close(o.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what=f"sparse {dt} S{S} K{K}")
+
+
+def torch_idx(idx):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).cuda()
+
+
+def test_all_pages_equals_dense(da):
+    c = synth.paged_case([202], 2, 4, 128, 1500, 16, 94, dtype="f16")
+    P = 94
+    idx = np.broadcast_to(np.arange(P, dtype=np.int32), (2, 4, P)).copy()
+    q, k, v = to_dev(c.q, "f16"), to_dev(c.k, "f16"), to_dev(c.v, "f16")
+    o = da.da_decode_attention_paged(q, k, v, torch_idx(idx), 16).cpu().numpy()
+    ref = decode_attention(as_f64(c.q, "f16"), as_f64(c.k, "f16"), as_f64(c.v, "f16"), c.scale)
+    assert_close(o, ref, atol=1e-5, rel_rms=1e-4, what="all pages = dense")
+
+
+def test_out_of_range_pages_are_skipped(da):
+    c = synth.paged_case([203], 1, 2, 64, 100, 16, 4, dtype="f16")   # P = 7, last page 4 tokens
+    idx = np.array([[[0, 3, 6, 99]], [[-1, 2, 5, 1000]]], dtype=np.int32).reshape(1, 2, 4)
+    q, k, v = to_dev(c.q, "f16"), to_dev(c.k, "f16"), to_dev(c.v, "f16")
+    o = da.da_decode_attention_paged(q, k, v, torch_idx(idx), 16).cpu().numpy()
+    ref0 = sparse_attention(as_f64(c.q, "f16")[:, :1], as_f64(c.k, "f16")[:, :1],
+                            as_f64(c.v, "f16")[:, :1], np.array([[[0, 3, 6]]], dtype=np.int32),
+                            16, c.scale)
+    ref1 = sparse_attention(as_f64(c.q, "f16")[:, 1:], as_f64(c.k, "f16")[:, 1:],
+                            as_f64(c.v, "f16")[:, 1:], np.array([[[2, 5]]], dtype=np.int32),
+                            16, c.scale)
+    assert_close(o[:, :1], ref0, atol=1e-5, what="skip >= P")
+    assert_close(o[:, 1:], ref1, atol=1e-5, what="skip < 0")
+
+
+def test_split_sizes_agree_paged(da):
+    c = synth.paged_case([204], 1, 2, 64, 4000, 16, 60, dtype="f16")
+    q, k, v = to_dev(c.q, "f16"), to_dev(c.k, "f16"), to_dev(c.v, "f16")
+    kmin, kmax = da.da_build_page_meta(k, 16)
+    idx = da.da_select_pages(q, kmin, kmax, 16, 60, 4000)
+    ref = sparse_attention(as_f64(c.q, "f16"), as_f64(c.k, "f16"), as_f64(c.v, "f16"),
+                           idx.cpu().numpy(), 16, c.scale)
+    for st in (16, 64, 256, 1024):
+        o = da.da_decode_attention_paged(q, k, v, idx, 16, split_tokens=st).cpu().numpy()
+        assert_close(o, ref, atol=1e-5, rel_rms=1e-4, what=f"paged split {st}")
+
+
+def test_workload3_full_size_sampled(da):
+    """TinyServe shape (B32 H16 D64 N32768 fp16, page 16, top-128), in the
+    benchmark's launch configuration; selection and attention checked on
+    sampled (row, head) pairs, metadata on sampled pages."""
+    import torch
+    c = synth.workload3()
+    S, K = c.page_size, c.top_k
+    q, k, v = to_dev(c.q, "f16"), to_dev(c.k, "f16"), to_dev(c.v, "f16")
+    kmin, kmax = da.da_build_page_meta(k, S)
+    idx = da.da_select_pages(q, kmin, kmax, S, K, 32768)
+    o = da.da_decode_attention_paged(q, k, v, idx, S)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    o = o.cpu().numpy()
+    kmin = kmin.cpu().numpy()
+    rng = np.random.default_rng(3)
+    picks = [(0, 0), (31, 15)] + [(int(b), int(h)) for b, h in
+                                  zip(rng.integers(0, 32, 6), rng.integers(0, 16, 6))]
+    for b, h in picks:
+        q64 = as_f64(c.q[b:b + 1, h:h + 1], "f16")
+        k64 = as_f64(c.k[b:b + 1, h:h + 1], "f16")
+        v64 = as_f64(c.v[b:b + 1, h:h + 1], "f16")
+        rmin, rmax = page_meta(k64, S)
+        assert np.array_equal(kmin[b:b + 1, h:h + 1].astype(np.float64), rmin)
+        r = bound_scores(q64, rmin, rmax)
+        check_selection(idx[b:b + 1, h:h + 1], r, K)
+        ref = sparse_attention(q64, k64, v64, idx[b:b + 1, h:h + 1], S, c.scale)
+        assert_close(o[b, h], ref[0, 0], atol=1e-3, rel_rms=1e-4, what=f"w3 b{b} h{h}")

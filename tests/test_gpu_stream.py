@@ -1,0 +1,108 @@
+"""Head-wise streamed decode on the GPU (HeadInfer): K/V of each (layer, KV
+head) in pinned host memory, copied into two ping-pong device buffers on a copy
+stream while attention runs on the compute stream.  Checked against the
+oracle's head-by-head driver, and bitwise against da_decode_attention on the
+same data resident in device memory."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import headwise_attention
+from oracle.numerics import as_f64
+from gpu_util import assert_close, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def host_heads(spec):
+    import torch
+    ks, vs, k64, v64 = [], [], [], []
+    for l in range(spec.n_layers):
+        k64.append([])
+        v64.append([])
+        for h in range(spec.n_kv_heads):
+            k, v = spec.head(l, h)
+            tk = torch.empty(k.shape, dtype=torch.bfloat16, pin_memory=True)
+            tv = torch.empty(v.shape, dtype=torch.bfloat16, pin_memory=True)
+            tk.view(torch.int16).numpy()[...] = k.view(np.int16)
+            tv.view(torch.int16).numpy()[...] = v.view(np.int16)
+            ks.append(tk)
+            vs.append(tv)
+            k64[-1].append(as_f64(k, "bf16"))
+            v64[-1].append(as_f64(v, "bf16"))
+    return ks, vs, k64, v64
+
+
+def run_stream(da, spec, hpc, ks, vs):
+    import torch
+    hs = da.HeadwiseStream(spec.batch, spec.n_q_heads, spec.n_kv_heads, spec.head_dim,
+                           spec.n_ctx, da.DA_F32, da.DA_BF16, heads_per_chunk=hpc)
+    buf0 = torch.empty(hs.buffer_bytes, dtype=torch.uint8, device="cuda")
+    buf1 = torch.empty(hs.buffer_bytes, dtype=torch.uint8, device="cuda")
+    q = to_dev(spec.q(), "f32")
+    out = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(16, hs.workspace_bytes), dtype=torch.uint8, device="cuda")
+    comp = torch.cuda.current_stream()
+    cpy = torch.cuda.Stream()
+    cpy.wait_stream(comp)
+    hs.da_stream_headwise(ks, vs, buf0, buf1, q, out, ws, comp, cpy)
+    torch.cuda.synchronize()
+    hs.close()
+    return q, out.cpu().numpy()
+
+
+@pytest.mark.parametrize("hpc", [1, 2])
+def test_stream_matches_oracle_and_resident_path(da, hpc):
+    import torch
+    spec = synth.small_headwise(n_layers=3, n_kv_heads=2, n_q_heads=8, batch=2, head_dim=64,
+                                n_ctx=1000)
+    ks, vs, k64, v64 = host_heads(spec)
+    q, got = run_stream(da, spec, hpc, ks, vs)
+    ref = headwise_attention(as_f64(spec.q(), "f32"), k64, v64, 1.0 / np.sqrt(64))
+    assert_close(got, ref, atol=1e-5, rel_rms=1e-4, what=f"stream hpc{hpc}")
+    H = spec.n_kv_heads
+    for l in range(spec.n_layers):
+        kl = torch.stack([ks[l * H + h] for h in range(H)], dim=1).cuda()   # [B][Hkv][N][D]
+        vl = torch.stack([vs[l * H + h] for h in range(H)], dim=1).cuda()
+        o = da.da_decode_attention(q[l].contiguous(), kl.contiguous(), vl.contiguous())
+        torch.cuda.synchronize()
+        assert np.array_equal(o.cpu().numpy(), got[l]), f"layer {l}: not bitwise equal"
+
+
+def test_not_pinned_is_rejected(da):
+    import torch
+    spec = synth.small_headwise(n_layers=1, n_kv_heads=2, n_q_heads=4, batch=1, head_dim=64,
+                                n_ctx=100)
+    ks = [torch.zeros((1, 100, 64), dtype=torch.bfloat16) for _ in range(2)]   # pageable
+    vs = [torch.zeros((1, 100, 64), dtype=torch.bfloat16) for _ in range(2)]
+    with pytest.raises(da.DaError) as e:
+        run_stream(da, spec, 1, ks, vs)
+    assert e.value.status == da.DA_E_NOT_PINNED
+
+
+def test_workload5_shape_one_layer(da):
+    """HeadInfer shape at full context (N = 2^20, 8 KV heads, 32 query heads,
+    bf16) for one layer: two layer-heads carry the seeded data and are checked
+    against the oracle; the other six hold zeros, whose output must be 0."""
+    import torch
+    spec = synth.HeadwiseSpec(n_layers=1)
+    ks, vs = [], []
+    real = {0: None, 7: None}
+    for h in range(spec.n_kv_heads):
+        tk = torch.zeros((1, spec.n_ctx, 128), dtype=torch.bfloat16, pin_memory=True)
+        tv = torch.zeros((1, spec.n_ctx, 128), dtype=torch.bfloat16, pin_memory=True)
+        if h in real:
+            spec.head(0, h, tk.view(torch.int16).numpy().view(np.uint16),
+                      tv.view(torch.int16).numpy().view(np.uint16))
+        ks.append(tk)
+        vs.append(tv)
+    q, got = run_stream(da, spec, 1, ks, vs)
+    q64 = as_f64(spec.q(), "f32")
+    for h in real:
+        k64 = as_f64(ks[h].view(torch.int16).numpy().view(np.uint16), "bf16")
+        v64 = as_f64(vs[h].view(torch.int16).numpy().view(np.uint16), "bf16")
+        ref = headwise_attention(q64[:, :, 4 * h:4 * h + 4], [[k64]], [[v64]], 1.0 / np.sqrt(128))
+        assert_close(got[:, :, 4 * h:4 * h + 4], ref, atol=1e-3, rel_rms=1e-4, what=f"w5 head {h}")
+    for h in range(spec.n_kv_heads):
+        if h not in real:
+            assert not np.any(got[:, :, 4 * h:4 * h + 4]), f"zero head {h}"
