@@ -353,6 +353,12 @@ def main(argv=None) -> int:
     ap.add_argument("--no-stream", action="store_true", help="skip the head-wise streamed workload")
     ap.add_argument("--stream-pool-heads", type=int, default=16)
     ap.add_argument("--stream-steps", type=int, default=2)
+    ap.add_argument("--only", default="",
+                    help="comma list of dense,sparse,kv4,stream (profiling runs; no JSON line "
+                         "unless dense is included)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run three 512 MiB device-to-device copies (a kernel of known "
+                         "traffic, for scaling hardware byte counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
@@ -370,6 +376,24 @@ def main(argv=None) -> int:
         return 1
     da.load()
     torch.cuda.set_device(0)
+    only = set(x for x in args.only.split(",") if x)
+
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration: 3 device copies of 512 MiB (read 512 MiB + write 512 MiB each)")
+        del src, dst
+
+    if only and "dense" not in only:
+        runners = {"sparse": bench_sparse, "kv4": bench_kv4, "stream": bench_stream}
+        for name in ("sparse", "kv4", "stream"):
+            if name in only:
+                torch.cuda.empty_cache()
+                print(json.dumps({name: runners[name](args, torch, np, da, synth)}), flush=True)
+        return 0
 
     c, dense = bench_dense(args, torch, np, da, synth)
     cpu = None
@@ -379,6 +403,15 @@ def main(argv=None) -> int:
         log(f"cpu oracle: {cpu['value']:.2f} GB/s on {cpu['cores']} threads")
     del c
     extra = {}
+    if only:
+        args.no_extra = True
+        for key, name, fn in (("sparse", "page_sparse", bench_sparse), ("kv4", "uint4", bench_kv4)):
+            if key in only:
+                torch.cuda.empty_cache()
+                extra[name] = fn(args, torch, np, da, synth)
+        if "stream" in only:
+            torch.cuda.empty_cache()
+            extra["headwise_stream"] = bench_stream(args, torch, np, da, synth)
     if not args.no_extra:
         for name, fn in (("page_sparse", bench_sparse), ("uint4", bench_kv4)):
             torch.cuda.empty_cache()
