@@ -69,6 +69,31 @@ def time_events(torch, fn, steps: int, warmup: int, stream=None) -> float:
     return a.elapsed_time(b) / steps
 
 
+def capture(torch, fn, n: int = 2):
+    """Capture fn(0) .. fn(n-1) into one HIP graph (after warming them up on
+    a side stream, as graph capture requires)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(n):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, fn, steps: int, warmup: int, per_graph: int = 2) -> float:
+    """Average ms per step with `per_graph` steps captured in one HIP graph."""
+    g = capture(torch, fn, per_graph)
+    reps = max(1, -(-steps // per_graph))
+    return time_events(torch, lambda i: g.replay(), reps, max(1, warmup // per_graph)) / per_graph
+
+
 def time_each(torch, fn, steps: int, stream=None) -> float:
     """Mean of per-launch event durations (events recorded on `stream`)."""
     stream = stream or torch.cuda.current_stream()
@@ -102,22 +127,25 @@ def bench_dense(args, torch, np, da, synth):
     vs.append(vs[0].clone())
     out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
     ns = da.da_decode_attention_n_split(B, Hq, Hkv, D, N)
-    ws = torch.empty((B, Hq, ns, D + 4), dtype=torch.float32, device="cuda")
+    ws_p = torch.empty((B, Hq, ns, D + 4), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(da.da_decode_attention_workspace(B, Hq, Hkv, D, N), dtype=torch.uint8,
+                     device="cuda")
 
     def step(i):
         da.da_decode_attention(q, ks[i & 1], vs[i & 1], scale=c.scale, out=out, ws=ws)
 
-    ms = time_events(torch, step, args.steps, args.warmup)
+    ms_eager = time_events(torch, step, args.steps, args.warmup)
+    ms = ms_eager if args.no_graph else time_graph(torch, step, args.steps, args.warmup)
 
     def partial(i):
-        da.da_decode_attention_partials(q, ks[i & 1], vs[i & 1], scale=c.scale, ws=ws)
+        da.da_decode_attention_partials(q, ks[i & 1], vs[i & 1], scale=c.scale, ws=ws_p)
 
     for i in range(3):
         partial(i)
     ms_partial = time_each(torch, partial, args.steps)
 
     def merge(i):
-        da.da_merge_partials(ws, out=out)
+        da.da_merge_partials(ws_p, out=out)
 
     ms_merge = time_each(torch, merge, args.steps)
 
@@ -132,8 +160,9 @@ def bench_dense(args, torch, np, da, synth):
         "ms_per_step": ms, "gbs": gbs, "tokens_per_s": B / (ms * 1e-3),
         "step_bytes": step_bytes, "partial_ms": ms_partial, "partial_bytes": part_bytes,
         "partial_gbs": part_gbs, "merge_ms": ms_merge, "n_split": ns,
+        "eager_ms_per_step": ms_eager, "launch": "eager" if args.no_graph else "hip-graph, 2 steps per replay",
     }
-    log(f"dense: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s); "
+    log(f"dense: {ms * 1e3:.1f} us/step (eager {ms_eager * 1e3:.1f}), {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s); "
         f"partial pass {ms_partial * 1e3:.1f} us ({part_gbs:.0f} GB/s), merge {ms_merge * 1e3:.1f} us")
     return c, res
 
@@ -185,7 +214,7 @@ def bench_sparse(args, torch, np, da, synth):
     idx = torch.empty((B, H, K), dtype=torch.int32, device="cuda")
     out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
     wsz = 4 * B * H * D
-    ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(1 << 24, dtype=torch.uint8, device="cuda")
 
     def step(i):
         kk, vv = copies[i & 1]
@@ -193,7 +222,8 @@ def bench_sparse(args, torch, np, da, synth):
         da.da_select_pages(q, mn, mx, S, K, N, page_idx=idx)
         da.da_decode_attention_paged(q, kk, vv, idx, S, out=out, ws=ws)
 
-    ms = time_events(torch, step, args.steps, args.warmup)
+    ms_eager = time_events(torch, step, args.steps, args.warmup)
+    ms = ms_eager if args.no_graph else time_graph(torch, step, args.steps, args.warmup)
 
     def sel(i):
         mn, mx = metas[i & 1]
@@ -206,7 +236,7 @@ def bench_sparse(args, torch, np, da, synth):
         da.da_decode_attention_paged(q, kk, vv, idx, S, out=out, ws=ws)
 
     ms_gather = time_each(torch, gather, args.steps)
-    wsd = torch.empty(1 << 26, dtype=torch.uint8, device="cuda")
+    wsd = torch.zeros(1 << 26, dtype=torch.uint8, device="cuda")
 
     def dense(i):
         kk, vv = copies[i & 1]
@@ -224,7 +254,7 @@ def bench_sparse(args, torch, np, da, synth):
         "select_ms": ms_sel, "select_gbs": (meta_bytes + B * H * D * 2) / (ms_sel * 1e-3) / 1e9,
         "gather_attention_ms": ms_gather,
         "gather_gbs": (sel_kv_bytes + B * H * D * 6) / (ms_gather * 1e-3) / 1e9,
-        "page_meta_ms": ms_meta, "dense_same_cache_ms": ms_dense,
+        "page_meta_ms": ms_meta, "dense_same_cache_ms": ms_dense, "eager_ms_per_step": ms_eager,
         "speedup_vs_dense": ms_dense / ms,
     }
     log(f"sparse: {ms * 1e3:.1f} us/step ({gbs:.0f} GB/s), select {ms_sel * 1e3:.1f} us, "
@@ -248,13 +278,14 @@ def bench_kv4(args, torch, np, da, synth):
     ms_quant = time_events(torch, lambda i: da.da_quantize_kv4(k), 5, 1)
     copies = [da.da_quantize_kv4(k) + da.da_quantize_kv4(v) for _ in range(2)]
     out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
-    ws = torch.empty(1 << 26, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(1 << 26, dtype=torch.uint8, device="cuda")
 
     def step(i):
         kc, kmn, ksc, vc, vmn, vsc = copies[i & 1]
         da.da_decode_attention_kv4(q, kc, kmn, ksc, vc, vmn, vsc, out=out, ws=ws)
 
-    ms = time_events(torch, step, args.steps, args.warmup)
+    ms_eager = time_events(torch, step, args.steps, args.warmup)
+    ms = ms_eager if args.no_graph else time_graph(torch, step, args.steps, args.warmup)
     code_bytes = 2 * B * H * N * D // 2
     ms_bytes = 2 * 2 * B * H * N * (D // 64) * 2
     step_bytes = code_bytes + ms_bytes + B * H * D * 2 + B * H * D * 4
@@ -262,7 +293,7 @@ def bench_kv4(args, torch, np, da, synth):
     del k, v
     res = {"workload": "flexgen-uint4 B64 H56 D128 N1024 groups of 64", "ms_per_step": ms,
            "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "step_bytes": step_bytes,
-           "tokens_per_s": B / (ms * 1e-3), "quantize_k_ms": ms_quant}
+           "tokens_per_s": B / (ms * 1e-3), "quantize_k_ms": ms_quant, "eager_ms_per_step": ms_eager}
     log(f"kv4: {ms * 1e3:.1f} us/step ({gbs:.0f} GB/s)")
     return res
 
@@ -315,7 +346,7 @@ def bench_stream(args, torch, np, da, synth):
     buf1 = torch.empty(nb, dtype=torch.uint8, device="cuda")
     q = up(spec.q(), "f32", torch, np)
     out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(16, hs.workspace_bytes), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(16, hs.workspace_bytes), dtype=torch.uint8, device="cuda")
     L, H = spec.n_layers, spec.n_kv_heads
     k_list = [kh[(i) % pool_heads] for i in range(L * H)]
     v_list = [vh[(i) % pool_heads] for i in range(L * H)]
@@ -351,6 +382,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-stream", action="store_true", help="skip the head-wise streamed workload")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of HIP-graph replays of the step")
     ap.add_argument("--stream-pool-heads", type=int, default=16)
     ap.add_argument("--stream-steps", type=int, default=2)
     ap.add_argument("--only", default="",

@@ -87,6 +87,26 @@ def da_decode_attention(q, k, v, scale=None, split_tokens=0, out=None, ws=None, 
     return out
 
 
+def da_decode_attention_workspace(batch, n_q_heads, n_kv_heads, head_dim, n_ctx, q_dtype=DA_F32,
+                                  kv_dtype=DA_BF16, split_tokens=0) -> int:
+    s = attn_shape(batch, n_q_heads, n_kv_heads, head_dim, n_ctx, None, q_dtype, kv_dtype,
+                   split_tokens)
+    return int(load().da_decode_attention_workspace(ctypes.byref(s)))
+
+
+def da_decode_attention_paged_workspace(batch, n_heads, head_dim, n_ctx, page_size, top_k,
+                                        q_dtype=DA_F16, kv_dtype=DA_F16, split_tokens=0) -> int:
+    s = attn_shape(batch, n_heads, n_heads, head_dim, n_ctx, None, q_dtype, kv_dtype, split_tokens)
+    return int(load().da_decode_attention_paged_workspace(ctypes.byref(s), page_size, top_k))
+
+
+def da_decode_attention_kv4_workspace(batch, n_q_heads, n_kv_heads, head_dim, n_ctx,
+                                      q_dtype=DA_F16, split_tokens=0) -> int:
+    s = attn_shape(batch, n_q_heads, n_kv_heads, head_dim, n_ctx, None, q_dtype, DA_F16,
+                   split_tokens)
+    return int(load().da_decode_attention_kv4_workspace(ctypes.byref(s)))
+
+
 def da_decode_attention_n_split(batch, n_q_heads, n_kv_heads, head_dim, n_ctx, split_tokens=0) -> int:
     s = attn_shape(batch, n_q_heads, n_kv_heads, head_dim, n_ctx, None, DA_F32, DA_BF16, split_tokens)
     return int(load().da_decode_attention_n_split(ctypes.byref(s)))

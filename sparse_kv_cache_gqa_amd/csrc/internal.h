@@ -18,7 +18,7 @@ enum Fmt : int { FMT_F32 = 0, FMT_F16 = 1, FMT_BF16 = 2, FMT_U4 = 3 };
 constexpr int kDefaultSplitDenseMin = 256;
 constexpr int kDefaultSplitDense = 2048;
 constexpr int kDefaultSplitU4 = 512;
-constexpr int kDefaultSplitPaged = 256;
+constexpr int kDefaultSplitPaged = 512;
 
 // One attention launch (split-K partial pass + cross-split merge).
 // The KV cache is addressed by rows (tokens): row r of (batch b, KV head h)

@@ -34,8 +34,6 @@ using namespace dev;
 
 
 constexpr int kSub = 16;               // tokens per MFMA (its N dimension)
-constexpr int kTS = 2;                 // MFMA sub-tiles per wave iteration
-constexpr int kTile = kSub * kTS;      // tokens per wave iteration
 constexpr int kMaxPagesPerSplit = 1024;
 
 // Compile-time layout of one kernel instance.
@@ -57,6 +55,10 @@ struct Cfg {
     static constexpr int TPP = 1024 / R;                // token stride between V pieces
     static constexpr int CPL = KF == FMT_F32 ? 4 : (U4 ? 32 : 8);   // V channels per lane
     static constexpr int CH_LANES = R / 16;             // lanes covering one row (V side)
+    // sub-tiles per pipeline stage (measured on MI355X): 4 for 128-byte rows;
+    // 2 otherwise -- uint4 rows are VALU-heavy and deeper stages cost occupancy
+    static constexpr int TS = R == 128 ? 4 : 2;
+    static constexpr int TILE = kSub * TS;              // tokens per stage
     // 16 MFMA rows must hold every (head, group, split term); rows fit 64..1024 bytes
     static constexpr bool ok = RPH0 <= 4 && G * RPH <= 16 && R >= 64 && R <= 1024;
 };
@@ -84,15 +86,15 @@ __device__ __forceinline__ u32x4 u4_to_f16x8(uint32_t x) {
     return r;
 }
 
-// Registers of one pipeline stage: the K and V of kTS sub-tiles of 16 tokens.
+// Registers of one pipeline stage: the K and V of TS sub-tiles of 16 tokens.
 template <int KF, int QF, int D, int G>
 struct Stage {
     using C = Cfg<KF, QF, D, G>;
-    u32x4 K[kTS][C::NCH];
-    u32x4 V[kTS][C::VP];
-    bool kok[kTS];
-    uint32_t kmn[kTS], ksc[kTS];       // uint4: fp16 min/scale pairs of the K row (both groups)
-    float vmn[kTS], vsc[kTS];          // uint4: min/scale of the V row's group
+    u32x4 K[C::TS][C::NCH];
+    u32x4 V[C::TS][C::VP];
+    bool kok[C::TS];
+    uint32_t kmn[C::TS], ksc[C::TS];   // uint4: fp16 min/scale pairs of the K row (both groups)
+    float vmn[C::TS], vsc[C::TS];      // uint4: min/scale of the V row's group
 };
 
 // One wave per workgroup; the wave reduces one split of one (batch row, KV
@@ -107,6 +109,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a) {
     constexpr int NCH = C::NCH, NMF = C::NMF, VP = C::VP, TPP = C::TPP, CPL = C::CPL;
     constexpr int MT = C::U4 ? FMT_F16 : KF;
     constexpr int PSTR = D + 4;        // floats per partial row: u[D], m, l, pad, pad
+    constexpr int kTS = C::TS, kTile = C::TILE;
 
     __shared__ float p_lds[kTile][G];
     __shared__ int32_t pg_lds[PAGED ? kMaxPagesPerSplit : 1];
@@ -167,28 +170,37 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a) {
     };
 
     // ---- issue the loads of one tile ---------------------------------------
+    // dense: buffer resources over this split's rows (rows past the split
+    // read as zeros, so the last tile needs no per-lane masks)
+    // (unused in paged mode, where they cover nothing)
+    const uint32_t kv_bytes = PAGED ? 0u : (uint32_t)ntok * R;
+    const uint32_t ms_bytes = (PAGED || !C::U4) ? 0u : (uint32_t)ntok * NGRP * 2;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + s0 * R, kv_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase + s0 * R, kv_bytes);
+    const __amdgpu_buffer_rsrc_t kmrs = make_rsrc(kmn + s0 * NGRP, ms_bytes);
+    const __amdgpu_buffer_rsrc_t ksrs = make_rsrc(ksc + s0 * NGRP, ms_bytes);
+    const __amdgpu_buffer_rsrc_t vmrs = make_rsrc(vmn + s0 * NGRP, ms_bytes);
+    const __amdgpu_buffer_rsrc_t vsrs = make_rsrc(vsc + s0 * NGRP, ms_bytes);
+
     auto load_tile = [&](St &st, int t0) {
-        if (!PAGED && t0 + kTile <= ntok) {
-            // full dense tile: rows s0 + t0 .. s0 + t0 + 31, no masks
-            const char *kb = kbase + (s0 + t0) * R + 16 * g4;
-            const char *vb = vbase + (s0 + t0) * R + vcol;
+        if constexpr (!PAGED) {
 #pragma unroll
             for (int ts = 0; ts < kTS; ++ts) {
-                st.kok[ts] = true;
+                const int rk = t0 + ts * kSub + n16;          // row within the split
+                st.kok[ts] = rk < ntok;
 #pragma unroll
                 for (int c = 0; c < NCH; ++c)
-                    st.K[ts][c] = ld_stream(kb + (ts * kSub + n16) * R + 64 * c);
+                    st.K[ts][c] = buf_load16(krs, (uint32_t)rk * R + 16 * g4 + 64 * c);
 #pragma unroll
                 for (int p = 0; p < VP; ++p)
-                    st.V[ts][p] = ld_stream(vb + (ts * kSub + p * TPP + vtok) * R);
+                    st.V[ts][p] = buf_load16(vrs, (uint32_t)(t0 + ts * kSub + p * TPP + vtok) * R + vcol);
                 if constexpr (C::U4) {
-                    const int64_t rk = s0 + t0 + ts * kSub + n16;
-                    st.kmn[ts] = ld_stream32(kmn + rk * NGRP);
-                    st.ksc[ts] = ld_stream32(ksc + rk * NGRP);
-                    const int64_t rv = s0 + t0 + ts * kSub + vtok;     // VP == 1 for uint4
+                    st.kmn[ts] = buf_load4(kmrs, (uint32_t)rk * NGRP * 2);
+                    st.ksc[ts] = buf_load4(ksrs, (uint32_t)rk * NGRP * 2);
+                    const uint32_t rv = t0 + ts * kSub + vtok;     // VP == 1 for uint4
                     const int gr = vcol / 32;
-                    st.vmn[ts] = f16_to_f32(ld_stream16(vmn + rv * NGRP + gr));
-                    st.vsc[ts] = f16_to_f32(ld_stream16(vsc + rv * NGRP + gr));
+                    st.vmn[ts] = f16_to_f32(buf_load2(vmrs, (rv * NGRP + gr) * 2));
+                    st.vsc[ts] = f16_to_f32(buf_load2(vsrs, (rv * NGRP + gr) * 2));
                 }
             }
             return;
@@ -407,24 +419,27 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a) {
                         for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pv[h], xv, acc[h][e]);
                     }
                 } else if constexpr (C::U4) {
-                    float wv[G];
+                    // even channels: low nibbles -> c; odd channels: high
+                    // nibbles left in place -> 16 c, so their weight is w / 16
+                    float wv[G], wv16[G];
 #pragma unroll
                     for (int h = 0; h < G; ++h) {
                         wv[h] = pv[h] * st.vsc[ts];
+                        wv16[h] = wv[h] * 0.0625f;
                         amin[h] = fmaf(pv[h], st.vmn[ts], amin[h]);
                     }
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        const uint32_t lo = x[u] & 0x0F0F0F0Fu;
-                        const uint32_t hi = (x[u] >> 4) & 0x0F0F0F0Fu;
+                        const uint32_t lo = opaque(x[u] & 0x0F0F0F0Fu);
+                        const uint32_t hi = opaque(x[u] & 0xF0F0F0F0u);
 #pragma unroll
                         for (int bb = 0; bb < 4; ++bb) {
-                            const float c0 = (float)((lo >> (8 * bb)) & 0xFFu);
-                            const float c1 = (float)((hi >> (8 * bb)) & 0xFFu);
+                            const float c0 = ubyte_f32(lo, bb);
+                            const float c1 = ubyte_f32(hi, bb);
 #pragma unroll
                             for (int h = 0; h < G; ++h) {
                                 acc[h][8 * u + 2 * bb] = fmaf(wv[h], c0, acc[h][8 * u + 2 * bb]);
-                                acc[h][8 * u + 2 * bb + 1] = fmaf(wv[h], c1, acc[h][8 * u + 2 * bb + 1]);
+                                acc[h][8 * u + 2 * bb + 1] = fmaf(wv16[h], c1, acc[h][8 * u + 2 * bb + 1]);
                             }
                         }
                     }

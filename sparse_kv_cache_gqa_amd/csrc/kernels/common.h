@@ -52,6 +52,31 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 
+// Buffer resource over [base, base + bytes): loads through it use 32-bit
+// lane offsets, and any access at or beyond `bytes` returns zeros instead of
+// touching memory (hardware range check on the lane offset).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16-byte non-temporal (streaming) load through a buffer resource.
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 2);
+}
+__device__ __forceinline__ uint16_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 2);
+}
+
+// Hide a value's known bits from the optimiser (no instruction is emitted).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+// Byte n of x as float (selects v_cvt_f32_ubyte{0..3}).
+__device__ __forceinline__ float ubyte_f32(uint32_t x, int n) { return (float)(unsigned char)(x >> (8 * n)); }
+
 // Physical channel fed by MFMA `mf`, lane group g (lane / 16), element e, when
 // a lane loads 16 bytes at byte offset 64 * chunk + 16 * g of a row:
 //   fp32:  16x16x4 MFMA per element  -> channel 16 * chunk + 4 * g + e (mf = 4 * chunk + e)

@@ -141,7 +141,7 @@ def test_page_checks(lib):
     assert paged(s, 0) == L.DA_E_INVALID
     assert paged(mha(n_q_heads=32), 128) == L.DA_E_UNSUPPORTED
     need = lib.da_decode_attention_paged_workspace(ctypes.byref(s), 16, 128)
-    assert need == 32 * 16 * 8 * 68 * 4           # 128 pages of 16 = 2048 positions / 256
+    assert need == 32 * 16 * 4 * 68 * 4           # 128 pages of 16 = 2048 positions / 512
     assert paged(s, 128, need - 4) == L.DA_E_WORKSPACE
 
 

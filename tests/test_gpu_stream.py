@@ -41,7 +41,7 @@ def run_stream(da, spec, hpc, ks, vs):
     buf1 = torch.empty(hs.buffer_bytes, dtype=torch.uint8, device="cuda")
     q = to_dev(spec.q(), "f32")
     out = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(16, hs.workspace_bytes), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(16, hs.workspace_bytes), dtype=torch.uint8, device="cuda")
     comp = torch.cuda.current_stream()
     cpy = torch.cuda.Stream()
     cpy.wait_stream(comp)
