@@ -94,6 +94,24 @@ def time_graph(torch, fn, steps: int, warmup: int, per_graph: int = 2) -> float:
     return time_events(torch, lambda i: g.replay(), reps, max(1, warmup // per_graph)) / per_graph
 
 
+def measured_traffic(key: str, launch_bytes: int):
+    """Calibrated HBM bytes per launch from profiles/traffic.json, if it was
+    measured on the current kernel sources; else None."""
+    try:
+        from sparse_kv_cache_gqa_amd.pmc_traffic import source_hash
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            t = json.load(f)
+        if t.get("source_sha256") != source_hash() or key not in t["kernels"]:
+            return None
+        k = t["kernels"][key]
+        return {"fetch_bytes": k["fetch_bytes"], "write_bytes": k["write_bytes"],
+                "total_bytes": k["fetch_bytes"] + k["write_bytes"],
+                "vs_algorithmic": (k["fetch_bytes"] + k["write_bytes"]) / launch_bytes,
+                "source": "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, scaled by a 512 MiB copy"}
+    except (OSError, ValueError, KeyError):
+        return None
+
+
 def time_each(torch, fn, steps: int, stream=None) -> float:
     """Mean of per-launch event durations (events recorded on `stream`)."""
     stream = stream or torch.cuda.current_stream()
@@ -471,7 +489,8 @@ def main(argv=None) -> int:
                    "q_dtype": "f32", "accumulate": "f32", "parallelism": "single-gpu"},
         "tokens_per_s": dense["tokens_per_s"],
         "roofline": {"bound": "hbm", "achieved": dense["partial_gbs"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": dense["partial_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": dense["partial_gbs"] / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("attn_split_llama3_8b_32k", dense["partial_bytes"]),
                      "kernel": "attn_split_kernel (split-K partial pass)",
                      "bytes_per_launch": dense["partial_bytes"], "avg_launch_ms": dense["partial_ms"]},
         "cpu_baseline": cpu,
