@@ -14,11 +14,11 @@
 //      fp32; q in fp32 is split into 16-bit terms on the A rows.  Scores stay
 //      in LDS (and optionally go to page_score).
 //   2. Top-K by a most-significant-digit radix select (4 passes of 8 bits)
-//      over an order-preserving uint32 image of the fp32 scores, with
-//      per-wave LDS histograms.  Ties at the K-th score go to the lower page
+//      over an order-preserving uint32 image of the fp32 scores, one shared
+//      LDS histogram per pass.  Ties at the K-th score go to the lower page
 //      index: the equal keys are ranked by a block-wide prefix count in index
-//      order.  The kept indices are compacted in index order, so they come out
-//      ascending.
+//      order (skipped when every key equal to the K-th is kept).  The kept
+//      indices are compacted in index order, so they come out ascending.
 #include "common.h"
 
 namespace da {
@@ -159,9 +159,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int64_t P, int top_
     constexpr int SPL = (KF == FMT_F32 || QF == KF) ? 1 : (KF == FMT_BF16 ? 3 : 2);
 
     extern __shared__ float sc_lds[];              // [P]
-    __shared__ uint32_t hist[kSelWaves][256];
+    __shared__ uint32_t hist[256];
     __shared__ uint32_t scan_buf[kSelWaves + 1];
-    __shared__ uint32_t pick_digit, pick_need;
+    __shared__ uint32_t pick_digit, pick_need, pick_count;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g4 = lane >> 4, n16 = lane & 15;
@@ -242,28 +242,27 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int64_t P, int top_
     __syncthreads();
 
     // ---- 2. radix select of the top_k largest keys -------------------------
+    // MSB-first, 8 bits per pass, one shared 256-bin histogram per pass.
     uint32_t prefix = 0, pmask = 0;
     uint32_t need = (uint32_t)top_k;
+    uint32_t eq_count = 0;
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) hist[w][lane * 4 + j] = 0u;
+        if (tid < 256) hist[tid] = 0u;
         __syncthreads();
         for (int64_t i = tid; i < P; i += kSelThreads) {
             const uint32_t key = order_key(sc_lds[i]);
-            if ((key & pmask) == prefix) atomicAdd(&hist[w][(key >> shift) & 255u], 1u);
+            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
         }
         __syncthreads();
         if (w == 0) {
             uint32_t c[4], loc = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                uint32_t s = 0;
-                for (int ww = 0; ww < kSelWaves; ++ww) s += hist[ww][lane * 4 + j];
-                c[j] = s;
-                loc += s;
+                c[j] = hist[lane * 4 + j];
+                loc += c[j];
             }
-            // number of candidates in bins above this lane's four bins
+            // candidates in bins above this lane's four bins
             uint32_t suf = loc;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
@@ -276,6 +275,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int64_t P, int top_
                 if (cum < need && cum + c[j] >= need) {
                     pick_digit = (uint32_t)(lane * 4 + j);
                     pick_need = need - cum;
+                    pick_count = c[j];
                 }
                 cum += c[j];
             }
@@ -284,24 +284,30 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int64_t P, int top_
         prefix |= pick_digit << shift;
         pmask |= 0xFFu << shift;
         need = pick_need;
-        __syncthreads();
+        eq_count = pick_count;
     }
     const uint32_t T = prefix;              // key of the top_k-th largest score
 
     // ---- 3. ties by lower index; compact in index order --------------------
+    // Keep every key > T and the `need` lowest-indexed keys == T.  When all
+    // eq_count keys equal to T are kept (need == eq_count) that is key >= T.
     const int64_t E = (P + kSelThreads - 1) / kSelThreads;
     const int64_t i0 = (int64_t)tid * E, i1 = min(i0 + E, P);
-    uint32_t n_eq = 0;
-    for (int64_t i = i0; i < i1; ++i) n_eq += order_key(sc_lds[i]) == T;
     uint32_t tot;
-    uint32_t eq_before = block_exscan(n_eq, scan_buf, &tot);
+    uint32_t eq_before = 0;
+    const bool all_ties = need == eq_count;
+    if (!all_ties) {
+        uint32_t n_eq = 0;
+        for (int64_t i = i0; i < i1; ++i) n_eq += order_key(sc_lds[i]) == T;
+        eq_before = block_exscan(n_eq, scan_buf, &tot);
+    }
     uint32_t n_sel = 0;
     {
         uint32_t r = eq_before;
         for (int64_t i = i0; i < i1; ++i) {
             const uint32_t key = order_key(sc_lds[i]);
             if (key > T) ++n_sel;
-            else if (key == T) { if (r < need) ++n_sel; ++r; }
+            else if (key == T) { if (all_ties || r < need) ++n_sel; ++r; }
         }
     }
     uint32_t pos = block_exscan(n_sel, scan_buf, &tot);
@@ -311,7 +317,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int64_t P, int top_
         for (int64_t i = i0; i < i1; ++i) {
             const uint32_t key = order_key(sc_lds[i]);
             bool sel = key > T;
-            if (key == T) { sel = r < need; ++r; }
+            if (key == T) { sel = all_ties || r < need; ++r; }
             if (sel && pos < (uint32_t)top_k) out[pos++] = (int32_t)i;
         }
     }

@@ -138,3 +138,27 @@ def test_workload3_full_size_sampled(da):
         check_selection(idx[b:b + 1, h:h + 1], r, K)
         ref = sparse_attention(q64, k64, v64, idx[b:b + 1, h:h + 1], S, c.scale)
         assert_close(o[b, h], ref[0, 0], atol=1e-3, rel_rms=1e-4, what=f"w3 b{b} h{h}")
+
+
+@pytest.mark.parametrize("P,K", [(64, 10), (300, 77), (2048, 128)])
+def test_selection_with_exact_ties(da, P, K):
+    """Pages are copies of four patterns, so bound scores take four values
+    and the k-th score is shared by many pages: the lower indices must win,
+    exactly as in the oracle (equal scores are equal in fp32 too)."""
+    import torch
+    rng = np.random.default_rng(P)
+    S, D = 4, 64
+    pats = rng.standard_normal((4, S, D)).astype(np.float16)
+    which = rng.integers(0, 4, size=P)
+    k = pats[which].reshape(1, 1, P * S, D)
+    q = rng.standard_normal((1, 1, D)).astype(np.float16)
+    kmin, kmax = da.da_build_page_meta(to_dev(k, "f16"), S)
+    idx, score = da.da_select_pages(to_dev(q, "f16"), kmin, kmax, S, K, P * S, want_scores=True)
+    torch.cuda.synchronize()
+    rmin, rmax = page_meta(as_f64(k, "f16"), S)
+    r = bound_scores(as_f64(q, "f16"), rmin, rmax)
+    s = score.cpu().numpy()
+    # identical pages give identical fp32 scores; rank by (-score, index) on them
+    order = sorted(range(P), key=lambda j: (-float(s[0, 0, j]), j))
+    assert idx.cpu().numpy()[0, 0].tolist() == sorted(order[:K])
+    check_selection(idx.cpu().numpy(), r, K)
