@@ -185,27 +185,38 @@ def bench_dense(args, torch, np, da, synth):
     return c, res
 
 
+def time_oracle(fn, min_total: float, min_runs: int = 3, max_runs: int = 50):
+    """Median wall time of fn() over repeated runs (after one warm-up) until
+    min_total seconds of runs have accumulated."""
+    fn()
+    runs = []
+    while len(runs) < max_runs and (len(runs) < min_runs or sum(runs) < min_total):
+        t = time.perf_counter()
+        fn()
+        runs.append(time.perf_counter() - t)
+    return statistics.median(runs), len(runs), sum(runs)
+
+
 def cpu_baseline_dense(c, np):
-    """The fp64 oracle on batch row 0 of the same workload (all 32 query heads)."""
+    """The fp64 oracle on the whole step of the same workload (all batch rows
+    and query heads), repeated for about ten seconds of CPU time."""
     from oracle import decode_attention
     from oracle.numerics import as_f64
+    B, Hq, Hkv, D, N = c.shape
+    rows = B
 
     def once():
-        t = time.perf_counter()
-        decode_attention(as_f64(c.q[0:1], "f32"), as_f64(c.k[0:1], "bf16"),
-                         as_f64(c.v[0:1], "bf16"), c.scale)
-        return time.perf_counter() - t
+        decode_attention(as_f64(c.q[0:rows], "f32"), as_f64(c.k[0:rows], "bf16"),
+                         as_f64(c.v[0:rows], "bf16"), c.scale)
 
-    once()
-    runs = [once() for _ in range(3)]
-    sec = statistics.median(runs)
-    B, Hq, Hkv, D, N = c.shape
-    sample_bytes = 2 * Hkv * N * D * 2 + Hq * D * 4 * 2
+    sec, n, total = time_oracle(once, 10.0)
+    sample_bytes = rows * (2 * Hkv * N * D * 2 + Hq * D * 4 * 2)
     return {
         "value": sample_bytes / sec / 1e9, "unit": "GB/s", "cores": cpu_threads(), "kind": "oracle",
-        "sample": f"batch row 0 of {B} (all {Hq} query heads over {N} tokens), median of 3 runs "
-                  f"after 1 warm-up, {sec:.2f} s per run",
-        "tokens_per_s": 1.0 / sec,
+        "sample": f"the whole step ({rows} batch rows x {Hq} query heads over {N} tokens, inputs "
+                  f"converted from storage types inside the timed call), median of {n} runs after "
+                  f"1 warm-up, {sec:.2f} s per run, {total:.1f} s in all",
+        "tokens_per_s": rows / sec,
     }
 
 
@@ -222,6 +233,7 @@ def bench_sparse(args, torch, np, da, synth):
     q = up(c.q, "f16", torch, np)
     k0 = up(c.k, "f16", torch, np)
     v0 = up(c.v, "f16", torch, np)
+    host = None if args.no_cpu else (c.q[0:1].copy(), c.k[0:1].copy(), c.v[0:1].copy())
     del c
     copies = [(k0, v0), (k0.clone(), v0.clone())]
     metas = []
@@ -277,7 +289,62 @@ def bench_sparse(args, torch, np, da, synth):
     }
     log(f"sparse: {ms * 1e3:.1f} us/step ({gbs:.0f} GB/s), select {ms_sel * 1e3:.1f} us, "
         f"gather {ms_gather * 1e3:.1f} us, dense on same cache {ms_dense * 1e3:.1f} us")
+    if not args.no_sweep:
+        res["page_size_sweep"] = sparse_sweep(args, torch, da, q, copies, B, H, D, N)
+    if host is not None:
+        res["cpu_baseline"] = cpu_sparse(host, S, K, step_bytes / B)
     return res
+
+
+def sparse_sweep(args, torch, da, q, copies, B, H, D, N):
+    """TinyServe's page-size and selection-ratio trade-off on the same cache:
+    page sizes 4..64 at a 2048-token budget, and ratios K/P of 0.1, 0.3, 0.5
+    at page size 16.  Bytes per step follow the memory model: metadata
+    2 * (N/S) * D * 2 B + kept K/V 2 * K * S * D * 2 B per head."""
+    rows = []
+    cases = [(S, 2048 // S) for S in (4, 8, 16, 32, 64)]
+    cases += [(16, int(round(r * (N // 16)))) for r in (0.1, 0.3, 0.5)]
+    ws = torch.zeros(1 << 26, dtype=torch.uint8, device="cuda")
+    for S, K in cases:
+        P = N // S
+        metas = [da.da_build_page_meta(kk, S) for kk, _ in copies]
+        idx = torch.empty((B, H, K), dtype=torch.int32, device="cuda")
+        out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+
+        def step(i):
+            kk, vv = copies[i & 1]
+            da.da_select_pages(q, *metas[i & 1], S, K, N, page_idx=idx)
+            da.da_decode_attention_paged(q, kk, vv, idx, S, out=out, ws=ws)
+
+        ms = time_graph(torch, step, max(10, args.steps // 2), 4)
+        nbytes = B * H * (2 * P * D * 2 + 2 * K * S * D * 2)
+        rows.append({"page_size": S, "top_k": K, "ratio": K / P, "tokens": K * S,
+                     "ms_per_step": ms, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                     "model_fraction_of_dense": 1.0 / S + K * S / N})
+        del metas
+    log("page-size sweep: " + ", ".join(f"S{r['page_size']}/K{r['top_k']} {r['ms_per_step'] * 1e3:.0f}us"
+                                         for r in rows))
+    return rows
+
+
+def cpu_sparse(host, S, K, bytes_per_row):
+    """Oracle select + sparse attention on batch row 0 (all heads)."""
+    import numpy as np
+    from oracle import bound_scores, page_meta, sparse_attention, topk_pages
+    from oracle.numerics import as_f64
+    q, k, v = host
+
+    def once():
+        k64 = as_f64(k, "f16")
+        mn, mx = page_meta(k64, S)
+        idx = topk_pages(bound_scores(as_f64(q, "f16"), mn, mx), K)
+        sparse_attention(as_f64(q, "f16"), k64, as_f64(v, "f16"), idx, S, 1.0 / np.sqrt(q.shape[-1]))
+
+    sec, n, _ = time_oracle(once, 3.0)
+    return {"value": bytes_per_row / sec / 1e9, "unit": "GB/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"batch row 0 of 32 (16 heads): page metadata, bound scores, top-{K} and sparse "
+                      f"attention, median of {n} runs after 1 warm-up, {sec:.2f} s per run (metadata build "
+                      f"included; bytes counted as in the GPU step)"}
 
 
 # ---------------------------------------------------------------------------
@@ -292,6 +359,7 @@ def bench_kv4(args, torch, np, da, synth):
     q = up(c.q, "f16", torch, np)
     k = up(c.k, "f16", torch, np)
     v = up(c.v, "f16", torch, np)
+    host = None if args.no_cpu else (c.q[0:1].copy(), c.k[0:1].copy(), c.v[0:1].copy())
     del c
     ms_quant = time_events(torch, lambda i: da.da_quantize_kv4(k), 5, 1)
     copies = [da.da_quantize_kv4(k) + da.da_quantize_kv4(v) for _ in range(2)]
@@ -313,7 +381,26 @@ def bench_kv4(args, torch, np, da, synth):
            "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "step_bytes": step_bytes,
            "tokens_per_s": B / (ms * 1e-3), "quantize_k_ms": ms_quant, "eager_ms_per_step": ms_eager}
     log(f"kv4: {ms * 1e3:.1f} us/step ({gbs:.0f} GB/s)")
+    if host is not None:
+        res["cpu_baseline"] = cpu_kv4(host, step_bytes / B)
     return res
+
+
+def cpu_kv4(host, bytes_per_row):
+    """Oracle uint4 dequantize + attention on batch row 0 (all 56 heads)."""
+    import numpy as np
+    from oracle import kv4_attention, quantize_kv4
+    from oracle.numerics import as_f64
+    q, k, v = host
+    kq, vq = quantize_kv4(k), quantize_kv4(v)
+
+    def once():
+        kv4_attention(as_f64(q, "f16"), *kq, *vq, 1.0 / np.sqrt(q.shape[-1]))
+
+    sec, n, _ = time_oracle(once, 3.0)
+    return {"value": bytes_per_row / sec / 1e9, "unit": "GB/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"batch row 0 of 64 (56 heads x 1024 tokens): dequantize + attention, median of {n} "
+                      f"runs after 1 warm-up, {sec:.2f} s per run"}
 
 
 # ---------------------------------------------------------------------------
@@ -357,29 +444,38 @@ def bench_stream(args, torch, np, da, synth):
     h2d_ms = time_events(torch, h2d, 6, 2, stream=cs)
     h2d_gbs = hb / (h2d_ms * 1e-3) / 1e9
 
-    hs = da.HeadwiseStream(spec.batch, spec.n_q_heads, spec.n_kv_heads, spec.head_dim, spec.n_ctx,
-                           da.DA_F32, da.DA_BF16, heads_per_chunk=1)
-    nb = hs.buffer_bytes
-    buf0 = torch.empty(nb, dtype=torch.uint8, device="cuda")
-    buf1 = torch.empty(nb, dtype=torch.uint8, device="cuda")
     q = up(spec.q(), "f32", torch, np)
     out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
-    ws = torch.zeros(max(16, hs.workspace_bytes), dtype=torch.uint8, device="cuda")
     L, H = spec.n_layers, spec.n_kv_heads
     k_list = [kh[(i) % pool_heads] for i in range(L * H)]
     v_list = [vh[(i) % pool_heads] for i in range(L * H)]
     comp = torch.cuda.current_stream()
     cpy = torch.cuda.Stream()
-
-    def step(i):
-        cpy.wait_stream(comp)
-        hs.da_stream_headwise(k_list, v_list, buf0, buf1, q, out, ws, comp, cpy)
-
-    steps = args.stream_steps
-    ms = time_events(torch, step, steps, 1)
     total = 2 * L * H * hb
+    steps = args.stream_steps
+    grouping = {}
+    for hpc in ([1] if args.no_sweep else [1, 2, 8]):
+        hs = da.HeadwiseStream(spec.batch, spec.n_q_heads, spec.n_kv_heads, spec.head_dim, spec.n_ctx,
+                               da.DA_F32, da.DA_BF16, heads_per_chunk=hpc)
+        nb = hs.buffer_bytes
+        buf0 = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        buf1 = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(16, hs.workspace_bytes), dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            cpy.wait_stream(comp)
+            hs.da_stream_headwise(k_list, v_list, buf0, buf1, q, out, ws, comp, cpy)
+
+        t = time_events(torch, step, steps if hpc == 1 else 1, 1)
+        grouping[hpc] = {"ms_per_step": t, "h2d_gbs": total / (t * 1e-3) / 1e9,
+                         "device_buffer_bytes": 2 * nb}
+        hs.close()
+        del buf0, buf1, ws
+        torch.cuda.empty_cache()
+        log(f"stream heads_per_chunk={hpc}: {t:.0f} ms/step, {total / (t * 1e-3) / 1e9:.1f} GB/s, "
+            f"device buffers {2 * nb / 2**30:.0f} GiB")
+    ms = grouping[1]["ms_per_step"]
     gbs = total / (ms * 1e-3) / 1e9
-    hs.close()
     res = {"workload": "headinfer-headwise L32 Hkv8 Hq32 D128 N1048576 bf16 B1",
            "ms_per_step": ms, "h2d_bytes_per_step": total, "h2d_gbs": gbs,
            "measured_h2d_peak_gbs": h2d_gbs, "frac_measured_h2d": gbs / h2d_gbs,
@@ -387,9 +483,31 @@ def bench_stream(args, torch, np, da, synth):
            "steps": steps,
            "pool": f"{pool_heads} distinct pinned layer-heads ({2 * pool_heads * hb / 2**30:.0f} GiB) "
                    f"reused cyclically for the 256 layer-heads of a step; every layer-head is a real "
-                   f"512 MiB H2D copy"}
+                   f"512 MiB H2D copy",
+           "head_grouping": {str(k): v for k, v in grouping.items()}}
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_stream(spec, kh[0], vh[0], hb)
     log(f"stream: {ms:.0f} ms/step, {gbs:.1f} GB/s H2D vs measured peak {h2d_gbs:.1f} GB/s")
     return res
+
+
+def cpu_stream(spec, kh0, vh0, hb):
+    """Oracle head-wise driver on one layer-head (512 MiB of K/V)."""
+    import numpy as np
+    import torch
+    from oracle import headwise_attention
+    from oracle.numerics import as_f64
+    q = as_f64(spec.q(), spec.q_dtype)[0:1, :, 0:4]
+    k = kh0.view(torch.int16).numpy().view(np.uint16)
+    v = vh0.view(torch.int16).numpy().view(np.uint16)
+
+    def once():
+        headwise_attention(q, [[as_f64(k, "bf16")]], [[as_f64(v, "bf16")]], 1.0 / np.sqrt(spec.head_dim))
+
+    sec, n, _ = time_oracle(once, 3.0)
+    return {"value": 2 * hb / sec / 1e9, "unit": "GB/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"one layer-head (K and V of 2^20 tokens, 512 MiB), median of {n} runs after 1 warm-up, {sec:.2f} s "
+                      f"per run; a full step (256 layer-heads) would take about {256 * sec:.0f} s"}
 
 
 def main(argv=None) -> int:
@@ -400,6 +518,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-stream", action="store_true", help="skip the head-wise streamed workload")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the page-size and head-grouping sweeps")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of HIP-graph replays of the step")
     ap.add_argument("--stream-pool-heads", type=int, default=16)
