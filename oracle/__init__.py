@@ -21,7 +21,8 @@ Sources (the pages these functions follow):
 
 Modules:
 
-* :mod:`oracle.attention` -- dense / GQA decode attention, head-wise driver.
+* :mod:`oracle.attention` -- dense / GQA decode attention, its split-K
+  partials and their merge, head-wise driver.
 * :mod:`oracle.paged` -- page metadata, bound score, top-K, sparse attention.
 * :mod:`oracle.kv4` -- uint4 group quantization, dequantization, attention.
 
@@ -30,7 +31,8 @@ invariants, brute force on tiny inputs or an independent library routine (see
 ``tests/test_oracle_*.py``); none is "parity unpinned".
 """
 from .numerics import as_f64, f64_to_f16_bits  # noqa: F401
-from .attention import decode_attention, headwise_attention  # noqa: F401
+from .attention import (decode_attention, headwise_attention,  # noqa: F401
+                        split_partials, merge_partials)
 from .paged import (page_meta, bound_scores, topk_pages,  # noqa: F401
                     sparse_attention)
 from .kv4 import quantize_kv4, dequantize_kv4, kv4_attention  # noqa: F401

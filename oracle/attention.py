@@ -39,6 +39,49 @@ def decode_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     return o
 
 
+def split_partials(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                   split_tokens: int):
+    """Flash-decode partials of each token split (the split-K form of the
+    per-head equation: the softmax over all N tokens factors into per-split
+    maxima, sums and unnormalised outputs).
+
+    Split s covers tokens [s * S, min((s + 1) * S, N)), S = split_tokens.
+    For every (b, query head j, split s), with h = j // G and
+    x_i = scale * q[b,j] . k[b,h,i] over the split's tokens:
+    m = max x_i, l = sum exp(x_i - m), u = sum exp(x_i - m) v[b,h,i].
+    Returns u [B][Hq][n_split][D], m and l [B][Hq][n_split] (natural base).
+    """
+    B, Hq, D = q.shape
+    _, Hkv, N, _ = k.shape
+    G = Hq // Hkv
+    S = int(split_tokens)
+    ns = -(-N // S)
+    u = np.zeros((B, Hq, ns, D))
+    m = np.empty((B, Hq, ns))
+    l = np.empty((B, Hq, ns))
+    for b in range(B):
+        for j in range(Hq):
+            h = j // G
+            for s in range(ns):
+                t0, t1 = s * S, min((s + 1) * S, N)
+                x = scale * (k[b, h, t0:t1] @ q[b, j])
+                m[b, j, s] = x.max()
+                e = np.exp(x - m[b, j, s])
+                l[b, j, s] = e.sum()
+                u[b, j, s] = e @ v[b, h, t0:t1]
+    return u, m, l
+
+
+def merge_partials(u: np.ndarray, m: np.ndarray, l: np.ndarray) -> np.ndarray:
+    """Combine split partials: M = max_s m_s, L = sum_s l_s exp(m_s - M),
+    o = sum_s u_s exp(m_s - M) / L.  A split with m = -inf (no tokens)
+    carries no weight.  u [..., n_split, D], m and l [..., n_split]."""
+    M = m.max(axis=-1, keepdims=True)
+    w = np.where(np.isneginf(m), 0.0, np.exp(m - M))
+    L = (w * l).sum(axis=-1)
+    return (w[..., None] * u).sum(axis=-2) / L[..., None]
+
+
 def headwise_attention(q: np.ndarray, k_heads, v_heads, scale: float) -> np.ndarray:
     """Head-by-head decode over a multi-layer cache (HeadInfer).
 

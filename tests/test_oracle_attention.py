@@ -4,7 +4,10 @@ Each check is independent of the oracle's own formula: an independent library
 implementation (torch's scaled_dot_product_attention on CPU in float64), closed
 forms (one token, two tokens as a logistic blend, zero query, constant values),
 structural invariants (token permutation, score shift, GQA head mapping,
-batch independence) and a 50-digit brute force.
+batch independence) and a 50-digit brute force.  The split-K partials and
+their merge are pinned the same way: merged partials against torch's
+attention for ragged, single-token and whole-range splits, and the partial
+of one split against its closed form.
 """
 import math
 
@@ -12,7 +15,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import decode_attention, headwise_attention
+from oracle import decode_attention, headwise_attention, merge_partials, split_partials
 from oracle.numerics import as_f64
 
 pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
@@ -170,3 +173,55 @@ def test_headwise_equals_all_heads_at_once():
         vall = np.stack(vs[l], axis=1)
         ref = decode_attention(q[l], kall, vall, 0.25)
         np.testing.assert_array_equal(o[l], ref)
+
+
+def _sdpa(q, k, v):
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    G = q.shape[1] // k.shape[1]
+    tq = torch.from_numpy(q)[:, :, None, :]
+    tk = torch.from_numpy(k).repeat_interleave(G, dim=1).contiguous()
+    tv = torch.from_numpy(v).repeat_interleave(G, dim=1).contiguous()
+    return F.scaled_dot_product_attention(tq, tk, tv)[:, :, 0, :].numpy()
+
+
+@pytest.mark.parametrize("S", [1, 7, 16, 37, 64])
+def test_merged_split_partials_match_torch_sdpa(S):
+    q, k, v = _rand(500 + S, 2, 8, 2, 16, 37)
+    u, m, l = split_partials(q, k, v, 0.25, S)
+    assert u.shape == (2, 8, -(-37 // S), 16)
+    np.testing.assert_allclose(merge_partials(u, m, l), _sdpa(q, k, v), rtol=0, atol=1e-12)
+
+
+def test_one_split_partial_is_max_sum_and_unnormalised_output():
+    q, k, v = _rand(510, 1, 4, 2, 8, 20)
+    u, m, l = split_partials(q, k, v, 1.0 / math.sqrt(8), 20)
+    torch = pytest.importorskip("torch")
+    for j in range(4):
+        h = j // 2
+        x = (torch.from_numpy(k[0, h]) @ torch.from_numpy(q[0, j])).numpy() / math.sqrt(8)
+        assert m[0, j, 0] == pytest.approx(x.max(), abs=1e-14)
+        assert l[0, j, 0] >= 1.0
+    np.testing.assert_allclose(u[..., 0, :] / l[..., 0, None], _sdpa(q, k, v), rtol=0, atol=1e-12)
+
+
+def test_single_token_splits_carry_their_score_and_value():
+    q, k, v = _rand(511, 1, 2, 1, 4, 3)
+    u, m, l = split_partials(q, k, v, 0.5, 1)
+    for i in range(3):
+        assert m[0, 0, i] == pytest.approx(0.5 * float(q[0, 0] @ k[0, 0, i]), abs=1e-14)
+        assert l[0, 0, i] == 1.0
+        np.testing.assert_array_equal(u[0, 0, i], v[0, 0, i])
+
+
+def test_merge_ignores_split_order_and_empty_splits():
+    q, k, v = _rand(512, 1, 4, 1, 8, 50)
+    u, m, l = split_partials(q, k, v, 0.3, 8)
+    o = merge_partials(u, m, l)
+    perm = np.random.default_rng(0).permutation(u.shape[2])
+    np.testing.assert_allclose(merge_partials(u[:, :, perm], m[:, :, perm], l[:, :, perm]), o,
+                               rtol=0, atol=1e-14)
+    ue = np.concatenate([u, np.zeros_like(u[:, :, :1])], axis=2)
+    me = np.concatenate([m, np.full_like(m[:, :, :1], -np.inf)], axis=2)
+    le = np.concatenate([l, np.zeros_like(l[:, :, :1])], axis=2)
+    np.testing.assert_allclose(merge_partials(ue, me, le), o, rtol=0, atol=1e-15)
