@@ -117,6 +117,11 @@ const char *da_last_error(void);
  *      per-split (max, sum, unnormalised output) partials; contents on entry
  *      are ignored.
  * Two kernels on `stream`: a split-K partial pass and a cross-split merge.
+ * When there is one split, or at most four splits per (batch row, KV head)
+ * with at least 256 such units and at most 4096 splits in all, the splits of
+ * a unit instead run as the waves of one workgroup and merge in LDS: one
+ * kernel, the same result bit for bit, and ws is not written.  The same rule
+ * holds for the paged, uint4 and head-wise entry points.
  * ------------------------------------------------------------------------ */
 size_t da_decode_attention_workspace(const da_attn_shape *s);
 da_status da_decode_attention(const da_attn_shape *s, const void *q,
@@ -130,7 +135,8 @@ da_status da_decode_attention(const da_attn_shape *s, const void *q,
  *
  * da_decode_attention_partials: the split-K pass only.  Writes, for every
  *   query-head row r = b * n_q_heads + j and split i (tokens
- *   [i * split, min((i+1) * split, n_ctx)), split = split_tokens or 512),
+ *   [i * split, min((i+1) * split, n_ctx)), split = split_tokens or the
+ *   dense default above),
  *   ws[r][i][0..head_dim+3] fp32 = (u[0..head_dim-1], m, l, pad, pad)
  *   with m = max_t x_t, l = sum_t 2^(x_t - m), u = sum_t 2^(x_t - m) v_t and
  *   x_t = scale * log2(e) * q . k_t (base-2 logits).  n_split is

@@ -46,7 +46,16 @@ struct AttnLaunch {
     int32_t split_tokens = kDefaultSplitDense;
     int32_t n_split = 0;
     float *ws = nullptr;           // [B*Hkv*G][n_split][D+4]
+
+    // Waves per workgroup (1..kMaxWavesPerBlock); wave w of workgroup x
+    // reduces split x * wpb + w.  With `fused` set, one workgroup holds every
+    // split of its (b, h) (n_split <= wpb) and merges them through LDS into
+    // o; the workspace is then not touched and no merge kernel runs.
+    int32_t wpb = 1;
+    int32_t fused = 0;
 };
+
+constexpr int kMaxWavesPerBlock = 4;
 
 int32_t default_split_dense(int64_t n_ctx);
 
@@ -58,7 +67,9 @@ size_t attn_ws_bytes(int64_t rows, int32_t n_split, int32_t D);
 // True if a kernel is built for this combination.
 bool attn_supported(int kv_fmt, int q_fmt, int D, int G, bool paged);
 
-// Split-K partial pass + cross-split merge.
+// Split-K partial pass + cross-split merge.  When a (b, h) has at most
+// kMaxWavesPerBlock splits they run as the waves of one workgroup and merge
+// in LDS (same arithmetic, in the same order, as the merge kernel).
 hipError_t launch_attention(const AttnLaunch &a, hipStream_t stream);
 // The two halves on their own.  Partials: [rows][n_split][D + 4] fp32 holding
 // (unnormalised output u[D], max m of the base-2 logits, sum l of

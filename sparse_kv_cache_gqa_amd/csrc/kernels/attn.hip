@@ -3,9 +3,10 @@
 // Computes, per (batch row b, KV head h) and each of its G query heads, the
 // decode-attention output softmax(scale * q . k_i) v_i over a token range
 // (HeadInfer, section "核心 idea", per-head equation; TinyServe, section
-// "方法细节", Attn and SparseAttn).  One workgroup reduces one split of the
-// range to a partial (running max, running sum, unnormalised output); a second
-// kernel merges the splits.
+// "方法细节", Attn and SparseAttn).  One wave reduces one split of the range
+// to a partial (running max, running sum, unnormalised output); a second
+// kernel merges the splits, unless all splits of a (b, h) fit in one
+// workgroup, whose waves then merge them through LDS.
 //
 // Mapping to the hardware
 //   * q.K^T runs on the matrix cores.  A 16x16x32 MFMA takes 16 tokens as its
@@ -21,8 +22,11 @@
 //     into the scale); the per-head tile max is reduced with lane shuffles
 //     and broadcast with readlane; accumulators are rescaled only when a max
 //     changes.
-//   * The four waves of a workgroup merge through LDS; the partial goes to the
-//     workspace, and attn_reduce combines the splits of each query head.
+//   * A workgroup holds 1..4 waves, one split each.  Partials go to the
+//     workspace and attn_reduce combines the splits of each query head; or,
+//     when the workgroup holds every split of its (b, h), the partials go to
+//     LDS and the workgroup merges them itself, in the same order as
+//     attn_reduce (so both routes give identical bits).
 #include "common.h"
 
 #include <math.h>
@@ -35,6 +39,17 @@ using namespace dev;
 
 constexpr int kSub = 16;               // tokens per MFMA (its N dimension)
 constexpr int kMaxPagesPerSplit = 1024;
+
+// Pages per split of a paged launch.
+__host__ __device__ inline int pages_per_split(int split_tokens, int log2_page) {
+    const int pps = split_tokens >> log2_page;
+    return pps < 1 ? 1 : (pps > kMaxPagesPerSplit ? kMaxPagesPerSplit : pps);
+}
+
+// Dynamic LDS of the in-workgroup merge: one partial [G][D + 4] per wave.
+__host__ __device__ inline size_t merge_lds_bytes(int wpb, int G, int D) {
+    return (size_t)wpb * G * (D + 4) * sizeof(float);
+}
 
 // Compile-time layout of one kernel instance.
 template <int KF, int QF, int D, int G>
@@ -97,11 +112,11 @@ struct Stage {
     float vmn[C::TS], vsc[C::TS];      // uint4: min/scale of the V row's group
 };
 
-// One wave per workgroup; the wave reduces one split of one (batch row, KV
-// head) to a partial per query head.  Loads of the next 32-token tile are
-// issued before the current tile is computed (two register stages).
+// Each wave reduces one split of one (batch row, KV head) to a partial per
+// query head.  Loads of the next tile are issued before the current tile is
+// computed (two register stages).
 template <int KF, int QF, int D, int G, bool PAGED>
-__global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a) {
+__global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(AttnLaunch a) {
     using C = Cfg<KF, QF, D, G>;
     static_assert(C::ok, "unsupported layout");
     using St = Stage<KF, QF, D, G>;
@@ -111,25 +126,30 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a) {
     constexpr int PSTR = D + 4;        // floats per partial row: u[D], m, l, pad, pad
     constexpr int kTS = C::TS, kTile = C::TILE;
 
-    __shared__ float p_lds[kTile][G];
-    __shared__ int32_t pg_lds[PAGED ? kMaxPagesPerSplit : 1];
+    __shared__ float p_all[kMaxWavesPerBlock][G > 1 ? kTile * G : 1];            // p exchange
+    __shared__ int32_t pg_all[kMaxWavesPerBlock][PAGED ? kMaxPagesPerSplit : 1];  // page lists
+    extern __shared__ float mrg_lds[];                                            // merge slots
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int g4 = lane >> 4;          // lane group (MFMA k-chunk / C row block)
     const int n16 = lane & 15;         // token within sub-tile (K side)
-    const int split = blockIdx.x;
+    const int split = blockIdx.x * a.wpb + wave;
     const int unit = blockIdx.y;       // b * Hkv + h
     const int b = unit / a.Hkv;
     const int hkv = unit - b * a.Hkv;
+    const int pps = PAGED ? pages_per_split(a.split_tokens, a.log2_page) : 0;
 
-    // ---- token range of this split --------------------------------------
+    float *const p_lds = p_all[wave];
+    int32_t *const pg_lds = pg_all[wave];
+
+    // ---- token range of this split (empty past the last split) ----------
     int64_t s0 = 0;
     int ntok;
     int pg_mask = 0;
     if constexpr (PAGED) {
-        const int pps = min(kMaxPagesPerSplit, max(1, a.split_tokens >> a.log2_page));
         const int p0 = split * pps;
-        const int np = min(pps, a.top_k - p0);
+        const int np = max(0, min(pps, a.top_k - p0));
         const int32_t *lst = a.page_idx + (int64_t)unit * a.top_k + p0;
         for (int i = lane; i < np; i += 64) pg_lds[i] = lst[i];
         ntok = np << a.log2_page;
@@ -137,7 +157,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a) {
         wave_lds_sync();
     } else {
         s0 = (int64_t)split * a.split_tokens;
-        ntok = (int)min((int64_t)a.split_tokens, a.N - s0);
+        ntok = (int)max((int64_t)0, min((int64_t)a.split_tokens, a.N - s0));
     }
 
     const int64_t kvoff = (int64_t)b * a.kv_bstride + (int64_t)hkv * a.kv_hstride;
@@ -386,6 +406,9 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a) {
                 l_part[hh] *= al;
             }
         }
+        // G == 1: head 0's p of token (ts, n16) stays in lane n16 and the P.V
+        // lanes fetch it with a lane shuffle; otherwise p goes through LDS
+        float p0[kTS];
 #pragma unroll
         for (int hh = 0; hh < HPL; ++hh) {
             const int h = g4 * HPL + hh;
@@ -396,10 +419,14 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a) {
             for (int ts = 0; ts < kTS; ++ts) {
                 const float p = (sc[ts][hh] == neg_inf()) ? 0.f : fast_exp2(sc[ts][hh] - mh);
                 l_part[hh] += p;
-                if (h < G) p_lds[ts * kSub + n16][h] = p;
+                if constexpr (G == 1) {
+                    if (hh == 0) p0[ts] = p;
+                } else {
+                    if (h < G) p_lds[(ts * kSub + n16) * G + h] = p;
+                }
             }
         }
-        wave_lds_sync();
+        if constexpr (G > 1) wave_lds_sync();
 
         // P.V on the VALU
 #pragma unroll
@@ -408,8 +435,12 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a) {
             for (int p = 0; p < VP; ++p) {
                 const int t = ts * kSub + p * TPP + vtok;
                 float pv[G];
+                if constexpr (G == 1) {
+                    pv[0] = __shfl(p0[ts], p * TPP + vtok, 64);     // lane = token in the sub-tile
+                } else {
 #pragma unroll
-                for (int h = 0; h < G; ++h) pv[h] = p_lds[t][h];
+                    for (int h = 0; h < G; ++h) pv[h] = p_lds[t * G + h];
+                }
                 const u32x4 x = st.V[ts][p];
                 if constexpr (KF == FMT_F32) {
 #pragma unroll
@@ -463,7 +494,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a) {
                 }
             }
         }
-        wave_lds_sync();
+        if constexpr (G > 1) wave_lds_sync();
     };
 
     // ---- main loop: two register stages -------------------------------------
@@ -495,30 +526,69 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnLaunch a) {
             for (int c = 0; c < CPL; ++c) acc[h][c] += shfl_xor(acc[h][c], mask);
         }
     }
-    float *dst0 = a.ws + ((int64_t)unit * G * a.n_split + split) * PSTR;
-    const int64_t hstride = (int64_t)a.n_split * PSTR;
-    if (lane == 0) {
+    // to the workspace, or to this wave's LDS slot [G][PSTR] for the merge
+    // below (two separate store paths, so each keeps its own address space)
+    const bool fused = a.fused != 0;
+    auto emit = [&](float *dst0, int64_t hstride) {
+        if (lane == 0) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) dst0[h * hstride + D] = m_run[h];
-    }
-    if (n16 == 0) {
-#pragma unroll
-        for (int hh = 0; hh < HPL; ++hh) {
-            const int h = g4 * HPL + hh;
-            if (h < G) dst0[h * hstride + D + 1] = l_part[hh];
+            for (int h = 0; h < G; ++h) dst0[h * hstride + D] = m_run[h];
         }
-    }
-    if (lane < C::CH_LANES) {
-        const int c0 = KF == FMT_F32 ? vcol / 4 : (C::U4 ? vcol * 2 : vcol / 2);
+        if (n16 == 0) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-#pragma unroll
-            for (int c = 0; c < CPL; c += 4) {
-                f32x4 v4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v4[e] = acc[h][c + e] + (C::U4 ? amin[h] : 0.f);
-                *(f32x4 *)(dst0 + h * hstride + c0 + c) = v4;
+            for (int hh = 0; hh < HPL; ++hh) {
+                const int h = g4 * HPL + hh;
+                if (h < G) dst0[h * hstride + D + 1] = l_part[hh];
             }
+        }
+        if (lane < C::CH_LANES) {
+            const int c0 = KF == FMT_F32 ? vcol / 4 : (C::U4 ? vcol * 2 : vcol / 2);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+#pragma unroll
+                for (int c = 0; c < CPL; c += 4) {
+                    f32x4 v4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v4[e] = acc[h][c + e] + (C::U4 ? amin[h] : 0.f);
+                    *(f32x4 *)(dst0 + h * hstride + c0 + c) = v4;
+                }
+            }
+        }
+    };
+    if (fused) emit(mrg_lds + wave * G * PSTR, PSTR);
+    else if (split < a.n_split)
+        emit(a.ws + ((int64_t)unit * G * a.n_split + split) * PSTR, (int64_t)a.n_split * PSTR);
+
+    // ---- in-workgroup merge of the n_split (<= waves) partials -------------
+    // The operations and their order are those of attn_reduce_kernel for
+    // n_split <= 4: max; weights 2^(m_s - M); L = (w0 l0 + w1 l1) + (w2 l2 +
+    // w3 l3) (its shuffle tree; adding to a +0 start is exact, the terms are
+    // >= 0); O = fma chain over s; o = O / L.
+    if (fused) {
+        __syncthreads();
+        const int ns = a.n_split;
+        const int slot = G * PSTR;
+        float *ob = a.o + (int64_t)b * a.o_bstride + (int64_t)hkv * G * D;
+#pragma unroll 1
+        for (int idx = wave * 64 + lane; idx < G * D; idx += a.wpb * 64) {
+            const int h = idx / D, d = idx - h * D;
+            const float *ps = mrg_lds + h * PSTR;
+            float M = neg_inf();
+#pragma unroll 1
+            for (int s = 0; s < ns; ++s) M = fmaxf(M, ps[s * slot + D]);
+            float L01 = 0.f, L23 = 0.f, O0 = 0.f;
+            const float O1 = 0.f, O2 = 0.f, O3 = 0.f;
+#pragma unroll 1
+            for (int s = 0; s < ns; ++s) {
+                const float m = ps[s * slot + D];
+                const float w = (m == neg_inf()) ? 0.f : fast_exp2(m - M);
+                const float pl = fmaf(w, ps[s * slot + D + 1], 0.f);
+                if (s < 2) L01 += pl;
+                else L23 += pl;
+                O0 = fmaf(w, ps[s * slot + d], O0);
+            }
+            const float L = L01 + L23;
+            ob[h * D + d] = ((O0 + O1) + (O2 + O3)) / L;
         }
     }
 }
@@ -595,66 +665,72 @@ __global__ __launch_bounds__(128) void attn_reduce_kernel(const float *__restric
 
 using SplitFn = void (*)(AttnLaunch);
 
+struct SplitKernel {
+    SplitFn fn = nullptr;
+    explicit operator bool() const { return fn != nullptr; }
+};
+
 template <int KF, int QF, int D, int G, bool PAGED>
-SplitFn pick_one() {
-    if constexpr (Cfg<KF, QF, D, G>::ok) return attn_split_kernel<KF, QF, D, G, PAGED>;
-    else return nullptr;
+SplitKernel pick_one() {
+    using C = Cfg<KF, QF, D, G>;
+    if constexpr (C::ok) return {attn_split_kernel<KF, QF, D, G, PAGED>};
+    else return {};
 }
 
 template <int KF, int QF, int D, bool PAGED>
-SplitFn pick_g(int G) {
-    if constexpr (PAGED) return G == 1 ? pick_one<KF, QF, D, 1, PAGED>() : nullptr;
+SplitKernel pick_g(int G) {
+    if constexpr (PAGED) return G == 1 ? pick_one<KF, QF, D, 1, PAGED>() : SplitKernel{};
     switch (G) {
     case 1: return pick_one<KF, QF, D, 1, PAGED>();
     case 2: return pick_one<KF, QF, D, 2, PAGED>();
     case 4: return pick_one<KF, QF, D, 4, PAGED>();
     case 8: return pick_one<KF, QF, D, 8, PAGED>();
-    default: return nullptr;
+    default: return {};
     }
 }
 
 template <int KF, int QF, bool PAGED>
-SplitFn pick_d(int D, int G) {
+SplitKernel pick_d(int D, int G) {
     if constexpr (KF == FMT_U4) {
-        return D == 128 ? pick_g<KF, QF, 128, PAGED>(G) : nullptr;
+        return D == 128 ? pick_g<KF, QF, 128, PAGED>(G) : SplitKernel{};
     } else {
         if (D == 64) return pick_g<KF, QF, 64, PAGED>(G);
         if (D == 128) return pick_g<KF, QF, 128, PAGED>(G);
-        return nullptr;
+        return {};
     }
 }
 
-SplitFn pick(int kv, int qf, int D, int G, bool paged) {
+SplitKernel pick(int kv, int qf, int D, int G, bool paged) {
     if (paged) {
-        if (G != 1) return nullptr;
+        if (G != 1) return {};
         switch (kv) {
-        case FMT_F32: return qf == FMT_F32 ? pick_d<FMT_F32, FMT_F32, true>(D, G) : nullptr;
+        case FMT_F32: return qf == FMT_F32 ? pick_d<FMT_F32, FMT_F32, true>(D, G) : SplitKernel{};
         case FMT_F16:
             if (qf == FMT_F16) return pick_d<FMT_F16, FMT_F16, true>(D, G);
             if (qf == FMT_F32) return pick_d<FMT_F16, FMT_F32, true>(D, G);
-            return nullptr;
+            return {};
         case FMT_BF16:
             if (qf == FMT_BF16) return pick_d<FMT_BF16, FMT_BF16, true>(D, G);
             if (qf == FMT_F32) return pick_d<FMT_BF16, FMT_F32, true>(D, G);
-            return nullptr;
-        default: return nullptr;
+            return {};
+        default: return {};
         }
     }
     switch (kv) {
-    case FMT_F32: return qf == FMT_F32 ? pick_d<FMT_F32, FMT_F32, false>(D, G) : nullptr;
+    case FMT_F32: return qf == FMT_F32 ? pick_d<FMT_F32, FMT_F32, false>(D, G) : SplitKernel{};
     case FMT_F16:
         if (qf == FMT_F16) return pick_d<FMT_F16, FMT_F16, false>(D, G);
         if (qf == FMT_F32) return pick_d<FMT_F16, FMT_F32, false>(D, G);
-        return nullptr;
+        return {};
     case FMT_BF16:
         if (qf == FMT_BF16) return pick_d<FMT_BF16, FMT_BF16, false>(D, G);
         if (qf == FMT_F32) return pick_d<FMT_BF16, FMT_F32, false>(D, G);
-        return nullptr;
+        return {};
     case FMT_U4:
         if (qf == FMT_F16) return pick_d<FMT_U4, FMT_F16, false>(D, G);
         if (qf == FMT_F32) return pick_d<FMT_U4, FMT_F32, false>(D, G);
-        return nullptr;
-    default: return nullptr;
+        return {};
+    default: return {};
     }
 }
 
@@ -683,14 +759,18 @@ size_t attn_ws_bytes(int64_t rows, int32_t n_split, int32_t D) {
 }
 
 bool attn_supported(int kv_fmt, int q_fmt, int D, int G, bool paged) {
-    return pick(kv_fmt, q_fmt, D, G, paged) != nullptr;
+    return static_cast<bool>(pick(kv_fmt, q_fmt, D, G, paged));
 }
 
 hipError_t launch_split(const AttnLaunch &a, hipStream_t stream) {
-    SplitFn fn = pick(a.kv_fmt, a.q_fmt, a.D, a.G, a.page_idx != nullptr);
-    if (!fn) return hipErrorInvalidValue;
-    dim3 grid(a.n_split, a.B * a.Hkv);
-    hipLaunchKernelGGL(fn, grid, dim3(64), 0, stream, a);
+    const bool paged = a.page_idx != nullptr;
+    const SplitKernel k = pick(a.kv_fmt, a.q_fmt, a.D, a.G, paged);
+    if (!k) return hipErrorInvalidValue;
+    if (a.wpb < 1 || a.wpb > kMaxWavesPerBlock || a.n_split < 1) return hipErrorInvalidValue;
+    if (a.fused && a.n_split > a.wpb) return hipErrorInvalidValue;
+    const size_t lds = a.fused ? merge_lds_bytes(a.wpb, a.G, a.D) : 0;
+    dim3 grid((a.n_split + a.wpb - 1) / a.wpb, a.B * a.Hkv);
+    hipLaunchKernelGGL(k.fn, grid, dim3(64 * a.wpb), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -703,9 +783,26 @@ hipError_t launch_merge(int64_t rows, int32_t heads_per_row, int32_t n_split, in
     return hipGetLastError();
 }
 
+// When to merge in the workgroup (measured on MI355X).  A single split
+// always does (nothing to wait for).  Several splits do when there are at
+// least as many (b, h) units as compute units (fewer would leave CUs idle)
+// and the whole grid is at most 4 waves per SIMD: with more waves queued the
+// separate merge costs little and 1-wave workgroups schedule more freely.
+constexpr int64_t kFuseMinUnits = 256;
+constexpr int64_t kFuseMaxWaves = 4096;
+
 hipError_t launch_attention(const AttnLaunch &a, hipStream_t stream) {
-    hipError_t e = launch_split(a, stream);
-    if (e != hipSuccess) return e;
+    AttnLaunch f = a;
+    f.wpb = 1;
+    f.fused = 0;
+    const int64_t units = (int64_t)a.B * a.Hkv;
+    if (a.n_split == 1 || (a.n_split <= kMaxWavesPerBlock && units >= kFuseMinUnits &&
+                           units * a.n_split <= kFuseMaxWaves)) {
+        f.wpb = a.n_split;
+        f.fused = 1;
+    }
+    hipError_t e = launch_split(f, stream);
+    if (e != hipSuccess || f.fused) return e;
     return launch_merge((int64_t)a.B * a.Hkv * a.G, a.Hkv * a.G, a.n_split, a.D, a.ws, a.o, a.o_bstride, stream);
 }
 

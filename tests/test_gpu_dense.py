@@ -108,3 +108,84 @@ def test_workload2_full_size_sampled(da):
         v = as_f64(c.v[b:b + 1, h:h + 1], "bf16")
         ref = decode_attention(q, k, v, c.scale)[0, 0]
         assert_close(got[b, j], ref, atol=1e-3, rel_rms=1e-4, what=f"w2 b{b} j{j}")
+
+
+def _upload(c):
+    q = to_dev(c.q, c.q_dtype)
+    k = to_dev(c.k, c.kv_dtype)
+    v = to_dev(c.v, c.kv_dtype)
+    return q, k, v
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,N,qd,kd,st", [
+    (2, 8, 2, 128, 1000, "f32", "bf16", 256),   # 4 splits, ragged last
+    (1, 4, 4, 64, 300, "f16", "f16", 64),       # MHA fp16, 5 splits
+    (1, 16, 2, 64, 77, "f32", "f32", 32),       # fp32 cache, G = 8
+])
+def test_partials_match_oracle(da, B, Hq, Hkv, D, N, qd, kd, st):
+    """The split-K pass on its own: every split's (u, m, l) against the
+    oracle's partials (the kernel keeps m in base 2)."""
+    import torch
+    from oracle import split_partials
+    c = synth.dense_case([105, B, Hq, Hkv, D, N], B, Hq, Hkv, D, N, qd, kd)
+    q, k, v = _upload(c)
+    ws = da.da_decode_attention_partials(q, k, v, scale=c.scale, split_tokens=st)
+    torch.cuda.synchronize()
+    ws = ws.cpu().numpy().astype(np.float64)
+    u, m, l = split_partials(as_f64(c.q, qd), as_f64(c.k, kd), as_f64(c.v, kd), c.scale, st)
+    assert ws.shape == (B, Hq, u.shape[2], D + 4)
+    m_got = ws[..., D] * np.log(2.0)
+    np.testing.assert_allclose(m_got, m, rtol=0, atol=2e-6 * max(1.0, np.abs(m).max()))
+    np.testing.assert_allclose(ws[..., D + 1], l, rtol=2e-6, atol=0)
+    assert_close(ws[..., :D], u, atol=2e-6 * np.abs(u).max(), what=f"partials u split {st}")
+
+
+@pytest.mark.parametrize("ns,D", [(1, 64), (3, 128), (20, 64), (100, 128)])
+def test_merge_matches_oracle(da, ns, D):
+    """The cross-split merge on its own, on seeded partials with empty splits
+    (m = -inf) and a wide spread of maxima."""
+    import torch
+    from oracle import merge_partials
+    rng = np.random.default_rng([106, ns, D])
+    rows = 37
+    m2 = rng.uniform(-20.0, 20.0, (rows, ns))
+    l = rng.uniform(1.0, 50.0, (rows, ns))
+    u = rng.standard_normal((rows, ns, D)) * l[..., None]
+    if ns > 1:
+        empty = rng.random((rows, ns)) < 0.2
+        empty[:, 0] = False
+        m2[empty] = -np.inf
+        l[empty] = 0.0
+        u[empty] = 0.0
+    part = np.zeros((rows, ns, D + 4), dtype=np.float32)
+    part[..., :D] = u
+    part[..., D] = m2
+    part[..., D + 1] = l
+    got = da.da_merge_partials(torch.from_numpy(part).cuda())
+    torch.cuda.synchronize()
+    p64 = part.astype(np.float64)
+    ref = merge_partials(p64[..., :D], p64[..., D] * np.log(2.0), p64[..., D + 1])
+    assert_close(got.cpu().numpy(), ref, atol=2e-6 * np.abs(ref).max(), what=f"merge ns{ns} D{D}")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,N,qd,kd", [
+    (64, 8, 4, 64, 1000, "f32", "bf16"),    # 256 units x 4 splits: one 4-wave workgroup each
+    (128, 4, 2, 128, 600, "f32", "bf16"),   # 3 splits
+    (1, 4, 1, 64, 200, "f32", "f32"),       # a single split
+    (32, 16, 8, 128, 700, "f16", "f16"),    # 3 splits, G = 2
+])
+def test_in_workgroup_merge_equals_merge_kernel_bitwise(da, B, Hq, Hkv, D, N, qd, kd):
+    """When a (b, h) has at most four splits they run as the waves of one
+    workgroup and merge in LDS; the result must carry the same bits as the
+    partial pass followed by the merge kernel, and match the oracle."""
+    import torch
+    c = synth.dense_case([107, B, Hq, Hkv, D, N], B, Hq, Hkv, D, N, qd, kd)
+    q, k, v = _upload(c)
+    assert da.da_decode_attention_n_split(B, Hq, Hkv, D, N) <= 4
+    fused = da.da_decode_attention(q, k, v, scale=c.scale)
+    two = da.da_merge_partials(da.da_decode_attention_partials(q, k, v, scale=c.scale))
+    torch.cuda.synchronize()
+    a = fused.cpu().numpy()
+    b = two.cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert_close(a, oracle_of(c), atol=1e-5, rel_rms=1e-4, what=f"fused B{B} N{N}")

@@ -48,6 +48,8 @@ SEL_CASES = [
     (1, 2, 64, 333, 1, 40, "f16"),         # one-token pages: bound = q.k
     (2, 2, 128, 2048, 64, 3, "bf16"),
     (1, 2, 64, 640, 16, 40, "f32"),        # top_k = P: every page
+    (32, 8, 64, 1024, 16, 24, "f16"),      # 256 heads, one split each
+    (16, 16, 64, 4096, 16, 100, "f16"),    # 256 heads x 4 splits merged in the workgroup
 ]
 
 
