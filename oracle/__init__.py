@@ -17,7 +17,8 @@ Sources (the pages these functions follow):
   standard decode equation, page partition, TopK, SparseAttn and the
   directional bounding-box score in section "方法细节" and Algorithm 1.
 * FlexGen (kwkr.cn digest, section "方法细节"): 4-bit min/max quantization in
-  groups of 64 along the hidden dimension, dequantized to FP16 before compute.
+  groups of 64 along the hidden dimension, dequantized to FP16 before compute;
+  sparse attention over the top 10% of the K cache per query.
 
 Modules:
 
@@ -25,6 +26,7 @@ Modules:
   partials and their merge, head-wise driver.
 * :mod:`oracle.paged` -- page metadata, bound score, top-K, sparse attention.
 * :mod:`oracle.kv4` -- uint4 group quantization, dequantization, attention.
+* :mod:`oracle.tokens` -- token-level top-k sparse attention (FlexGen).
 
 Pinning status: every function is pinned by tests against closed forms,
 invariants, brute force on tiny inputs or an independent library routine (see
@@ -36,3 +38,5 @@ from .attention import (decode_attention, headwise_attention,  # noqa: F401
 from .paged import (page_meta, bound_scores, topk_pages,  # noqa: F401
                     sparse_attention)
 from .kv4 import quantize_kv4, dequantize_kv4, kv4_attention  # noqa: F401
+from .tokens import (keep_count, token_scores, topk_tokens,  # noqa: F401
+                     topk_token_attention)
