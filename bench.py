@@ -404,6 +404,74 @@ def cpu_kv4(host, bytes_per_row):
 
 
 # ---------------------------------------------------------------------------
+# extra: token-level top-10% sparse attention (FlexGen shape)
+# ---------------------------------------------------------------------------
+def bench_topk(args, torch, np, da, synth):
+    log("extra: token top-10% sparse decode, B64 H56 D128 N1024 fp16")
+    t0 = time.time()
+    c = synth.workload4()
+    log(f"generated inputs in {time.time() - t0:.1f}s")
+    B, H, _, D, N = c.shape
+    K = da.keep_count(N)
+    q = up(c.q, "f16", torch, np)
+    k0 = up(c.k, "f16", torch, np)
+    v0 = up(c.v, "f16", torch, np)
+    host = None if args.no_cpu else (c.q[0:1].copy(), c.k[0:1].copy(), c.v[0:1].copy())
+    del c
+    copies = [(k0, v0), (k0.clone(), v0.clone())]
+    idx = torch.empty((B, H, K), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(1 << 26, dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        kk, vv = copies[i & 1]
+        da.da_select_tokens(q, kk, K, token_idx=idx)
+        da.da_decode_attention_paged(q, kk, vv, idx, 1, out=out, ws=ws)
+
+    ms_eager = time_events(torch, step, args.steps, args.warmup)
+    ms = ms_eager if args.no_graph else time_graph(torch, step, args.steps, args.warmup)
+    ms_sel = time_each(torch, lambda i: da.da_select_tokens(q, copies[i & 1][0], K, token_idx=idx),
+                       args.steps)
+    ms_att = time_each(torch, lambda i: da.da_decode_attention_paged(q, *copies[i & 1], idx, 1, out=out,
+                                                                     ws=ws), args.steps)
+    wsd = torch.zeros(1 << 26, dtype=torch.uint8, device="cuda")
+    ms_dense = time_events(torch, lambda i: da.da_decode_attention(q, *copies[i & 1], out=out, ws=wsd),
+                           max(5, args.steps // 4), 2)
+    k_bytes = B * H * N * D * 2
+    kept_bytes = 2 * B * H * K * D * 2
+    step_bytes = k_bytes + kept_bytes + 2 * B * H * D * 2 + B * H * D * 4 + 2 * B * H * K * 4
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    res = {"workload": f"flexgen-topk B{B} H{H} D{D} N{N} fp16 keep {K} tokens (10%)",
+           "ms_per_step": ms, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "step_bytes": step_bytes,
+           "tokens_per_s": B / (ms * 1e-3), "select_ms": ms_sel,
+           "select_gbs": (k_bytes + B * H * D * 2) / (ms_sel * 1e-3) / 1e9,
+           "attention_ms": ms_att, "dense_same_cache_ms": ms_dense, "speedup_vs_dense": ms_dense / ms,
+           "eager_ms_per_step": ms_eager}
+    log(f"topk: {ms * 1e3:.1f} us/step ({gbs:.0f} GB/s), select {ms_sel * 1e3:.1f} us, attention "
+        f"{ms_att * 1e3:.1f} us, dense on same cache {ms_dense * 1e3:.1f} us")
+    if host is not None:
+        res["cpu_baseline"] = cpu_topk(host, K, step_bytes / B)
+    return res
+
+
+def cpu_topk(host, K, bytes_per_row):
+    """Oracle token top-k attention on batch row 0 (all 56 heads)."""
+    import numpy as np
+    from oracle import topk_token_attention
+    from oracle.numerics import as_f64
+    q, k, v = host
+
+    def once():
+        topk_token_attention(as_f64(q, "f16"), as_f64(k, "f16"), as_f64(v, "f16"), K,
+                             1.0 / np.sqrt(q.shape[-1]))
+
+    sec, n, _ = time_oracle(once, 3.0)
+    return {"value": bytes_per_row / sec / 1e9, "unit": "GB/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"batch row 0 of 64 (56 heads x 1024 tokens): scores, top-{K} and attention over "
+                      f"them, median of {n} runs after 1 warm-up, {sec:.2f} s per run"}
+
+
+# ---------------------------------------------------------------------------
 # extra: head-wise streamed (HeadInfer shape)
 # ---------------------------------------------------------------------------
 def bench_stream(args, torch, np, da, synth):
@@ -525,7 +593,7 @@ def main(argv=None) -> int:
     ap.add_argument("--stream-pool-heads", type=int, default=16)
     ap.add_argument("--stream-steps", type=int, default=2)
     ap.add_argument("--only", default="",
-                    help="comma list of dense,sparse,kv4,stream (profiling runs; no JSON line "
+                    help="comma list of dense,sparse,kv4,topk,stream (profiling runs; no JSON line "
                          "unless dense is included)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run three 512 MiB device-to-device copies (a kernel of known "
@@ -559,8 +627,8 @@ def main(argv=None) -> int:
         del src, dst
 
     if only and "dense" not in only:
-        runners = {"sparse": bench_sparse, "kv4": bench_kv4, "stream": bench_stream}
-        for name in ("sparse", "kv4", "stream"):
+        runners = {"sparse": bench_sparse, "kv4": bench_kv4, "topk": bench_topk, "stream": bench_stream}
+        for name in ("sparse", "kv4", "topk", "stream"):
             if name in only:
                 torch.cuda.empty_cache()
                 print(json.dumps({name: runners[name](args, torch, np, da, synth)}), flush=True)
@@ -576,7 +644,8 @@ def main(argv=None) -> int:
     extra = {}
     if only:
         args.no_extra = True
-        for key, name, fn in (("sparse", "page_sparse", bench_sparse), ("kv4", "uint4", bench_kv4)):
+        for key, name, fn in (("sparse", "page_sparse", bench_sparse), ("kv4", "uint4", bench_kv4),
+                              ("topk", "token_topk", bench_topk)):
             if key in only:
                 torch.cuda.empty_cache()
                 extra[name] = fn(args, torch, np, da, synth)
@@ -584,7 +653,7 @@ def main(argv=None) -> int:
             torch.cuda.empty_cache()
             extra["headwise_stream"] = bench_stream(args, torch, np, da, synth)
     if not args.no_extra:
-        for name, fn in (("page_sparse", bench_sparse), ("uint4", bench_kv4)):
+        for name, fn in (("page_sparse", bench_sparse), ("uint4", bench_kv4), ("token_topk", bench_topk)):
             torch.cuda.empty_cache()
             extra[name] = fn(args, torch, np, da, synth)
         if not args.no_stream:

@@ -18,6 +18,10 @@
  *     da_decode_attention_paged  directional bound score, top-K pages, and
  *                                attention over the kept pages only
  *                                (TinyServe, section "方法细节", Algorithm 1).
+ *   - da_select_tokens +         FlexGen's token-level sparse attention: the
+ *     da_decode_attention_paged  top 10% of tokens by exact score q . k, then
+ *     (page_size 1)              attention over them only (FlexGen digest,
+ *                                section "方法细节").
  *   - da_quantize_kv4,           FlexGen's 4-bit min/max quantization in
  *     da_dequantize_kv4,         groups of 64 channels, and attention that
  *     da_decode_attention_kv4    dequantizes while loading (FlexGen digest,
@@ -182,6 +186,25 @@ da_status da_select_pages(const da_attn_shape *s, int32_t page_size,
                           int32_t top_k, const void *q, const void *kmin,
                           const void *kmax, int32_t *page_idx,
                           float *page_score, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Token selection by exact score (FlexGen's top-10% sparse attention keeps,
+ * per query, the indices of its best-scoring keys):
+ *   s_i = q . k_i accumulated in fp32 (products of fp16/bf16 values exact),
+ * then the top_k largest s_i per (batch row, head); equal scores keep the
+ * lower token index; the kept indices are written in ascending order.  Reads
+ * each key row once.  Attention over the kept tokens is
+ * da_decode_attention_paged with page_size 1 and page_idx = token_idx.
+ *   q           [batch][n_q_heads][head_dim]          q_dtype, device
+ *   k           [batch][n_kv_heads][n_ctx][head_dim]  kv_dtype, device
+ *   token_idx   [batch][n_q_heads][top_k] int32, device (written)
+ *   token_score [batch][n_q_heads][n_ctx] fp32, device, or NULL (written if
+ *               given; unscaled q . k)
+ * Requires n_q_heads == n_kv_heads, 1 <= top_k <= n_ctx <= 8192.
+ * ------------------------------------------------------------------------ */
+da_status da_select_tokens(const da_attn_shape *s, int32_t top_k,
+                           const void *q, const void *k, int32_t *token_idx,
+                           float *token_score, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Sparse attention over the selected pages only (TinyServe SparseAttn):

@@ -184,6 +184,39 @@ def da_select_pages(q, kmin, kmax, page_size, top_k, n_ctx, page_idx=None, page_
     return (page_idx, page_score) if want_scores else page_idx
 
 
+def da_select_tokens(q, k, top_k, token_idx=None, token_score=None, want_scores=False, stream=None):
+    """Top-k tokens by exact score q . k per (b, h), ascending int32 [B][H][top_k]."""
+    lib = load()
+    _dev(q, k, token_idx, token_score)
+    B, H, D = q.shape
+    N = k.shape[2]
+    _expect(k, (B, H, N, D), k.dtype, "k")
+    _expect(token_idx, (B, H, top_k), torch.int32, "token_idx")
+    _expect(token_score, (B, H, N), torch.float32, "token_score")
+    s = attn_shape(B, H, H, D, N, None, _DT[q.dtype], _DT[k.dtype])
+    if token_idx is None:
+        token_idx = torch.empty((B, H, top_k), dtype=torch.int32, device=q.device)
+    if want_scores and token_score is None:
+        token_score = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    check(lib.da_select_tokens(ctypes.byref(s), top_k, _vp(q), _vp(k), _vp(token_idx),
+                               _vp(token_score), _stream(stream)))
+    return (token_idx, token_score) if want_scores else token_idx
+
+
+def keep_count(n_ctx, keep=0.1):
+    """Tokens kept per query by the top-k sparse attention: ceil(keep * n_ctx),
+    at least 1."""
+    return min(n_ctx, max(1, math.ceil(keep * n_ctx - 1e-9)))
+
+
+def da_decode_attention_topk(q, k, v, top_k, scale=None, token_idx=None, out=None, ws=None,
+                             stream=None):
+    """FlexGen's token-level sparse attention: select the top_k tokens by
+    exact score, then attend over them only (two kernels + merge)."""
+    idx = da_select_tokens(q, k, top_k, token_idx=token_idx, stream=stream)
+    return da_decode_attention_paged(q, k, v, idx, 1, scale=scale, out=out, ws=ws, stream=stream)
+
+
 def da_decode_attention_paged(q, k, v, page_idx, page_size, scale=None, split_tokens=0, out=None,
                               ws=None, stream=None):
     """Attention over the tokens of the listed pages only; fp32 [B][H][D]."""

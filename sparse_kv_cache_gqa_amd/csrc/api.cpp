@@ -248,6 +248,27 @@ da_status da_select_pages(const da_attn_shape *s, int32_t page_size, int32_t top
     return ok();
 }
 
+da_status da_select_tokens(const da_attn_shape *s, int32_t top_k, const void *q, const void *k, int32_t *token_idx,
+                           float *token_score, hipStream_t stream) {
+    DA_TRY(check_shape(s, false));
+    if (s->n_q_heads != s->n_kv_heads)
+        return fail(DA_E_UNSUPPORTED, "token selection needs n_q_heads == n_kv_heads");
+    if (top_k < 1 || top_k > s->n_ctx)
+        return fail(DA_E_INVALID, "top_k %d not in [1, %lld]", top_k, (long long)s->n_ctx);
+    if (s->n_ctx > 8192) return fail(DA_E_UNSUPPORTED, "%lld tokens > 8192 per head", (long long)s->n_ctx);
+    if (s->batch == 0) return ok();
+    DA_TRY(check_ptr(q, "q"));
+    DA_TRY(check_ptr(k, "k"));
+    DA_TRY(check_ptr(token_idx, "token_idx"));
+    if (token_score && !aligned16(token_score)) return fail(DA_E_INVALID, "token_score is not 16-byte aligned");
+    if (!select_supported(s->kv_dtype, s->q_dtype, s->head_dim))
+        return fail(DA_E_UNSUPPORTED, "no selection kernel for this dtype / head_dim");
+    hipError_t e = launch_select(s->kv_dtype, s->q_dtype, (int64_t)s->batch * s->n_q_heads, s->n_ctx, s->head_dim,
+                                 top_k, q, k, k, token_idx, token_score, stream, true);
+    if (e != hipSuccess) return hip_fail(e, "token selection launch");
+    return ok();
+}
+
 size_t da_decode_attention_paged_workspace(const da_attn_shape *s, int32_t page_size, int32_t top_k) {
     if (check_shape(s, false) != DA_OK || check_page(page_size) != DA_OK) return 0;
     if (top_k < 1 || top_k > n_pages(s, page_size)) return 0;

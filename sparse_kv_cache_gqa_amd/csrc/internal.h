@@ -84,12 +84,13 @@ hipError_t launch_page_meta(int kv_fmt, int64_t BH, int64_t N, int D,
                             int log2_page, const void *k, void *kmin, void *kmax,
                             hipStream_t stream);
 
-// Bound score + top-K per (b, h).
+// Bound score + top-K per (b, h).  With `exact`, kmax holds the key rows
+// themselves (P = N tokens, kmin unused) and the score is q . k.
 bool select_supported(int kv_fmt, int q_fmt, int D);
 hipError_t launch_select(int kv_fmt, int q_fmt, int64_t BH, int64_t P, int D,
                          int top_k, const void *q, const void *kmin,
                          const void *kmax, int32_t *page_idx, float *page_score,
-                         hipStream_t stream);
+                         hipStream_t stream, bool exact = false);
 
 // uint4 group quantization.
 hipError_t launch_quantize_kv4(int64_t n_groups, const void *x, uint8_t *codes,

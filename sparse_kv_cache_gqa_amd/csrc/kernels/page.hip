@@ -13,6 +13,9 @@
 //      from HBM into the B operand.  Products of 16-bit values are exact in
 //      fp32; q in fp32 is split into 16-bit terms on the A rows.  Scores stay
 //      in LDS (and optionally go to page_score).
+//      With EXACT the key rows themselves are read once and scored against q
+//      (q . k_i, one MFMA per 32 channels): token-level selection (FlexGen's
+//      top-10% sparse attention, section "方法细节").
 //   2. Top-K by a most-significant-digit radix select (4 passes of 8 bits)
 //      over an order-preserving uint32 image of the fp32 scores, one shared
 //      LDS histogram per pass.  Ties at the K-th score go to the lower page
@@ -147,7 +150,7 @@ __device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t *buf, uint
     return before;
 }
 
-template <int KF, int QF, int D>
+template <int KF, int QF, int D, bool EXACT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(int64_t P, int top_k, const void *__restrict__ q,
                                                              const uint8_t *__restrict__ kmin,
                                                              const uint8_t *__restrict__ kmax,
@@ -167,7 +170,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int64_t P, int top_
     const int g4 = lane >> 4, n16 = lane & 15;
     const int64_t bh = blockIdx.x;
 
-    // A operands: row s holds the s-th split term of q+ (pos) or q- (neg)
+    // A operands: row s holds the s-th split term of q+ (pos) or q- (neg);
+    // EXACT: of q itself (pos only)
     u32x4 Apos[KF == FMT_F32 ? 1 : NMF], Aneg[KF == FMT_F32 ? 1 : NMF];
     float Fpos[KF == FMT_F32 ? NMF : 1], Fneg[KF == FMT_F32 ? NMF : 1];
     {
@@ -178,14 +182,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int64_t P, int top_
         for (int mf = 0; mf < NMF; ++mf) {
             if constexpr (KF == FMT_F32) {
                 const float x = rowok ? load_scalar<QF>(q, qoff + qk_dim<KF>(mf, g4, 0)) : 0.f;
-                Fpos[mf] = fmaxf(x, 0.f);
+                Fpos[mf] = EXACT ? x : fmaxf(x, 0.f);
                 Fneg[mf] = fminf(x, 0.f);
             } else {
                 uint32_t hp[8], hn[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float x = rowok ? load_scalar<QF>(q, qoff + qk_dim<KF>(mf, g4, e)) : 0.f;
-                    hp[e] = rowok ? split_term<KF>(fmaxf(x, 0.f), s) : 0u;
+                    hp[e] = rowok ? split_term<KF>(EXACT ? x : fmaxf(x, 0.f), s) : 0u;
                     hn[e] = rowok ? split_term<KF>(fminf(x, 0.f), s) : 0u;
                 }
 #pragma unroll
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int64_t P, int top_
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             Kx[c] = ok ? *(const u32x4 *)(mxb + pg * R + 64 * c) : (u32x4){0u, 0u, 0u, 0u};
-            Kn[c] = ok ? *(const u32x4 *)(mnb + pg * R + 64 * c) : (u32x4){0u, 0u, 0u, 0u};
+            if constexpr (!EXACT) Kn[c] = ok ? *(const u32x4 *)(mnb + pg * R + 64 * c) : (u32x4){0u, 0u, 0u, 0u};
         }
         f32x4 cc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -216,18 +220,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int64_t P, int top_
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     cc = __builtin_amdgcn_mfma_f32_16x16x4f32(Fpos[4 * c + e], __uint_as_float(Kx[c][e]), cc, 0, 0, 0);
-                    cc = __builtin_amdgcn_mfma_f32_16x16x4f32(Fneg[4 * c + e], __uint_as_float(Kn[c][e]), cc, 0, 0, 0);
+                    if constexpr (!EXACT)
+                        cc = __builtin_amdgcn_mfma_f32_16x16x4f32(Fneg[4 * c + e], __uint_as_float(Kn[c][e]), cc, 0, 0, 0);
                 }
             } else if constexpr (KF == FMT_BF16) {
                 cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Apos[c]),
                                                              __builtin_bit_cast(bf16x8, Kx[c]), cc, 0, 0, 0);
-                cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Aneg[c]),
-                                                             __builtin_bit_cast(bf16x8, Kn[c]), cc, 0, 0, 0);
+                if constexpr (!EXACT)
+                    cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Aneg[c]),
+                                                                 __builtin_bit_cast(bf16x8, Kn[c]), cc, 0, 0, 0);
             } else {
                 cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, Apos[c]),
                                                             __builtin_bit_cast(f16x8, Kx[c]), cc, 0, 0, 0);
-                cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, Aneg[c]),
-                                                            __builtin_bit_cast(f16x8, Kn[c]), cc, 0, 0, 0);
+                if constexpr (!EXACT)
+                    cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, Aneg[c]),
+                                                                __builtin_bit_cast(f16x8, Kn[c]), cc, 0, 0, 0);
             }
         }
         if (g4 == 0 && ok) {
@@ -325,23 +332,24 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int64_t P, int top_
 
 using SelFn = void (*)(int64_t, int, const void *, const uint8_t *, const uint8_t *, int32_t *, float *);
 
-template <int KF, int QF>
+template <int KF, int QF, bool EXACT>
 SelFn sel_d(int D) {
-    if (D == 64) return select_kernel<KF, QF, 64>;
-    if (D == 128) return select_kernel<KF, QF, 128>;
+    if (D == 64) return select_kernel<KF, QF, 64, EXACT>;
+    if (D == 128) return select_kernel<KF, QF, 128, EXACT>;
     return nullptr;
 }
 
+template <bool EXACT>
 SelFn sel_pick(int kv, int qf, int D) {
     switch (kv) {
-    case FMT_F32: return qf == FMT_F32 ? sel_d<FMT_F32, FMT_F32>(D) : nullptr;
+    case FMT_F32: return qf == FMT_F32 ? sel_d<FMT_F32, FMT_F32, EXACT>(D) : nullptr;
     case FMT_F16:
-        if (qf == FMT_F16) return sel_d<FMT_F16, FMT_F16>(D);
-        if (qf == FMT_F32) return sel_d<FMT_F16, FMT_F32>(D);
+        if (qf == FMT_F16) return sel_d<FMT_F16, FMT_F16, EXACT>(D);
+        if (qf == FMT_F32) return sel_d<FMT_F16, FMT_F32, EXACT>(D);
         return nullptr;
     case FMT_BF16:
-        if (qf == FMT_BF16) return sel_d<FMT_BF16, FMT_BF16>(D);
-        if (qf == FMT_F32) return sel_d<FMT_BF16, FMT_F32>(D);
+        if (qf == FMT_BF16) return sel_d<FMT_BF16, FMT_BF16, EXACT>(D);
+        if (qf == FMT_F32) return sel_d<FMT_BF16, FMT_F32, EXACT>(D);
         return nullptr;
     default: return nullptr;
     }
@@ -368,12 +376,12 @@ hipError_t launch_page_meta(int kv_fmt, int64_t BH, int64_t N, int D, int log2_p
     return hipGetLastError();
 }
 
-bool select_supported(int kv_fmt, int q_fmt, int D) { return sel_pick(kv_fmt, q_fmt, D) != nullptr; }
+bool select_supported(int kv_fmt, int q_fmt, int D) { return sel_pick<false>(kv_fmt, q_fmt, D) != nullptr; }
 
 hipError_t launch_select(int kv_fmt, int q_fmt, int64_t BH, int64_t P, int D, int top_k, const void *q,
                          const void *kmin, const void *kmax, int32_t *page_idx, float *page_score,
-                         hipStream_t stream) {
-    SelFn fn = sel_pick(kv_fmt, q_fmt, D);
+                         hipStream_t stream, bool exact) {
+    SelFn fn = exact ? sel_pick<true>(kv_fmt, q_fmt, D) : sel_pick<false>(kv_fmt, q_fmt, D);
     if (!fn) return hipErrorInvalidValue;
     const size_t lds = (size_t)P * sizeof(float);
     hipLaunchKernelGGL(fn, dim3((unsigned)BH), dim3(kSelThreads), lds, stream, P, top_k, q,

@@ -145,6 +145,19 @@ def test_page_checks(lib):
     assert paged(s, 128, need - 4) == L.DA_E_WORKSPACE
 
 
+def test_token_selection_checks(lib):
+    s = mha(n_ctx=1024)
+    sel = lambda sh, k, score=NULL: lib.da_select_tokens(ctypes.byref(sh), k, FAKE, FAKE, FAKE, score, NULL)
+    assert sel(s, 0) == L.DA_E_INVALID
+    assert sel(s, 1025) == L.DA_E_INVALID
+    assert sel(mha(n_q_heads=32, n_ctx=1024), 100) == L.DA_E_UNSUPPORTED    # GQA
+    assert sel(mha(n_ctx=8193), 100) == L.DA_E_UNSUPPORTED                  # > 8192 tokens
+    assert sel(s, 100, MISALIGNED) == L.DA_E_INVALID
+    assert lib.da_select_tokens(ctypes.byref(s), 100, FAKE, NULL, FAKE, NULL, NULL) == L.DA_E_INVALID
+    assert lib.da_select_tokens(ctypes.byref(mha(batch=0, n_ctx=1024)), 5, NULL, NULL, NULL, NULL,
+                                NULL) == L.DA_OK
+
+
 def test_kv4_checks(lib):
     q = lambda **kw: lib.da_quantize_kv4(kw.get("n", 4), kw.get("r", 128), FAKE, FAKE, FAKE, FAKE,
                                           NULL)

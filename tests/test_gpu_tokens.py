@@ -1,0 +1,91 @@
+"""Token-level top-k sparse attention (FlexGen) on the GPU against the fp64
+oracle: exact-score token selection, then attention over the kept tokens
+(paged attention with one-token pages).
+
+Selected sets must equal the oracle's except tokens whose oracle score lies
+within 1e-5 relative of the oracle's k-th score (fp32 accumulation may order
+near-ties differently); returned scores match q . k to 1e-6 of
+sum |q||k|.  Attention is checked against the oracle evaluated on the GPU's
+own set at |err| <= 1e-5 (small shapes) or 1e-3 (full size) and
+max|err|/rms <= 1e-4."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import keep_count, sparse_attention, token_scores, topk_token_attention, topk_tokens
+from oracle.numerics import as_f64
+from gpu_util import assert_close, check_selection, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run(da, c, top_k):
+    import torch
+    q, k, v = to_dev(c.q, c.q_dtype), to_dev(c.k, c.kv_dtype), to_dev(c.v, c.kv_dtype)
+    idx, score = da.da_select_tokens(q, k, top_k, want_scores=True)
+    o = da.da_decode_attention_paged(q, k, v, idx, 1, scale=c.scale)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), score.cpu().numpy(), o.cpu().numpy()
+
+
+CASES = [
+    # B, H, D, N, q dtype, kv dtype, top_k (0: ceil(10% of N))
+    (2, 3, 64, 1000, "f16", "f16", 0),
+    (1, 4, 128, 1024, "f16", "f16", 0),      # the FlexGen head shape
+    (2, 2, 64, 333, "bf16", "bf16", 0),
+    (1, 2, 128, 257, "f32", "f32", 0),
+    (1, 2, 64, 300, "f32", "bf16", 7),
+    (1, 2, 64, 50, "f16", "f16", 50),       # every token: dense attention
+    (1, 1, 64, 8192, "f16", "f16", 0),      # the longest context one workgroup holds
+]
+
+
+@pytest.mark.parametrize("B,H,D,N,qd,kd,K", CASES)
+def test_select_tokens_and_attention(da, B, H, D, N, qd, kd, K):
+    K = K or keep_count(N)
+    c = synth.dense_case([400, B, H, D, N, K], B, H, H, D, N, qd, kd)
+    idx, score, o = run(da, c, K)
+    q64, k64, v64 = as_f64(c.q, qd), as_f64(c.k, kd), as_f64(c.v, kd)
+    r = token_scores(q64, k64)
+    mag = np.einsum("bhd,bhnd->bhn", np.abs(q64), np.abs(k64))
+    assert np.all(np.abs(score - r) <= 1e-6 * mag + 1e-30), "token scores"
+    n_diff = check_selection(idx, r, K)
+    print(f"[parity] tokens B{B} H{H} D{D} N{N} K{K}: {n_diff} near-tie swaps", flush=True)
+    ref = sparse_attention(q64, k64, v64, idx, 1, c.scale)
+    assert_close(o, ref, atol=1e-5, rel_rms=1e-4, what=f"topk attention {qd}/{kd} N{N} K{K}")
+    if K == N:
+        dense, _ = topk_token_attention(q64, k64, v64, N, c.scale)
+        assert_close(o, dense, atol=1e-5, rel_rms=1e-4, what="  all tokens = dense")
+
+
+def test_exact_ties_keep_lower_index(da):
+    """Integer keys give exactly equal scores; the selection must match the
+    oracle's (lower index first) bit for bit."""
+    import torch
+    rng = np.random.default_rng(401)
+    B, H, D, N, K = 2, 2, 64, 600, 60
+    k = rng.integers(-2, 3, size=(B, H, N, D)).astype(np.float16)
+    q = rng.integers(-1, 2, size=(B, H, D)).astype(np.float16)
+    idx = da.da_select_tokens(to_dev(q, "f16"), to_dev(k, "f16"), K)
+    torch.cuda.synchronize()
+    want = topk_tokens(token_scores(q.astype(np.float64), k.astype(np.float64)), K)
+    assert np.array_equal(idx.cpu().numpy(), want)
+
+
+def test_flexgen_shape_full_size_sampled(da):
+    """OPT-30B attention at 1024 tokens (B64, H56, D128, fp16), 103 tokens kept
+    per query, in the benchmark's launch configuration; sampled heads."""
+    c = synth.workload4()
+    K = keep_count(c.k.shape[2])
+    idx, score, o = run(da, c, K)
+    rng = np.random.default_rng(402)
+    picks = [(0, 0), (63, 55)] + [(int(b), int(h)) for b, h in
+                                  zip(rng.integers(0, 64, 6), rng.integers(0, 56, 6))]
+    for b, h in picks:
+        q64 = as_f64(c.q[b:b + 1, h:h + 1], "f16")
+        k64 = as_f64(c.k[b:b + 1, h:h + 1], "f16")
+        v64 = as_f64(c.v[b:b + 1, h:h + 1], "f16")
+        r = token_scores(q64, k64)
+        check_selection(idx[b:b + 1, h:h + 1], r, K)
+        ref = sparse_attention(q64, k64, v64, idx[b:b + 1, h:h + 1], 1, c.scale)
+        assert_close(o[b, h], ref[0, 0], atol=1e-3, rel_rms=1e-4, what=f"w4 topk b{b} h{h}")
