@@ -425,11 +425,17 @@ def bench_topk(args, torch, np, da, synth):
 
     def step(i):
         kk, vv = copies[i & 1]
+        da.da_decode_attention_topk(q, kk, vv, K, out=out)
+
+    def two_kernels(i):
+        kk, vv = copies[i & 1]
         da.da_select_tokens(q, kk, K, token_idx=idx)
         da.da_decode_attention_paged(q, kk, vv, idx, 1, out=out, ws=ws)
 
     ms_eager = time_events(torch, step, args.steps, args.warmup)
     ms = ms_eager if args.no_graph else time_graph(torch, step, args.steps, args.warmup)
+    ms_fused_kernel = time_each(torch, step, args.steps)
+    ms_two = time_events(torch, two_kernels, args.steps, args.warmup)
     ms_sel = time_each(torch, lambda i: da.da_select_tokens(q, copies[i & 1][0], K, token_idx=idx),
                        args.steps)
     ms_att = time_each(torch, lambda i: da.da_decode_attention_paged(q, *copies[i & 1], idx, 1, out=out,
@@ -437,18 +443,20 @@ def bench_topk(args, torch, np, da, synth):
     wsd = torch.zeros(1 << 26, dtype=torch.uint8, device="cuda")
     ms_dense = time_events(torch, lambda i: da.da_decode_attention(q, *copies[i & 1], out=out, ws=wsd),
                            max(5, args.steps // 4), 2)
+    # one kernel: every key row, the kept value rows, q and o
     k_bytes = B * H * N * D * 2
-    kept_bytes = 2 * B * H * K * D * 2
-    step_bytes = k_bytes + kept_bytes + 2 * B * H * D * 2 + B * H * D * 4 + 2 * B * H * K * 4
+    step_bytes = k_bytes + B * H * K * D * 2 + B * H * D * 2 + B * H * D * 4
     gbs = step_bytes / (ms * 1e-3) / 1e9
     res = {"workload": f"flexgen-topk B{B} H{H} D{D} N{N} fp16 keep {K} tokens (10%)",
            "ms_per_step": ms, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "step_bytes": step_bytes,
-           "tokens_per_s": B / (ms * 1e-3), "select_ms": ms_sel,
-           "select_gbs": (k_bytes + B * H * D * 2) / (ms_sel * 1e-3) / 1e9,
-           "attention_ms": ms_att, "dense_same_cache_ms": ms_dense, "speedup_vs_dense": ms_dense / ms,
-           "eager_ms_per_step": ms_eager}
-    log(f"topk: {ms * 1e3:.1f} us/step ({gbs:.0f} GB/s), select {ms_sel * 1e3:.1f} us, attention "
-        f"{ms_att * 1e3:.1f} us, dense on same cache {ms_dense * 1e3:.1f} us")
+           "tokens_per_s": B / (ms * 1e-3), "kernel": "select_kernel (scores, top-k, attention over kept V)",
+           "avg_launch_ms": ms_fused_kernel, "kernel_gbs": step_bytes / (ms_fused_kernel * 1e-3) / 1e9,
+           "two_kernel_ms_per_step": ms_two, "two_kernel_select_ms": ms_sel,
+           "two_kernel_attention_ms": ms_att,
+           "dense_same_cache_ms": ms_dense, "speedup_vs_dense": ms_dense / ms, "eager_ms_per_step": ms_eager}
+    log(f"topk: {ms * 1e3:.1f} us/step ({gbs:.0f} GB/s) in one kernel; two kernels {ms_two * 1e3:.1f} us "
+        f"(select {ms_sel * 1e3:.1f} + attention {ms_att * 1e3:.1f}); dense on same cache "
+        f"{ms_dense * 1e3:.1f} us")
     if host is not None:
         res["cpu_baseline"] = cpu_topk(host, K, step_bytes / B)
     return res

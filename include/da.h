@@ -18,10 +18,10 @@
  *     da_decode_attention_paged  directional bound score, top-K pages, and
  *                                attention over the kept pages only
  *                                (TinyServe, section "方法细节", Algorithm 1).
- *   - da_select_tokens +         FlexGen's token-level sparse attention: the
- *     da_decode_attention_paged  top 10% of tokens by exact score q . k, then
- *     (page_size 1)              attention over them only (FlexGen digest,
- *                                section "方法细节").
+ *   - da_decode_attention_topk   FlexGen's token-level sparse attention: the
+ *     (or da_select_tokens +     top 10% of tokens by exact score q . k, then
+ *     da_decode_attention_paged  attention over them only (FlexGen digest,
+ *     with page_size 1)          section "方法细节").
  *   - da_quantize_kv4,           FlexGen's 4-bit min/max quantization in
  *     da_dequantize_kv4,         groups of 64 channels, and attention that
  *     da_decode_attention_kv4    dequantizes while loading (FlexGen digest,
@@ -205,6 +205,23 @@ da_status da_select_pages(const da_attn_shape *s, int32_t page_size,
 da_status da_select_tokens(const da_attn_shape *s, int32_t top_k,
                            const void *q, const void *k, int32_t *token_idx,
                            float *token_score, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Token-level top-k sparse attention in one kernel (FlexGen's top-10% sparse
+ * attention): per (batch row, head) the exact scores s_i = q . k_i of all
+ * n_ctx tokens, the top_k of them (as da_select_tokens), then
+ *   o = sum_i softmax(scale * s_i) v_i over the kept tokens only,
+ * reading only the value rows of the kept tokens.  No workspace.
+ *   q, k, v, o  as for da_decode_attention (n_q_heads == n_kv_heads)
+ *   token_idx   [batch][n_q_heads][top_k] int32, device, or NULL (written if
+ *               given: the kept tokens, ascending)
+ * Requires 1 <= top_k <= n_ctx and n_ctx + 2 top_k + 8 head_dim <= 16384
+ * (the scores, the kept list and its weights stay in LDS).
+ * ------------------------------------------------------------------------ */
+da_status da_decode_attention_topk(const da_attn_shape *s, int32_t top_k,
+                                   const void *q, const void *k, const void *v,
+                                   float *o, int32_t *token_idx,
+                                   hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Sparse attention over the selected pages only (TinyServe SparseAttn):

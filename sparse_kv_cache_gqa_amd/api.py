@@ -209,12 +209,25 @@ def keep_count(n_ctx, keep=0.1):
     return min(n_ctx, max(1, math.ceil(keep * n_ctx - 1e-9)))
 
 
-def da_decode_attention_topk(q, k, v, top_k, scale=None, token_idx=None, out=None, ws=None,
+def da_decode_attention_topk(q, k, v, top_k, scale=None, token_idx=None, want_idx=False, out=None,
                              stream=None):
-    """FlexGen's token-level sparse attention: select the top_k tokens by
-    exact score, then attend over them only (two kernels + merge)."""
-    idx = da_select_tokens(q, k, top_k, token_idx=token_idx, stream=stream)
-    return da_decode_attention_paged(q, k, v, idx, 1, scale=scale, out=out, ws=ws, stream=stream)
+    """FlexGen's token-level sparse attention in one kernel: the top_k tokens
+    by exact score, then attention over them only; fp32 [B][H][D]."""
+    lib = load()
+    _dev(q, k, v, token_idx, out)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must have the same shape and dtype")
+    B, H, D = q.shape
+    s = _dense_shape(q, k, scale, 0)
+    _expect(out, q.shape, torch.float32, "out")
+    _expect(token_idx, (B, H, top_k), torch.int32, "token_idx")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if want_idx and token_idx is None:
+        token_idx = torch.empty((B, H, top_k), dtype=torch.int32, device=q.device)
+    check(lib.da_decode_attention_topk(ctypes.byref(s), top_k, _vp(q), _vp(k), _vp(v), _vp(out),
+                                       _vp(token_idx), _stream(stream)))
+    return (out, token_idx) if want_idx else out
 
 
 def da_decode_attention_paged(q, k, v, page_idx, page_size, scale=None, split_tokens=0, out=None,

@@ -269,6 +269,31 @@ da_status da_select_tokens(const da_attn_shape *s, int32_t top_k, const void *q,
     return ok();
 }
 
+da_status da_decode_attention_topk(const da_attn_shape *s, int32_t top_k, const void *q, const void *k, const void *v,
+                                   float *o, int32_t *token_idx, hipStream_t stream) {
+    DA_TRY(check_shape(s, false));
+    if (s->n_q_heads != s->n_kv_heads)
+        return fail(DA_E_UNSUPPORTED, "top-k attention needs n_q_heads == n_kv_heads");
+    if (top_k < 1 || top_k > s->n_ctx)
+        return fail(DA_E_INVALID, "top_k %d not in [1, %lld]", top_k, (long long)s->n_ctx);
+    if (s->n_ctx + 2 * (int64_t)top_k + 8 * (int64_t)s->head_dim > 16384)
+        return fail(DA_E_UNSUPPORTED, "n_ctx + 2 top_k + 8 head_dim = %lld > 16384",
+                    (long long)(s->n_ctx + 2 * (int64_t)top_k + 8 * (int64_t)s->head_dim));
+    if (s->batch == 0) return ok();
+    DA_TRY(check_ptr(q, "q"));
+    DA_TRY(check_ptr(k, "k"));
+    DA_TRY(check_ptr(v, "v"));
+    DA_TRY(check_ptr(o, "o"));
+    if (token_idx && !aligned16(token_idx)) return fail(DA_E_INVALID, "token_idx is not 16-byte aligned");
+    if (!select_supported(s->kv_dtype, s->q_dtype, s->head_dim))
+        return fail(DA_E_UNSUPPORTED, "no selection kernel for this dtype / head_dim");
+    hipError_t e = launch_topk_attention(s->kv_dtype, s->q_dtype, (int64_t)s->batch * s->n_q_heads, s->n_ctx,
+                                         s->head_dim, top_k, s->scale * 1.4426950408889634f, q, k, v, o,
+                                         token_idx, stream);
+    if (e != hipSuccess) return hip_fail(e, "top-k attention launch");
+    return ok();
+}
+
 size_t da_decode_attention_paged_workspace(const da_attn_shape *s, int32_t page_size, int32_t top_k) {
     if (check_shape(s, false) != DA_OK || check_page(page_size) != DA_OK) return 0;
     if (top_k < 1 || top_k > n_pages(s, page_size)) return 0;

@@ -92,6 +92,13 @@ hipError_t launch_select(int kv_fmt, int q_fmt, int64_t BH, int64_t P, int D,
                          const void *kmax, int32_t *page_idx, float *page_score,
                          hipStream_t stream, bool exact = false);
 
+// Exact-score token selection fused with attention over the kept tokens:
+// one workgroup per (b, h); o [BH][D] fp32; token_idx optional.  Dynamic
+// LDS holds N + 2 * top_k + 8 * D floats.
+hipError_t launch_topk_attention(int kv_fmt, int q_fmt, int64_t BH, int64_t N, int D, int top_k,
+                                 float scale_log2, const void *q, const void *k, const void *v, float *o,
+                                 int32_t *token_idx, hipStream_t stream);
+
 // uint4 group quantization.
 hipError_t launch_quantize_kv4(int64_t n_groups, const void *x, uint8_t *codes,
                                void *gmin, void *gscale, hipStream_t stream);

@@ -113,8 +113,25 @@ __global__ __launch_bounds__(256) void page_meta_kernel(int64_t BH, int64_t N, i
     *(u32x4 *)(kmax + dst) = pack16<F>(mx);
 }
 
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
+// Selection modes: bound scores over pages; exact scores over tokens; exact
+// scores over tokens followed by attention over the kept tokens.
+enum SelMode : int { SEL_PAGES = 0, SEL_TOKENS = 1, SEL_ATTEND = 2 };
+
+// Threads per workgroup (measured on MI355X): 1024 for pages (P = 2048 at
+// the TinyServe shape), 512 for tokens (P = 1024 at the FlexGen shape).
+constexpr int sel_threads(int mode) { return mode == SEL_PAGES ? 1024 : 512; }
+
+struct SelArgs {
+    int64_t P = 0;                 // pages (or tokens) per (b, h)
+    int32_t top_k = 0;
+    const void *q = nullptr;
+    const uint8_t *kmin = nullptr, *kmax = nullptr;   // tokens: kmax = the key rows
+    int32_t *page_idx = nullptr;   // may be NULL in SEL_ATTEND
+    float *page_score = nullptr;   // optional
+    const uint8_t *v = nullptr;    // SEL_ATTEND: value rows, laid out as the keys
+    float *o = nullptr;            // SEL_ATTEND: [BH][D] fp32
+    float scale_log2 = 0.f;        // SEL_ATTEND: softmax scale * log2(e)
+};
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     if (f == 0.f) f = 0.f;                        // -0 and +0 are one score
@@ -122,8 +139,9 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum of `v` over the workgroup (thread order); returns the
-// total through *total.  Uses `buf` (kSelWaves + 1 entries).
+// Exclusive prefix sum of `v` over the workgroup of NW waves (thread order);
+// returns the total through *total.  Uses `buf` (NW + 1 entries).
+template <int NW>
 __device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t *buf, uint32_t *total) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     uint32_t x = v;
@@ -135,33 +153,127 @@ __device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t *buf, uint
     if (lane == 63) buf[w] = x;
     __syncthreads();
     if (w == 0) {
-        uint32_t s = lane < kSelWaves ? buf[lane] : 0u;
+        uint32_t s = lane < NW ? buf[lane] : 0u;
 #pragma unroll
-        for (int o = 1; o < kSelWaves; o <<= 1) {
+        for (int o = 1; o < NW; o <<= 1) {
             const uint32_t y = __shfl_up(s, o, 64);
             if (lane >= o) s += y;
         }
-        if (lane < kSelWaves) buf[lane] = s;       // inclusive over waves
+        if (lane < NW) buf[lane] = s;              // inclusive over waves
     }
     __syncthreads();
     const uint32_t before = (w ? buf[w - 1] : 0u) + x - v;
-    *total = buf[kSelWaves - 1];
+    *total = buf[NW - 1];
     __syncthreads();
     return before;
 }
 
-template <int KF, int QF, int D, bool EXACT>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(int64_t P, int top_k, const void *__restrict__ q,
-                                                             const uint8_t *__restrict__ kmin,
-                                                             const uint8_t *__restrict__ kmax,
-                                                             int32_t *__restrict__ page_idx,
-                                                             float *__restrict__ page_score) {
+// Float reduction over the workgroup (NW waves); every thread gets the result.
+template <int NW, bool MAX>
+__device__ __forceinline__ float block_reduce(float x, float *buf) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_xor(x, o, 64);
+        x = MAX ? fmaxf(x, y) : x + y;
+    }
+    if (lane == 0) buf[w] = x;
+    __syncthreads();
+    float r = buf[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) r = MAX ? fmaxf(r, buf[i]) : r + buf[i];
+    __syncthreads();
+    return r;
+}
+
+// Attention of one (b, h) over its kept tokens (FlexGen's top-k sparse
+// attention, section "方法细节": only the V rows of the kept keys are read).
+// The exact scores of the kept tokens are still in LDS: with M their maximum,
+// w_i = 2^((s_i - M) * scale * log2 e), o = sum_i w_i v_i / sum_i w_i.
+// Threads own 16-byte column chunks of the value rows; workgroup slots of CH
+// lanes walk the kept list; the slots are summed through LDS.
+template <int KF, int D, int NW>
+__device__ __forceinline__ void attend_kept(const SelArgs &args, int64_t bh, const int32_t *kept,
+                                            const float *sc_lds, uint32_t *scan_buf) {
+    constexpr int R = D * Elem<KF>::size;
+    constexpr int EPC = 16 / Elem<KF>::size;    // values per 16-byte chunk
+    constexpr int CH = R / 16;                  // chunks (lanes) per row
+    constexpr int NT = NW * 64;
+    constexpr int SLOTS = NT / CH;
+    const int tid = threadIdx.x;
+    const int K = args.top_k;
+    const int64_t P = args.P;
+    float *wl = (float *)(kept + K);            // weights [K]
+    float *red = wl + K;                        // [NW][D]
+    float *fbuf = (float *)scan_buf;
+    __syncthreads();                            // kept[] complete
+
+    // kept[] holds exactly K indices in [0, P); the clamp only guards memory
+    auto kept_at = [&](int i) -> int64_t {
+        const int32_t t = kept[i];
+        return (t >= 0 && t < P) ? t : 0;
+    };
+    float m = -__builtin_inff();
+    for (int i = tid; i < K; i += NT) m = fmaxf(m, sc_lds[kept_at(i)]);
+    const float M = block_reduce<NW, true>(m, fbuf);
+    float lsum = 0.f;
+    for (int i = tid; i < K; i += NT) {
+        const float w = exp2f((sc_lds[kept_at(i)] - M) * args.scale_log2);
+        wl[i] = w;
+        lsum += w;
+    }
+    const float L = block_reduce<NW, false>(lsum, fbuf);   // also orders wl[] before use
+
+    const int ch = tid % CH, slot = tid / CH;
+    const uint8_t *vb = args.v + bh * P * R + 16 * ch;
+    float acc[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+    for (int i = slot; i < K; i += SLOTS) {
+        const u32x4 x = __builtin_nontemporal_load((const u32x4 *)(vb + kept_at(i) * R));
+        float f[EPC];
+        unpack16<KF>(x, f);
+        const float w = wl[i];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[e] = fmaf(w, f[e], acc[e]);
+    }
+    // sum the slots of each wave (lanes with the same chunk), then the waves
+#pragma unroll
+    for (int o = CH; o < 64; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+    const int lane = tid & 63, w = tid >> 6;
+    if (lane < CH) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) red[w * D + ch * EPC + e] = acc[e];
+    }
+    __syncthreads();
+    for (int d = tid; d < D; d += NT) {
+        float sum = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) sum += red[ww * D + d];
+        args.o[bh * D + d] = sum / L;
+    }
+}
+
+template <int KF, int QF, int D, int MODE>
+__global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args) {
+    constexpr bool EXACT = MODE != SEL_PAGES;
+    constexpr int kSelThreads = sel_threads(MODE);
+    constexpr int kSelWaves = kSelThreads / 64;
+    const int64_t P = args.P;
+    const int top_k = args.top_k;
+    const void *__restrict__ q = args.q;
+    const uint8_t *__restrict__ kmin = args.kmin;
+    const uint8_t *__restrict__ kmax = args.kmax;
+    int32_t *__restrict__ page_idx = args.page_idx;
+    float *__restrict__ page_score = args.page_score;
     constexpr int R = D * Elem<KF>::size;
     constexpr int NCH = R / 64;
     constexpr int NMF = KF == FMT_F32 ? 4 * NCH : NCH;
     constexpr int SPL = (KF == FMT_F32 || QF == KF) ? 1 : (KF == FMT_BF16 ? 3 : 2);
 
-    extern __shared__ float sc_lds[];              // [P]
+    extern __shared__ float sc_lds[];              // [P] (SEL_ATTEND: then kept[top_k], w[top_k])
     __shared__ uint32_t hist[256];
     __shared__ uint32_t scan_buf[kSelWaves + 1];
     __shared__ uint32_t pick_digit, pick_need, pick_count;
@@ -306,7 +418,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int64_t P, int top_
     if (!all_ties) {
         uint32_t n_eq = 0;
         for (int64_t i = i0; i < i1; ++i) n_eq += order_key(sc_lds[i]) == T;
-        eq_before = block_exscan(n_eq, scan_buf, &tot);
+        eq_before = block_exscan<kSelWaves>(n_eq, scan_buf, &tot);
     }
     uint32_t n_sel = 0;
     {
@@ -317,40 +429,55 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int64_t P, int top_
             else if (key == T) { if (all_ties || r < need) ++n_sel; ++r; }
         }
     }
-    uint32_t pos = block_exscan(n_sel, scan_buf, &tot);
-    int32_t *out = page_idx + bh * top_k;
+    uint32_t pos = block_exscan<kSelWaves>(n_sel, scan_buf, &tot);
+    int32_t *out = page_idx ? page_idx + bh * top_k : nullptr;
+    int32_t *kept = (int32_t *)(sc_lds + P);       // SEL_ATTEND: kept indices, ascending
     {
         uint32_t r = eq_before;
         for (int64_t i = i0; i < i1; ++i) {
             const uint32_t key = order_key(sc_lds[i]);
             bool sel = key > T;
             if (key == T) { sel = all_ties || r < need; ++r; }
-            if (sel && pos < (uint32_t)top_k) out[pos++] = (int32_t)i;
+            if (sel && pos < (uint32_t)top_k) {
+                if (out) out[pos] = (int32_t)i;
+                if constexpr (MODE == SEL_ATTEND) kept[pos] = (int32_t)i;
+                ++pos;
+            }
         }
     }
+    if constexpr (MODE == SEL_ATTEND) attend_kept<KF, D, kSelWaves>(args, bh, kept, sc_lds, scan_buf);
 }
 
-using SelFn = void (*)(int64_t, int, const void *, const uint8_t *, const uint8_t *, int32_t *, float *);
+using SelFn = void (*)(SelArgs);
 
-template <int KF, int QF, bool EXACT>
+template <int KF, int QF, int MODE>
 SelFn sel_d(int D) {
-    if (D == 64) return select_kernel<KF, QF, 64, EXACT>;
-    if (D == 128) return select_kernel<KF, QF, 128, EXACT>;
+    if (D == 64) return select_kernel<KF, QF, 64, MODE>;
+    if (D == 128) return select_kernel<KF, QF, 128, MODE>;
     return nullptr;
 }
 
-template <bool EXACT>
+template <int MODE>
 SelFn sel_pick(int kv, int qf, int D) {
     switch (kv) {
-    case FMT_F32: return qf == FMT_F32 ? sel_d<FMT_F32, FMT_F32, EXACT>(D) : nullptr;
+    case FMT_F32: return qf == FMT_F32 ? sel_d<FMT_F32, FMT_F32, MODE>(D) : nullptr;
     case FMT_F16:
-        if (qf == FMT_F16) return sel_d<FMT_F16, FMT_F16, EXACT>(D);
-        if (qf == FMT_F32) return sel_d<FMT_F16, FMT_F32, EXACT>(D);
+        if (qf == FMT_F16) return sel_d<FMT_F16, FMT_F16, MODE>(D);
+        if (qf == FMT_F32) return sel_d<FMT_F16, FMT_F32, MODE>(D);
         return nullptr;
     case FMT_BF16:
-        if (qf == FMT_BF16) return sel_d<FMT_BF16, FMT_BF16, EXACT>(D);
-        if (qf == FMT_F32) return sel_d<FMT_BF16, FMT_F32, EXACT>(D);
+        if (qf == FMT_BF16) return sel_d<FMT_BF16, FMT_BF16, MODE>(D);
+        if (qf == FMT_F32) return sel_d<FMT_BF16, FMT_F32, MODE>(D);
         return nullptr;
+    default: return nullptr;
+    }
+}
+
+SelFn sel_for(int mode, int kv, int qf, int D) {
+    switch (mode) {
+    case SEL_PAGES: return sel_pick<SEL_PAGES>(kv, qf, D);
+    case SEL_TOKENS: return sel_pick<SEL_TOKENS>(kv, qf, D);
+    case SEL_ATTEND: return sel_pick<SEL_ATTEND>(kv, qf, D);
     default: return nullptr;
     }
 }
@@ -376,16 +503,45 @@ hipError_t launch_page_meta(int kv_fmt, int64_t BH, int64_t N, int D, int log2_p
     return hipGetLastError();
 }
 
-bool select_supported(int kv_fmt, int q_fmt, int D) { return sel_pick<false>(kv_fmt, q_fmt, D) != nullptr; }
+bool select_supported(int kv_fmt, int q_fmt, int D) { return sel_for(SEL_PAGES, kv_fmt, q_fmt, D) != nullptr; }
 
 hipError_t launch_select(int kv_fmt, int q_fmt, int64_t BH, int64_t P, int D, int top_k, const void *q,
                          const void *kmin, const void *kmax, int32_t *page_idx, float *page_score,
                          hipStream_t stream, bool exact) {
-    SelFn fn = exact ? sel_pick<true>(kv_fmt, q_fmt, D) : sel_pick<false>(kv_fmt, q_fmt, D);
+    const int mode = exact ? SEL_TOKENS : SEL_PAGES;
+    SelFn fn = sel_for(mode, kv_fmt, q_fmt, D);
     if (!fn) return hipErrorInvalidValue;
+    SelArgs a;
+    a.P = P;
+    a.top_k = top_k;
+    a.q = q;
+    a.kmin = (const uint8_t *)kmin;
+    a.kmax = (const uint8_t *)kmax;
+    a.page_idx = page_idx;
+    a.page_score = page_score;
     const size_t lds = (size_t)P * sizeof(float);
-    hipLaunchKernelGGL(fn, dim3((unsigned)BH), dim3(kSelThreads), lds, stream, P, top_k, q,
-                       (const uint8_t *)kmin, (const uint8_t *)kmax, page_idx, page_score);
+    hipLaunchKernelGGL(fn, dim3((unsigned)BH), dim3(sel_threads(mode)), lds, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_attention(int kv_fmt, int q_fmt, int64_t BH, int64_t N, int D, int top_k, float scale_log2,
+                                 const void *q, const void *k, const void *v, float *o, int32_t *token_idx,
+                                 hipStream_t stream) {
+    SelFn fn = sel_for(SEL_ATTEND, kv_fmt, q_fmt, D);
+    if (!fn) return hipErrorInvalidValue;
+    SelArgs a;
+    a.P = N;
+    a.top_k = top_k;
+    a.q = q;
+    a.kmin = (const uint8_t *)k;
+    a.kmax = (const uint8_t *)k;
+    a.page_idx = token_idx;
+    a.v = (const uint8_t *)v;
+    a.o = o;
+    a.scale_log2 = scale_log2;
+    const int nw = sel_threads(SEL_ATTEND) / 64;
+    const size_t lds = ((size_t)N + 2 * (size_t)top_k + (size_t)nw * D) * sizeof(float);
+    hipLaunchKernelGGL(fn, dim3((unsigned)BH), dim3(sel_threads(SEL_ATTEND)), lds, stream, a);
     return hipGetLastError();
 }
 

@@ -158,6 +158,19 @@ def test_token_selection_checks(lib):
                                 NULL) == L.DA_OK
 
 
+def test_topk_attention_checks(lib):
+    s = mha(n_ctx=1024, head_dim=128)
+    att = lambda sh, k, idx=NULL: lib.da_decode_attention_topk(ctypes.byref(sh), k, FAKE, FAKE, FAKE, FAKE,
+                                                               idx, NULL)
+    assert att(s, 0) == L.DA_E_INVALID
+    assert att(s, 1025) == L.DA_E_INVALID
+    assert att(mha(n_q_heads=32, n_ctx=1024), 100) == L.DA_E_UNSUPPORTED     # GQA
+    assert att(mha(n_ctx=8192, head_dim=128), 3585) == L.DA_E_UNSUPPORTED    # LDS budget
+    assert att(s, 100, MISALIGNED) == L.DA_E_INVALID
+    assert lib.da_decode_attention_topk(ctypes.byref(s), 100, FAKE, FAKE, NULL, FAKE, NULL,
+                                        NULL) == L.DA_E_INVALID
+
+
 def test_kv4_checks(lib):
     q = lambda **kw: lib.da_quantize_kv4(kw.get("n", 4), kw.get("r", 128), FAKE, FAKE, FAKE, FAKE,
                                           NULL)

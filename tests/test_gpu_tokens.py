@@ -89,3 +89,44 @@ def test_flexgen_shape_full_size_sampled(da):
         check_selection(idx[b:b + 1, h:h + 1], r, K)
         ref = sparse_attention(q64, k64, v64, idx[b:b + 1, h:h + 1], 1, c.scale)
         assert_close(o[b, h], ref[0, 0], atol=1e-3, rel_rms=1e-4, what=f"w4 topk b{b} h{h}")
+
+
+@pytest.mark.parametrize("B,H,D,N,qd,kd,K", CASES)
+def test_fused_topk_attention(da, B, H, D, N, qd, kd, K):
+    """The one-kernel path (scores, top-k and attention over the kept value
+    rows in one workgroup) selects the same tokens as da_select_tokens and
+    matches the oracle on that set."""
+    import torch
+    K = K or keep_count(N)
+    c = synth.dense_case([400, B, H, D, N, K], B, H, H, D, N, qd, kd)
+    q, k, v = to_dev(c.q, qd), to_dev(c.k, kd), to_dev(c.v, kd)
+    o, idx = da.da_decode_attention_topk(q, k, v, K, scale=c.scale, want_idx=True)
+    idx2 = da.da_select_tokens(q, k, K)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    assert np.array_equal(idx, idx2.cpu().numpy())
+    q64, k64, v64 = as_f64(c.q, qd), as_f64(c.k, kd), as_f64(c.v, kd)
+    check_selection(idx, token_scores(q64, k64), K)
+    ref = sparse_attention(q64, k64, v64, idx, 1, c.scale)
+    assert_close(o.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what=f"fused topk {qd}/{kd} N{N} K{K}")
+
+
+def test_fused_topk_flexgen_shape_sampled(da):
+    import torch
+    c = synth.workload4()
+    N = c.k.shape[2]
+    K = keep_count(N)
+    q, k, v = to_dev(c.q, "f16"), to_dev(c.k, "f16"), to_dev(c.v, "f16")
+    o, idx = da.da_decode_attention_topk(q, k, v, K, scale=c.scale, want_idx=True)
+    torch.cuda.synchronize()
+    o, idx = o.cpu().numpy(), idx.cpu().numpy()
+    rng = np.random.default_rng(403)
+    picks = [(0, 0), (63, 55)] + [(int(b), int(h)) for b, h in
+                                  zip(rng.integers(0, 64, 6), rng.integers(0, 56, 6))]
+    for b, h in picks:
+        q64 = as_f64(c.q[b:b + 1, h:h + 1], "f16")
+        k64 = as_f64(c.k[b:b + 1, h:h + 1], "f16")
+        v64 = as_f64(c.v[b:b + 1, h:h + 1], "f16")
+        check_selection(idx[b:b + 1, h:h + 1], token_scores(q64, k64), K)
+        ref = sparse_attention(q64, k64, v64, idx[b:b + 1, h:h + 1], 1, c.scale)
+        assert_close(o[b, h], ref[0, 0], atol=1e-3, rel_rms=1e-4, what=f"w4 fused topk b{b} h{h}")
