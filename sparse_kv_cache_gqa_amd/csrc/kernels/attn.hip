@@ -108,8 +108,10 @@ struct Stage {
     u32x4 K[C::TS][C::NCH];
     u32x4 V[C::TS][C::VP];
     bool kok[C::TS];
-    uint32_t kmn[C::TS], ksc[C::TS];   // uint4: fp16 min/scale pairs of the K row (both groups)
-    float vmn[C::TS], vsc[C::TS];      // uint4: min/scale of the V row's group
+    // uint4: the fp16 (min, min) / (scale, scale) pairs of both groups of the
+    // K and V rows of stage token (lane mod tile), one coalesced dword each;
+    // the lanes that use a token's pair fetch it with a lane shuffle
+    uint32_t mk, sk, mv, sv;
 };
 
 // Each wave reduces one split of one (batch row, KV head) to a partial per
@@ -119,6 +121,8 @@ template <int KF, int QF, int D, int G, bool PAGED>
 __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(AttnLaunch a) {
     using C = Cfg<KF, QF, D, G>;
     static_assert(C::ok, "unsupported layout");
+    static_assert(!(PAGED && C::U4), "no paged uint4 cache");
+    static_assert(!C::U4 || (C::NGRP == 2 && C::VP == 1 && C::TILE <= 64), "uint4 layout");
     using St = Stage<KF, QF, D, G>;
     constexpr int R = C::R, RPH = C::RPH, HPL = C::HPL, SPL = C::SPL, NGRP = C::NGRP;
     constexpr int NCH = C::NCH, NMF = C::NMF, VP = C::VP, TPP = C::TPP, CPL = C::CPL;
@@ -214,14 +218,13 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
 #pragma unroll
                 for (int p = 0; p < VP; ++p)
                     st.V[ts][p] = buf_load16(vrs, (uint32_t)(t0 + ts * kSub + p * TPP + vtok) * R + vcol);
-                if constexpr (C::U4) {
-                    st.kmn[ts] = buf_load4(kmrs, (uint32_t)rk * NGRP * 2);
-                    st.ksc[ts] = buf_load4(ksrs, (uint32_t)rk * NGRP * 2);
-                    const uint32_t rv = t0 + ts * kSub + vtok;     // VP == 1 for uint4
-                    const int gr = vcol / 32;
-                    st.vmn[ts] = f16_to_f32(buf_load2(vmrs, (rv * NGRP + gr) * 2));
-                    st.vsc[ts] = f16_to_f32(buf_load2(vsrs, (rv * NGRP + gr) * 2));
-                }
+            }
+            if constexpr (C::U4) {
+                const uint32_t off = (uint32_t)(t0 + lane % kTile) * NGRP * 2;
+                st.mk = buf_load4(kmrs, off);
+                st.sk = buf_load4(ksrs, off);
+                st.mv = buf_load4(vmrs, off);
+                st.sv = buf_load4(vsrs, off);
             }
             return;
         }
@@ -234,20 +237,11 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
 #pragma unroll
             for (int c = 0; c < NCH; ++c)
                 st.K[ts][c] = ok ? ld_stream(p + 64 * c) : (u32x4){0u, 0u, 0u, 0u};
-            if constexpr (C::U4) {
-                st.kmn[ts] = ok ? ld_stream32(kmn + r * NGRP) : 0u;
-                st.ksc[ts] = ok ? ld_stream32(ksc + r * NGRP) : 0u;
-            }
 #pragma unroll
             for (int p2 = 0; p2 < VP; ++p2) {
                 bool okv;
                 const int64_t rv = row_of(t0 + ts * kSub + p2 * TPP + vtok, okv);
                 st.V[ts][p2] = okv ? ld_stream(vbase + rv * R + vcol) : (u32x4){0u, 0u, 0u, 0u};
-                if constexpr (C::U4) {
-                    const int gr = vcol / 32;
-                    st.vmn[ts] = okv ? f16_to_f32(ld_stream16(vmn + rv * NGRP + gr)) : 0.f;
-                    st.vsc[ts] = okv ? f16_to_f32(ld_stream16(vsc + rv * NGRP + gr)) : 0.f;
-                }
             }
         }
     };
@@ -323,6 +317,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     // ---- scores, online softmax and P.V of one loaded tile ---------------------
     auto compute_tile = [&](St &st) {
         float sc[kTS][HPL];
+
 #pragma unroll
         for (int ts = 0; ts < kTS; ++ts) {
             f32x4 cc = {0.f, 0.f, 0.f, 0.f};
@@ -350,13 +345,16 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
                 const int h = g4 * HPL + hh;
                 float raw = 0.f;
                 if constexpr (C::U4) {
+                    // this lane's K token (ts, n16): its (min, min) and (scale, scale) pairs
+                    const uint32_t kmn2 = __shfl(st.mk, ts * kSub + n16, 64);
+                    const uint32_t ksc2 = __shfl(st.sk, ts * kSub + n16, 64);
 #pragma unroll
                     for (int gr = 0; gr < NGRP; ++gr) {
                         float dot = 0.f;
 #pragma unroll
                         for (int s = 0; s < SPL; ++s) dot += cc[hh * RPH + gr * SPL + s];
-                        const float mn = f16_to_f32((st.kmn[ts] >> (16 * gr)) & 0xFFFFu);
-                        const float sg = f16_to_f32((st.ksc[ts] >> (16 * gr)) & 0xFFFFu);
+                        const float mn = f16_to_f32((kmn2 >> (16 * gr)) & 0xFFFFu);
+                        const float sg = f16_to_f32((ksc2 >> (16 * gr)) & 0xFFFFu);
                         raw += mn * qs[hh][gr] + sg * dot;
                     }
                 } else {
@@ -452,12 +450,16 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
                 } else if constexpr (C::U4) {
                     // even channels: low nibbles -> c; odd channels: high
                     // nibbles left in place -> 16 c, so their weight is w / 16
+                    // this lane's V token (ts, vtok), group vcol / 32
+                    const int gsh = 16 * (vcol / 32);
+                    const float vmn1 = f16_to_f32((__shfl(st.mv, ts * kSub + vtok, 64) >> gsh) & 0xFFFFu);
+                    const float vsc1 = f16_to_f32((__shfl(st.sv, ts * kSub + vtok, 64) >> gsh) & 0xFFFFu);
                     float wv[G], wv16[G];
 #pragma unroll
                     for (int h = 0; h < G; ++h) {
-                        wv[h] = pv[h] * st.vsc[ts];
+                        wv[h] = pv[h] * vsc1;
                         wv16[h] = wv[h] * 0.0625f;
-                        amin[h] = fmaf(pv[h], st.vmn[ts], amin[h]);
+                        amin[h] = fmaf(pv[h], vmn1, amin[h]);
                     }
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
@@ -663,6 +665,50 @@ __global__ __launch_bounds__(128) void attn_reduce_kernel(const float *__restric
     }
 }
 
+// Merge for n_split <= 4: one thread per output element, no LDS and no
+// barriers (measured on MI355X: 3584 rows x 2 splits in a third of the time
+// of the block-per-row kernel; with 16 splits over 256 rows the block-per-row
+// kernel stays faster).  Bit for bit the result of attn_reduce_kernel: M is
+// a max; L = (w0 l0 + w1 l1) + (w2 l2 + w3 l3), the tree its shuffle
+// butterfly forms for n_split <= 4 (empty slots add 0); O is one fma chain.
+constexpr int kMergeSmall = 4;
+
+__global__ __launch_bounds__(256) void attn_reduce_small_kernel(const float *__restrict__ ws, float *__restrict__ o,
+                                                                int n_split, int D, int HG, int64_t o_bstride,
+                                                                int64_t total) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= total) return;
+    const int64_t row = t / D;
+    const int d = (int)(t - row * D);
+    const int64_t b = row / HG, hq = row - b * HG;
+    const int PSTR = D + 4;
+    const float *p = ws + row * n_split * PSTR;
+    float M = neg_inf();
+    for (int s = 0; s < n_split; ++s) M = fmaxf(M, p[s * PSTR + D]);
+    float w[kMergeSmall], pl[kMergeSmall];
+#pragma unroll
+    for (int s = 0; s < kMergeSmall; ++s) {
+        w[s] = 0.f;
+        pl[s] = 0.f;
+        if (s < n_split) {
+            const float m = p[s * PSTR + D];
+            w[s] = (m == neg_inf()) ? 0.f : fast_exp2(m - M);
+            pl[s] = fmaf(w[s], p[s * PSTR + D + 1], 0.f);
+        }
+    }
+#pragma unroll
+    for (int half = kMergeSmall / 2; half >= 1; half >>= 1)
+#pragma unroll
+        for (int i = 0; i < half; ++i) pl[i] = pl[2 * i] + pl[2 * i + 1];
+    const float L = pl[0];
+    float O0 = 0.f;
+    const float O1 = 0.f, O2 = 0.f, O3 = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMergeSmall; ++j)
+        if (j < n_split) O0 = fmaf(w[j], p[j * PSTR + d], O0);
+    o[b * o_bstride + hq * D + d] = ((O0 + O1) + (O2 + O3)) / L;
+}
+
 using SplitFn = void (*)(AttnLaunch);
 
 struct SplitKernel {
@@ -778,6 +824,14 @@ hipError_t launch_merge(int64_t rows, int32_t heads_per_row, int32_t n_split, in
                         int64_t o_bstride, hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
     if (rows > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (n_split <= kMergeSmall) {
+        const int64_t total = rows * D;
+        const int64_t blocks = (total + 255) / 256;
+        if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(attn_reduce_small_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ws, o, n_split,
+                           D, heads_per_row, o_bstride, total);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(attn_reduce_kernel, dim3((unsigned)rows), dim3(D), 0, stream, ws, o, n_split, D,
                        heads_per_row, o_bstride);
     return hipGetLastError();

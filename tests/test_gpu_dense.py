@@ -140,7 +140,7 @@ def test_partials_match_oracle(da, B, Hq, Hkv, D, N, qd, kd, st):
     assert_close(ws[..., :D], u, atol=2e-6 * np.abs(u).max(), what=f"partials u split {st}")
 
 
-@pytest.mark.parametrize("ns,D", [(1, 64), (3, 128), (20, 64), (100, 128)])
+@pytest.mark.parametrize("ns,D", [(1, 64), (3, 128), (16, 128), (7, 64), (20, 64), (100, 128)])
 def test_merge_matches_oracle(da, ns, D):
     """The cross-split merge on its own, on seeded partials with empty splits
     (m = -inf) and a wide spread of maxima."""
