@@ -552,6 +552,20 @@ def bench_stream(args, torch, np, da, synth):
             f"device buffers {2 * nb / 2**30:.0f} GiB")
     ms = grouping[1]["ms_per_step"]
     gbs = total / (ms * 1e-3) / 1e9
+    # the per-step append of the new token (K and V rows of every layer-head,
+    # device to host into row n_ctx - 1) on the copy stream
+    hs = da.HeadwiseStream(spec.batch, spec.n_q_heads, spec.n_kv_heads, spec.head_dim, spec.n_ctx,
+                           da.DA_F32, da.DA_BF16)
+    k_new = torch.zeros((L, spec.batch, H, spec.head_dim), dtype=torch.bfloat16, device="cuda")
+    v_new = torch.zeros_like(k_new)
+
+    def append(i):
+        hs.set_length(spec.n_ctx - 1)
+        hs.append(k_new, v_new, k_list, v_list, stream=cpy)
+
+    append_ms = time_events(torch, append, 5, 1, stream=cpy)
+    hs.close()
+    log(f"stream append of one token (32 layers x 8 heads, 512 B each): {append_ms * 1e3:.0f} us")
     res = {"workload": "headinfer-headwise L32 Hkv8 Hq32 D128 N1048576 bf16 B1",
            "ms_per_step": ms, "h2d_bytes_per_step": total, "h2d_gbs": gbs,
            "measured_h2d_peak_gbs": h2d_gbs, "frac_measured_h2d": gbs / h2d_gbs,
@@ -560,7 +574,8 @@ def bench_stream(args, torch, np, da, synth):
            "pool": f"{pool_heads} distinct pinned layer-heads ({2 * pool_heads * hb / 2**30:.0f} GiB) "
                    f"reused cyclically for the 256 layer-heads of a step; every layer-head is a real "
                    f"512 MiB H2D copy",
-           "head_grouping": {str(k): v for k, v in grouping.items()}}
+           "head_grouping": {str(k): v for k, v in grouping.items()},
+           "append_ms": append_ms, "append_bytes": 2 * L * H * spec.batch * spec.head_dim * 2}
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_stream(spec, kh[0], vh[0], hb)
     log(f"stream: {ms:.0f} ms/step, {gbs:.1f} GB/s H2D vs measured peak {h2d_gbs:.1f} GB/s")

@@ -303,6 +303,20 @@ da_status da_decode_attention_kv4(const da_attn_shape *s, const void *q,
  *   compute != copy.  The output is complete when `compute` drains.
  * Each head's result is bitwise equal to da_decode_attention on the same
  * data with the same split_tokens.
+ *
+ * Growing the context (the per-step append of the new token's K/V; HeadInfer
+ * keeps the whole cache on the host):  the n_ctx of `per_layer` is the row
+ * capacity `cap` of every host cache ([batch][cap][head_dim]); a context
+ * attends to the first `len` rows of each batch row (len = cap at creation,
+ * da_stream_length / da_stream_set_length, 1 <= len <= cap), copying them
+ * into a dense [batch][len][head_dim] buffer; the attention then equals
+ * da_decode_attention over those len tokens.
+ * da_stream_append: on `stream`, copies the new token's rows
+ *   k_new, v_new [n_layers][batch][n_kv_heads][head_dim] kv_dtype, device,
+ * into row len of every host cache (head_dim values per (layer, head, batch
+ * row), device to host), then sets len = len + 1 on the host.  Fails with
+ * DA_E_INVALID when len == cap.  Give it the copy stream of the next
+ * da_stream_headwise (or order the streams), so the rows land first.
  * ------------------------------------------------------------------------ */
 typedef struct da_stream_ctx da_stream_ctx;
 
@@ -318,6 +332,12 @@ da_status da_stream_headwise(da_stream_ctx *c, int32_t n_layers,
                              const void *q, float *o, void *ws,
                              size_t ws_bytes, hipStream_t compute,
                              hipStream_t copy);
+int64_t da_stream_length(const da_stream_ctx *c);
+da_status da_stream_set_length(da_stream_ctx *c, int64_t len);
+da_status da_stream_append(da_stream_ctx *c, int32_t n_layers,
+                           const void *k_new, const void *v_new,
+                           void *const *k_host, void *const *v_host,
+                           hipStream_t stream);
 void da_stream_destroy(da_stream_ctx *c);
 
 #ifdef __cplusplus

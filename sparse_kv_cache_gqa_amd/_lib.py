@@ -63,6 +63,9 @@ SIGNATURES = {
     "da_stream_workspace": (c_sz, [c_vp]),
     "da_stream_headwise": (ctypes.c_int, [c_vp, c_i32, _P(c_vp), _P(c_vp), c_vp, c_vp, c_vp, c_vp, c_vp,
                                           c_sz, c_vp, c_vp]),
+    "da_stream_length": (ctypes.c_int64, [c_vp]),
+    "da_stream_set_length": (ctypes.c_int, [c_vp, ctypes.c_int64]),
+    "da_stream_append": (ctypes.c_int, [c_vp, c_i32, c_vp, c_vp, _P(c_vp), _P(c_vp), c_vp]),
     "da_stream_destroy": (None, [c_vp]),
 }
 

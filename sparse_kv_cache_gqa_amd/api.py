@@ -374,6 +374,33 @@ class HeadwiseStream:
                                            _nbytes(ws), _stream(compute), _stream(copy)))
         return out
 
+    @property
+    def length(self) -> int:
+        """Rows attended per batch row (the host caches hold n_ctx rows)."""
+        return int(self._lib.da_stream_length(self._ctx))
+
+    def set_length(self, n):
+        check(self._lib.da_stream_set_length(self._ctx, int(n)))
+
+    def append(self, k_new, v_new, k_host, v_host, stream=None):
+        """Copy the new token's rows k_new, v_new [L][B][Hkv][D] (device) into
+        row `length` of every host cache, then extend the length by one."""
+        _dev(k_new, v_new)
+        n = len(k_host)
+        if n % self.shape.n_kv_heads or len(v_host) != n:
+            raise ValueError("need n_layers * n_kv_heads host tensors for K and for V")
+        L = n // self.shape.n_kv_heads
+        want = (L, self.shape.batch, self.shape.n_kv_heads, self.shape.head_dim)
+        for t in (k_new, v_new):
+            if tuple(t.shape) != want or not t.is_contiguous():
+                raise ValueError(f"new rows must be contiguous {want}")
+        for t in list(k_host) + list(v_host):
+            if t.is_cuda or not t.is_contiguous():
+                raise ValueError("host KV tensors must be contiguous CPU tensors")
+        kp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in k_host])
+        vp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in v_host])
+        check(self._lib.da_stream_append(self._ctx, L, _vp(k_new), _vp(v_new), kp, vp, _stream(stream)))
+
     def close(self):
         if self._ctx:
             self._lib.da_stream_destroy(self._ctx)

@@ -7,13 +7,19 @@
 //
 // HeadInfer also writes the previous head back device-to-host; a decode step
 // does not change the cached keys and values, so there is nothing to write
-// back and that copy is not issued.
+// back and that copy is not issued.  What a step does add is the new token:
+// da_stream_append copies its key and value rows (head_dim values per head
+// and batch row) device-to-host into row `len` of every host cache and
+// extends the attended length.  The host caches hold `cap` rows per batch row
+// (the n_ctx given at creation); a step streams the first `len` rows of each
+// batch row into a dense [batch][len][head_dim] buffer.
 #include "host.h"
 
 #include <new>
 
 struct da_stream_ctx {
-    da_attn_shape shape;
+    da_attn_shape shape;     // n_ctx = cap, the host caches' rows per batch row
+    int64_t len;             // rows attended (and copied) per batch row, <= cap
     int32_t hpc;             // heads per chunk (per transfer)
     int device;
     hipEvent_t ready[2];
@@ -73,6 +79,7 @@ da_status da_stream_create(const da_attn_shape *s, int32_t heads_per_chunk, da_s
     auto *c = new (std::nothrow) da_stream_ctx();
     if (!c) return fail(DA_E_INVALID, "out of host memory");
     c->shape = *s;
+    c->len = s->n_ctx;
     c->hpc = heads_per_chunk;
     hipError_t e = hipGetDevice(&c->device);
     int made = 0;
@@ -125,13 +132,23 @@ da_status da_stream_headwise(da_stream_ctx *c, int32_t n_layers, const void *con
     }
 
     const int G = s->n_q_heads / s->n_kv_heads;
-    const size_t hb = head_bytes(s);
+    da_attn_shape cur = *s;                       // the attended length
+    cur.n_ctx = c->len;
+    const size_t hb = head_bytes(&cur);           // bytes of one head's K (or V) in a buffer
+    const size_t row_dev = (size_t)c->len * s->head_dim * esize(s->kv_dtype);
+    const size_t row_host = (size_t)s->n_ctx * s->head_dim * esize(s->kv_dtype);
     const int n_chunks = s->n_kv_heads / c->hpc;
     const int qes = esize(s->q_dtype);
-    AttnLaunch a = dense_launch(s, s->kv_dtype, SPLIT_DENSE);
+    AttnLaunch a = dense_launch(&cur, s->kv_dtype, SPLIT_DENSE);
     a.Hkv = c->hpc;
-    a.kv_bstride = s->n_ctx;                      // buffer layout [hpc][B][N][D]
-    a.kv_hstride = (int64_t)s->batch * s->n_ctx;
+    a.kv_bstride = c->len;                        // buffer layout [hpc][B][len][D]
+    a.kv_hstride = (int64_t)s->batch * c->len;
+    // host rows [B][cap][D] -> device [B][len][D]: one copy when len == cap
+    auto h2d = [&](void *dst, const void *src) -> hipError_t {
+        if (row_dev == row_host) return hipMemcpyAsync(dst, src, hb, hipMemcpyHostToDevice, copy);
+        return hipMemcpy2DAsync(dst, row_dev, src, row_host, row_dev, (size_t)s->batch, hipMemcpyHostToDevice,
+                                copy);
+    };
     a.ws = (float *)ws;
     void *bufs[2] = {buf0, buf1};
 
@@ -145,8 +162,8 @@ da_status da_stream_headwise(da_stream_ctx *c, int32_t n_layers, const void *con
             if (u >= 2) e = hipStreamWaitEvent(copy, c->freed[slot], 0);
             for (int i = 0; i < c->hpc && e == hipSuccess; ++i) {
                 const int64_t hi = (int64_t)l * s->n_kv_heads + (int64_t)ch * c->hpc + i;
-                e = hipMemcpyAsync(kb + i * hb, k_host[hi], hb, hipMemcpyHostToDevice, copy);
-                if (e == hipSuccess) e = hipMemcpyAsync(vb + i * hb, v_host[hi], hb, hipMemcpyHostToDevice, copy);
+                e = h2d(kb + i * hb, k_host[hi]);
+                if (e == hipSuccess) e = h2d(vb + i * hb, v_host[hi]);
             }
             if (e == hipSuccess) e = hipEventRecord(c->ready[slot], copy);
             if (e == hipSuccess) e = hipStreamWaitEvent(compute, c->ready[slot], 0);
@@ -161,6 +178,53 @@ da_status da_stream_headwise(da_stream_ctx *c, int32_t n_layers, const void *con
         }
     }
     if (e != hipSuccess) return hip_fail(e, "head-wise streaming");
+    return ok();
+}
+
+int64_t da_stream_length(const da_stream_ctx *c) { return c ? c->len : 0; }
+
+da_status da_stream_set_length(da_stream_ctx *c, int64_t len) {
+    if (!c) return fail(DA_E_INVALID, "context is NULL");
+    if (len < 1 || len > c->shape.n_ctx)
+        return fail(DA_E_INVALID, "length %lld not in [1, %lld]", (long long)len, (long long)c->shape.n_ctx);
+    c->len = len;
+    return ok();
+}
+
+da_status da_stream_append(da_stream_ctx *c, int32_t n_layers, const void *k_new, const void *v_new,
+                           void *const *k_host, void *const *v_host, hipStream_t stream) {
+    if (!c) return fail(DA_E_INVALID, "context is NULL");
+    if (n_layers < 1) return fail(DA_E_INVALID, "n_layers %d < 1", n_layers);
+    if (!k_host || !v_host) return fail(DA_E_INVALID, "host pointer arrays are NULL");
+    const da_attn_shape *s = &c->shape;
+    if (c->len >= s->n_ctx)
+        return fail(DA_E_INVALID, "host caches are full (%lld rows)", (long long)s->n_ctx);
+    DA_TRY(check_ptr(k_new, "k_new"));
+    DA_TRY(check_ptr(v_new, "v_new"));
+    const int64_t n_heads = (int64_t)n_layers * s->n_kv_heads;
+    for (int64_t i = 0; i < n_heads; ++i) {
+        DA_TRY(check_pinned(k_host[i], "k_host", i));
+        DA_TRY(check_pinned(v_host[i], "v_host", i));
+    }
+    const size_t es = esize(s->kv_dtype);
+    const size_t row = (size_t)s->head_dim * es;                 // one token of one head
+    const size_t src_pitch = (size_t)s->n_kv_heads * row;        // new rows [L][B][Hkv][D]
+    const size_t dst_pitch = (size_t)s->n_ctx * row;             // host caches [B][cap][D]
+    hipError_t e = hipSuccess;
+    for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
+        for (int h = 0; h < s->n_kv_heads && e == hipSuccess; ++h) {
+            const int64_t hi = (int64_t)l * s->n_kv_heads + h;
+            const size_t src = ((size_t)l * s->batch * s->n_kv_heads + h) * row;
+            const size_t dst = (size_t)c->len * row;
+            e = hipMemcpy2DAsync((char *)k_host[hi] + dst, dst_pitch, (const char *)k_new + src, src_pitch, row,
+                                 (size_t)s->batch, hipMemcpyDeviceToHost, stream);
+            if (e == hipSuccess)
+                e = hipMemcpy2DAsync((char *)v_host[hi] + dst, dst_pitch, (const char *)v_new + src, src_pitch, row,
+                                     (size_t)s->batch, hipMemcpyDeviceToHost, stream);
+        }
+    }
+    if (e != hipSuccess) return hip_fail(e, "append");
+    c->len += 1;
     return ok();
 }
 

@@ -203,6 +203,9 @@ def test_headwise_sizes_match_the_pages_and_checks(lib):
     arr = (ctypes.c_void_p * 1)(FAKE)
     assert lib.da_stream_headwise(None, 1, arr, arr, FAKE, FAKE, FAKE, FAKE, FAKE, 1, NULL,
                                   ctypes.c_void_p(1)) == L.DA_E_INVALID
+    assert lib.da_stream_length(None) == 0
+    assert lib.da_stream_set_length(None, 5) == L.DA_E_INVALID
+    assert lib.da_stream_append(None, 1, FAKE, FAKE, arr, arr, NULL) == L.DA_E_INVALID
     assert lib.da_stream_buffer_bytes(None) == 0
     assert lib.da_stream_workspace(None) == 0
     lib.da_stream_destroy(None)

@@ -106,3 +106,60 @@ def test_workload5_shape_one_layer(da):
     for h in range(spec.n_kv_heads):
         if h not in real:
             assert not np.any(got[:, :, 4 * h:4 * h + 4]), f"zero head {h}"
+
+
+def test_append_new_token_then_stream(da):
+    """The per-step append: the new token's K/V rows go device-to-host into
+    row `length` of every host cache, the length grows by one, and the next
+    streamed step attends over the grown context (equal to the oracle and,
+    bitwise, to resident attention over the same rows)."""
+    import torch
+    spec = synth.small_headwise(n_layers=2, n_kv_heads=2, n_q_heads=4, batch=3, head_dim=64,
+                                n_ctx=300, tag=51)
+    ks, vs, k64, v64 = host_heads(spec)
+    L, H, B, D = spec.n_layers, spec.n_kv_heads, spec.batch, spec.head_dim
+    pos = 298
+    # the new token's rows, as a projection would leave them: [L][B][Hkv][D]
+    k_new = torch.stack([torch.stack([ks[l * H + h][:, pos] for h in range(H)], 1) for l in range(L)])
+    v_new = torch.stack([torch.stack([vs[l * H + h][:, pos] for h in range(H)], 1) for l in range(L)])
+    keep_k = [t[:, pos:].clone() for t in ks]
+    for t in ks + vs:
+        t[:, pos:] = 0
+    hs = da.HeadwiseStream(B, spec.n_q_heads, H, D, spec.n_ctx, da.DA_F32, da.DA_BF16)
+    hs.set_length(pos)
+    assert hs.length == pos
+    cpy = torch.cuda.Stream()
+    hs.append(k_new.cuda(), v_new.cuda(), ks, vs, stream=cpy)
+    cpy.synchronize()
+    assert hs.length == pos + 1
+    for i, t in enumerate(ks):
+        assert torch.equal(t[:, pos], keep_k[i][:, 0])
+        assert torch.count_nonzero(t[:, pos + 1:].float()) == 0
+
+    buf0 = torch.empty(hs.buffer_bytes, dtype=torch.uint8, device="cuda")
+    buf1 = torch.empty(hs.buffer_bytes, dtype=torch.uint8, device="cuda")
+    q = to_dev(spec.q(), "f32")
+    out = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(16, hs.workspace_bytes), dtype=torch.uint8, device="cuda")
+    comp = torch.cuda.current_stream()
+    cpy.wait_stream(comp)
+    hs.da_stream_headwise(ks, vs, buf0, buf1, q, out, ws, comp, cpy)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    n = pos + 1
+    ref = headwise_attention(as_f64(spec.q(), "f32"), [[k[:, :n] for k in kl] for kl in k64],
+                             [[v[:, :n] for v in vl] for vl in v64], 1.0 / np.sqrt(D))
+    assert_close(got, ref, atol=1e-5, rel_rms=1e-4, what="stream after append")
+    for l in range(L):
+        kres = torch.stack([ks[l * H + h][:, :n] for h in range(H)], 1).contiguous().cuda()
+        vres = torch.stack([vs[l * H + h][:, :n] for h in range(H)], 1).contiguous().cuda()
+        o = da.da_decode_attention(q[l], kres, vres)
+        torch.cuda.synchronize()
+        assert np.array_equal(o.cpu().numpy().view(np.uint32), got[l].view(np.uint32))
+
+    hs.append(k_new.cuda(), v_new.cuda(), ks, vs, stream=cpy)      # row 299: full now
+    cpy.synchronize()
+    assert hs.length == spec.n_ctx
+    with pytest.raises(da.DaError):
+        hs.append(k_new.cuda(), v_new.cuda(), ks, vs, stream=cpy)
+    hs.close()
