@@ -286,6 +286,9 @@ def bench_sparse(args, torch, np, da, synth):
         "gather_gbs": (sel_kv_bytes + B * H * D * 6) / (ms_gather * 1e-3) / 1e9,
         "page_meta_ms": ms_meta, "dense_same_cache_ms": ms_dense, "eager_ms_per_step": ms_eager,
         "speedup_vs_dense": ms_dense / ms,
+        "traffic": {"select": measured_traffic("select_tinyserve_32k", meta_bytes + B * H * D * 2),
+                    "gather_attention": measured_traffic("attn_split_paged_tinyserve_32k",
+                                                         sel_kv_bytes + B * H * D * 2)},
     }
     log(f"sparse: {ms * 1e3:.1f} us/step ({gbs:.0f} GB/s), select {ms_sel * 1e3:.1f} us, "
         f"gather {ms_gather * 1e3:.1f} us, dense on same cache {ms_dense * 1e3:.1f} us")
@@ -379,7 +382,8 @@ def bench_kv4(args, torch, np, da, synth):
     del k, v
     res = {"workload": "flexgen-uint4 B64 H56 D128 N1024 groups of 64", "ms_per_step": ms,
            "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "step_bytes": step_bytes,
-           "tokens_per_s": B / (ms * 1e-3), "quantize_k_ms": ms_quant, "eager_ms_per_step": ms_eager}
+           "tokens_per_s": B / (ms * 1e-3), "quantize_k_ms": ms_quant, "eager_ms_per_step": ms_eager,
+           "traffic": measured_traffic("attn_split_uint4_flexgen", code_bytes + ms_bytes + B * H * D * 2)}
     log(f"kv4: {ms * 1e3:.1f} us/step ({gbs:.0f} GB/s)")
     if host is not None:
         res["cpu_baseline"] = cpu_kv4(host, step_bytes / B)
@@ -453,7 +457,8 @@ def bench_topk(args, torch, np, da, synth):
            "avg_launch_ms": ms_fused_kernel, "kernel_gbs": step_bytes / (ms_fused_kernel * 1e-3) / 1e9,
            "two_kernel_ms_per_step": ms_two, "two_kernel_select_ms": ms_sel,
            "two_kernel_attention_ms": ms_att,
-           "dense_same_cache_ms": ms_dense, "speedup_vs_dense": ms_dense / ms, "eager_ms_per_step": ms_eager}
+           "dense_same_cache_ms": ms_dense, "speedup_vs_dense": ms_dense / ms, "eager_ms_per_step": ms_eager,
+           "traffic": measured_traffic("topk_attention_flexgen", step_bytes)}
     log(f"topk: {ms * 1e3:.1f} us/step ({gbs:.0f} GB/s) in one kernel; two kernels {ms_two * 1e3:.1f} us "
         f"(select {ms_sel * 1e3:.1f} + attention {ms_att * 1e3:.1f}); dense on same cache "
         f"{ms_dense * 1e3:.1f} us")
