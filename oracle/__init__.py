@@ -12,7 +12,8 @@ Sources (the pages these functions follow):
 * HeadInfer (blog.gzher.com, "论文阅读：HeadInfer"): per-head decode attention
   equation in section "核心 idea"; head independence, ping-pong buffers and the
   on-GPU size formula in sections "核心 idea", "三个维度的切分" and "方法：
-  ping-pong memory 与异步重叠".
+  ping-pong memory 与异步重叠"; chunked prefill in "chunked prefill 与 adaptive
+  head grouping".
 * TinyServe (papercache.org, "TinyServe: Query-Aware Cache Selection"):
   standard decode equation, page partition, TopK, SparseAttn and the
   directional bounding-box score in section "方法细节" and Algorithm 1.
@@ -27,6 +28,7 @@ Modules:
 * :mod:`oracle.paged` -- page metadata, bound score, top-K, sparse attention.
 * :mod:`oracle.kv4` -- uint4 group quantization, dequantization, attention.
 * :mod:`oracle.tokens` -- token-level top-k sparse attention (FlexGen).
+* :mod:`oracle.prefill` -- chunked prefill attention (HeadInfer).
 
 Pinning status: every function is pinned by tests against closed forms,
 invariants, brute force on tiny inputs or an independent library routine (see
@@ -40,3 +42,4 @@ from .paged import (page_meta, bound_scores, topk_pages,  # noqa: F401
 from .kv4 import quantize_kv4, dequantize_kv4, kv4_attention  # noqa: F401
 from .tokens import (keep_count, token_scores, topk_tokens,  # noqa: F401
                      topk_token_attention)
+from .prefill import chunk_prefill_attention  # noqa: F401
