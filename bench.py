@@ -485,6 +485,67 @@ def cpu_topk(host, K, bytes_per_row):
 
 
 # ---------------------------------------------------------------------------
+# extra: chunked prefill (HeadInfer shape), matrix-core bound
+# ---------------------------------------------------------------------------
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak (no sparsity)
+
+
+def bench_prefill(args, torch, np, da, synth):
+    log("extra: chunked prefill, Llama-3-8B heads (32 q / 8 KV, D128, bf16), 10K chunk after 30K prefix")
+    t0 = time.time()
+    c = synth.workload6()
+    log(f"generated inputs in {time.time() - t0:.1f}s")
+    B, Hq, C, D = c.q.shape
+    Hkv, T = c.k.shape[1], c.k.shape[2]
+    P = c.prefix
+    q = up(c.q, "bf16", torch, np)
+    k = up(c.k, "bf16", torch, np)
+    v = up(c.v, "bf16", torch, np)
+    host = None if args.no_cpu else (c.q[:, 0:1, 0:256].copy(), c.k[:, 0:1, :P + 256].copy(),
+                                     c.v[:, 0:1, :P + 256].copy(), P)
+    del c
+    out = torch.empty((B, Hq, C, D), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        da.da_prefill_attention(q, k, v, out=out)
+
+    steps = max(5, args.steps // 5)
+    ms = time_each(torch, step, steps)
+    # algorithmic flops: query i sees prefix + i + 1 keys; q.k and p.v are 2 D flops each per key
+    flops = 4.0 * D * B * Hq * (C * P + C * (C + 1) / 2)
+    tflops = flops / (ms * 1e-3) / 1e12
+    res = {"workload": f"headinfer-chunked-prefill B{B} Hq{Hq} Hkv{Hkv} D{D} chunk {C} after prefix {P} bf16",
+           "ms_per_step": ms, "flops_per_step": flops, "tflops": tflops,
+           "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "kernel": "prefill_kernel",
+                        "note": "algorithmic flops; the kernel issues 1.5x for the two-term probabilities"},
+           "tokens_per_s": C / (ms * 1e-3)}
+    log(f"prefill: {ms:.2f} ms per chunk, {tflops:.0f} TFLOP/s ({tflops / MFMA_BF16_PEAK_TFLOPS:.1%} of "
+        f"the 2.5 PFLOP/s bf16 peak), {C / (ms * 1e-3):.0f} tokens/s per layer")
+    if host is not None:
+        res["cpu_baseline"] = cpu_prefill(host, D)
+    return res
+
+
+def cpu_prefill(host, D):
+    """Oracle prefill on one query head and the first 256 queries of the chunk."""
+    import numpy as np
+    from oracle import chunk_prefill_attention
+    from oracle.numerics import as_f64
+    q, k, v, P = host
+    C = q.shape[2]
+
+    def once():
+        chunk_prefill_attention(as_f64(q, "bf16"), as_f64(k, "bf16"), as_f64(v, "bf16"), 1.0 / np.sqrt(D), P)
+
+    sec, n, _ = time_oracle(once, 3.0)
+    flops = 4.0 * D * (C * P + C * (C + 1) / 2)
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"query head 0, the first {C} queries of the chunk (prefix {P}), median of {n} runs "
+                      f"after 1 warm-up, {sec:.2f} s per run"}
+
+
+# ---------------------------------------------------------------------------
 # extra: head-wise streamed (HeadInfer shape)
 # ---------------------------------------------------------------------------
 def bench_stream(args, torch, np, da, synth):
@@ -621,7 +682,7 @@ def main(argv=None) -> int:
     ap.add_argument("--stream-pool-heads", type=int, default=16)
     ap.add_argument("--stream-steps", type=int, default=2)
     ap.add_argument("--only", default="",
-                    help="comma list of dense,sparse,kv4,topk,stream (profiling runs; no JSON line "
+                    help="comma list of dense,sparse,kv4,topk,prefill,stream (profiling runs; no JSON line "
                          "unless dense is included)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run three 512 MiB device-to-device copies (a kernel of known "
@@ -655,8 +716,9 @@ def main(argv=None) -> int:
         del src, dst
 
     if only and "dense" not in only:
-        runners = {"sparse": bench_sparse, "kv4": bench_kv4, "topk": bench_topk, "stream": bench_stream}
-        for name in ("sparse", "kv4", "topk", "stream"):
+        runners = {"sparse": bench_sparse, "kv4": bench_kv4, "topk": bench_topk, "prefill": bench_prefill,
+                   "stream": bench_stream}
+        for name in ("sparse", "kv4", "topk", "prefill", "stream"):
             if name in only:
                 torch.cuda.empty_cache()
                 print(json.dumps({name: runners[name](args, torch, np, da, synth)}), flush=True)
@@ -673,7 +735,7 @@ def main(argv=None) -> int:
     if only:
         args.no_extra = True
         for key, name, fn in (("sparse", "page_sparse", bench_sparse), ("kv4", "uint4", bench_kv4),
-                              ("topk", "token_topk", bench_topk)):
+                              ("topk", "token_topk", bench_topk), ("prefill", "chunked_prefill", bench_prefill)):
             if key in only:
                 torch.cuda.empty_cache()
                 extra[name] = fn(args, torch, np, da, synth)
@@ -681,7 +743,8 @@ def main(argv=None) -> int:
             torch.cuda.empty_cache()
             extra["headwise_stream"] = bench_stream(args, torch, np, da, synth)
     if not args.no_extra:
-        for name, fn in (("page_sparse", bench_sparse), ("uint4", bench_kv4), ("token_topk", bench_topk)):
+        for name, fn in (("page_sparse", bench_sparse), ("uint4", bench_kv4), ("token_topk", bench_topk),
+                         ("chunked_prefill", bench_prefill)):
             torch.cuda.empty_cache()
             extra[name] = fn(args, torch, np, da, synth)
         if not args.no_stream:

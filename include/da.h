@@ -26,6 +26,9 @@
  *     da_dequantize_kv4,         groups of 64 channels, and attention that
  *     da_decode_attention_kv4    dequantizes while loading (FlexGen digest,
  *                                section "方法细节").
+ *   - da_prefill_attention       HeadInfer's chunked prefill: a chunk of
+ *                                queries attends causally to the cache so far
+ *                                and to itself (compute-bound; matrix cores).
  *   - da_stream_*                HeadInfer's head-wise offload: the cache of
  *                                each (layer, KV head) lives in pinned host
  *                                memory and is copied into one of two
@@ -279,6 +282,25 @@ da_status da_decode_attention_kv4(const da_attn_shape *s, const void *q,
                                   const void *v_min, const void *v_scale,
                                   float *o, void *ws, size_t ws_bytes,
                                   hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Chunked prefill attention (HeadInfer, section "chunked prefill 与 adaptive
+ * head grouping"): a chunk of `chunk` queries at positions
+ * prefix .. prefix + chunk - 1, prefix = n_ctx - chunk, attends causally:
+ *   o[b][j][i] = sum_{t <= prefix + i} softmax_t(scale * q[b][j][i] . k[b][h][t]) v[b][h][t]
+ * with h = floor(j / G).  The cache rows of the chunk itself must already be
+ * in k and v (n_ctx = prefix + chunk rows).  Matrix-core products with fp32
+ * accumulation; the probabilities enter the second product as two 16-bit
+ * terms (about 2^-16 relative each).
+ *   q [batch][n_q_heads][chunk][head_dim]   q_dtype == kv_dtype, bf16 or fp16
+ *   k, v [batch][n_kv_heads][n_ctx][head_dim]
+ *   o [batch][n_q_heads][chunk][head_dim]   fp32, device (written)
+ * Requires 1 <= chunk <= n_ctx, head_dim in {64, 128}, batch * n_q_heads
+ * <= 65535.  No workspace.
+ * ------------------------------------------------------------------------ */
+da_status da_prefill_attention(const da_attn_shape *s, int64_t chunk,
+                               const void *q, const void *k, const void *v,
+                               float *o, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Head-wise streamed decode (HeadInfer).

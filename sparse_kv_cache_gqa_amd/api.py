@@ -230,6 +230,25 @@ def da_decode_attention_topk(q, k, v, top_k, scale=None, token_idx=None, want_id
     return (out, token_idx) if want_idx else out
 
 
+def da_prefill_attention(q, k, v, scale=None, out=None, stream=None):
+    """Chunked prefill: q [B][Hq][C][D] at the last C positions of k, v
+    [B][Hkv][T][D] (causal); fp32 [B][Hq][C][D]."""
+    lib = load()
+    _dev(q, k, v, out)
+    if v.shape != k.shape or v.dtype != k.dtype or q.dtype != k.dtype:
+        raise ValueError("q, k and v must share a dtype; k and v a shape")
+    B, Hq, C, D = q.shape
+    Bk, Hkv, T, Dk = k.shape
+    if (Bk, Dk) != (B, D) or C > T:
+        raise ValueError("q [B][Hq][C][D] needs k, v [B][Hkv][T][D] with T >= C")
+    s = attn_shape(B, Hq, Hkv, D, T, scale, _DT[q.dtype], _DT[k.dtype])
+    _expect(out, q.shape, torch.float32, "out")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    check(lib.da_prefill_attention(ctypes.byref(s), C, _vp(q), _vp(k), _vp(v), _vp(out), _stream(stream)))
+    return out
+
+
 def da_decode_attention_paged(q, k, v, page_idx, page_size, scale=None, split_tokens=0, out=None,
                               ws=None, stream=None):
     """Attention over the tokens of the listed pages only; fp32 [B][H][D]."""

@@ -26,6 +26,7 @@ SOURCES = [
     "csrc/kernels/attn.hip",
     "csrc/kernels/page.hip",
     "csrc/kernels/kv4.hip",
+    "csrc/kernels/prefill.hip",
 ]
 
 ARCH = "gfx950"

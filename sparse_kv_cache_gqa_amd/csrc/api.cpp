@@ -294,6 +294,29 @@ da_status da_decode_attention_topk(const da_attn_shape *s, int32_t top_k, const 
     return ok();
 }
 
+da_status da_prefill_attention(const da_attn_shape *s, int64_t chunk, const void *q, const void *k, const void *v,
+                               float *o, hipStream_t stream) {
+    DA_TRY(check_shape(s, false));
+    if (chunk < 1 || chunk > s->n_ctx)
+        return fail(DA_E_INVALID, "chunk %lld not in [1, n_ctx = %lld]", (long long)chunk, (long long)s->n_ctx);
+    if (s->q_dtype != s->kv_dtype || (s->kv_dtype != DA_BF16 && s->kv_dtype != DA_F16))
+        return fail(DA_E_UNSUPPORTED, "prefill needs q and kv both bf16 or both fp16");
+    if (!prefill_supported(s->kv_dtype, s->head_dim))
+        return fail(DA_E_UNSUPPORTED, "head_dim %d not supported", s->head_dim);
+    if (s->n_ctx * (int64_t)s->head_dim * 2 > 0xFFFFFFFFll || chunk * (int64_t)s->head_dim * 2 > 0xFFFFFFFFll)
+        return fail(DA_E_UNSUPPORTED, "one head's rows exceed 4 GiB");
+    if ((int64_t)s->batch * s->n_q_heads > 65535) return fail(DA_E_UNSUPPORTED, "batch * n_q_heads > 65535");
+    if (s->batch == 0) return ok();
+    DA_TRY(check_ptr(q, "q"));
+    DA_TRY(check_ptr(k, "k"));
+    DA_TRY(check_ptr(v, "v"));
+    DA_TRY(check_ptr(o, "o"));
+    hipError_t e = launch_prefill(s->kv_dtype, s->batch, s->n_q_heads, s->n_kv_heads, s->head_dim, chunk, s->n_ctx,
+                                  s->scale * 1.4426950408889634f, q, k, v, o, stream);
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return ok();
+}
+
 size_t da_decode_attention_paged_workspace(const da_attn_shape *s, int32_t page_size, int32_t top_k) {
     if (check_shape(s, false) != DA_OK || check_page(page_size) != DA_OK) return 0;
     if (top_k < 1 || top_k > n_pages(s, page_size)) return 0;

@@ -99,6 +99,13 @@ hipError_t launch_topk_attention(int kv_fmt, int q_fmt, int64_t BH, int64_t N, i
                                  float scale_log2, const void *q, const void *k, const void *v, float *o,
                                  int32_t *token_idx, hipStream_t stream);
 
+// Chunked prefill attention: q [B][Hq][C][D], k/v [B][Hkv][T][D] (T = prefix
+// + C), o [B][Hq][C][D] fp32; q, k and v in `fmt` (bf16 or fp16).
+bool prefill_supported(int fmt, int D);
+hipError_t launch_prefill(int fmt, int64_t B, int32_t Hq, int32_t Hkv, int D, int64_t C, int64_t T,
+                          float scale_log2, const void *q, const void *k, const void *v, float *o,
+                          hipStream_t stream);
+
 // uint4 group quantization.
 hipError_t launch_quantize_kv4(int64_t n_groups, const void *x, uint8_t *codes,
                                void *gmin, void *gscale, hipStream_t stream);

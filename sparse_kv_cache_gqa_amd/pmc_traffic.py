@@ -34,7 +34,7 @@ KERNELS = {                    # short name -> substring of the mangled kernel n
 
 def source_hash() -> str:
     h = hashlib.sha256()
-    for rel in ("csrc/kernels/attn.hip", "csrc/kernels/page.hip", "csrc/kernels/kv4.hip",
+    for rel in ("csrc/kernels/attn.hip", "csrc/kernels/page.hip", "csrc/kernels/kv4.hip", "csrc/kernels/prefill.hip",
                 "csrc/kernels/common.h", "csrc/internal.h"):
         with open(os.path.join(PKG, rel), "rb") as f:
             h.update(f.read())

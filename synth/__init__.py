@@ -208,6 +208,35 @@ def workload4(rows=None) -> DenseCase:
 
 
 # ----------------------------------------------------------------------------
+# chunked prefill inputs
+# ----------------------------------------------------------------------------
+@dataclass
+class PrefillCase:
+    q: np.ndarray          # [B][Hq][C][D], positions prefix .. prefix + C - 1
+    k: np.ndarray          # [B][Hkv][prefix + C][D]
+    v: np.ndarray
+    dtype: str
+    prefix: int
+    scale: float
+
+
+def prefill_case(tag, B, Hq, Hkv, C, prefix, D, dtype="bf16") -> PrefillCase:
+    """i.i.d. N(0,1) q, K, V.  q <- [42, *tag, 0]; K <- [42, *tag, 1];
+    V <- [42, *tag, 2]."""
+    tag = list(tag) if isinstance(tag, (list, tuple)) else [tag]
+    q = _normal([SEED, *tag, 0], (B, Hq, C, D), dtype)
+    k = _normal([SEED, *tag, 1], (B, Hkv, prefix + C, D), dtype)
+    v = _normal([SEED, *tag, 2], (B, Hkv, prefix + C, D), dtype)
+    return PrefillCase(q=q, k=k, v=v, dtype=dtype, prefix=prefix, scale=1.0 / np.sqrt(D))
+
+
+def workload6() -> PrefillCase:
+    """HeadInfer chunked prefill on Llama-3-8B attention: the fourth 10K-token
+    chunk (prefix 30720), 32 query / 8 KV heads, D 128, bf16."""
+    return prefill_case(6, 1, 32, 8, 10240, 30720, 128, "bf16")
+
+
+# ----------------------------------------------------------------------------
 # head-wise streamed inputs
 # ----------------------------------------------------------------------------
 @dataclass

@@ -171,6 +171,16 @@ def test_topk_attention_checks(lib):
                                         NULL) == L.DA_E_INVALID
 
 
+def test_prefill_checks(lib):
+    s = shape(batch=1, n_ctx=4096, q_dtype=L.DA_BF16, kv_dtype=L.DA_BF16)
+    pre = lambda sh, c: lib.da_prefill_attention(ctypes.byref(sh), c, FAKE, FAKE, FAKE, FAKE, NULL)
+    assert pre(s, 0) == L.DA_E_INVALID
+    assert pre(s, 4097) == L.DA_E_INVALID
+    assert pre(shape(batch=1, n_ctx=4096), 128) == L.DA_E_UNSUPPORTED                 # fp32 q
+    assert pre(shape(batch=1, n_ctx=4096, q_dtype=L.DA_F16, kv_dtype=L.DA_BF16), 128) == L.DA_E_UNSUPPORTED
+    assert lib.da_prefill_attention(ctypes.byref(s), 128, FAKE, FAKE, FAKE, NULL, NULL) == L.DA_E_INVALID
+
+
 def test_kv4_checks(lib):
     q = lambda **kw: lib.da_quantize_kv4(kw.get("n", 4), kw.get("r", 128), FAKE, FAKE, FAKE, FAKE,
                                           NULL)
