@@ -31,7 +31,6 @@ using namespace dev;
 
 constexpr int kPreQ = 128;          // queries per workgroup
 constexpr int kPreKeys = 64;        // keys per tile
-constexpr int kPreThreads = 256;
 
 template <int F>
 __device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
@@ -43,16 +42,31 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f3
                                                       0, 0, 0);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats rounded (nearest, ties to even) to the 16-bit type, packed low
+// then high; bf16 uses the packed hardware conversion.
 template <int F>
-__device__ __forceinline__ uint32_t to16(float x) {
-    if constexpr (F == FMT_BF16) return f32_to_bf16(x);
-    else return f32_to_f16(x);
+__device__ __forceinline__ uint32_t pack16(float a, float b) {
+    if constexpr (F == FMT_BF16) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+    } else {
+        return f32_to_f16(a) | (f32_to_f16(b) << 16);
+    }
 }
 template <int F>
-__device__ __forceinline__ float from16(uint32_t b) {
-    if constexpr (F == FMT_BF16) return bf16_to_f32(b);
-    else return f16_to_f32(b);
+__device__ __forceinline__ float lo16(uint32_t w) {
+    if constexpr (F == FMT_BF16) return __uint_as_float(w << 16);
+    else return f16_to_f32(w & 0xFFFFu);
 }
+template <int F>
+__device__ __forceinline__ float hi16(uint32_t w) {
+    if constexpr (F == FMT_BF16) return __uint_as_float(w & 0xFFFF0000u);
+    else return f16_to_f32(w >> 16);
+}
+
+constexpr float kLazy = 8.f;        // log2 headroom before the running max is raised
 
 struct PrefillArgs {
     const void *q;          // [B][Hq][C][D]
@@ -63,15 +77,23 @@ struct PrefillArgs {
     float scale_log2;
 };
 
-template <int F, int D>
-__global__ __launch_bounds__(kPreThreads) void prefill_kernel(PrefillArgs a) {
+// QB blocks of 16 queries per wave; kPreQ / (16 QB) waves per workgroup.
+template <int QB>
+constexpr int pre_threads() { return 64 * (kPreQ / (16 * QB)); }
+
+template <int F, int D, int QB>
+__global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs a) {
+    constexpr int kPreThreads = pre_threads<QB>();
     constexpr int KSTR = D + 8;                 // K tile row stride (elements)
-    constexpr int VSTR = kPreKeys + 8;          // V^T row stride (elements)
+    constexpr int VSTR = kPreKeys + 4;          // V^T row stride (elements; 8-byte rows for the reads)
     constexpr int NKS = D / 32;                 // 32-channel steps of S
     constexpr int NCB = D / 16;                 // 16-channel blocks of O
     constexpr int CPR = D / 8;                  // 16-byte chunks per row
     constexpr int NLD = kPreKeys * CPR / kPreThreads;   // chunks per thread per tile
     static_assert(NLD * kPreThreads == kPreKeys * CPR, "tile split");
+    constexpr int NVA = kPreKeys / 2 * CPR;                        // V (key pair, chunk) assignments
+    constexpr int NV = NVA >= kPreThreads ? NVA / kPreThreads : 1; // per thread
+    static_assert(NVA % kPreThreads == 0 || NVA < kPreThreads, "V split");
 
     __shared__ uint16_t k_lds[kPreKeys * KSTR];
     __shared__ uint16_t vt_lds[D * VSTR];
@@ -83,7 +105,7 @@ __global__ __launch_bounds__(kPreThreads) void prefill_kernel(PrefillArgs a) {
     const int64_t b = bh / a.Hq, hq = bh - b * a.Hq;
     const int64_t hkv = hq / a.G;
     const int64_t q0 = (int64_t)blockIdx.x * kPreQ;     // first query of the workgroup (chunk-relative)
-    const int64_t qw = q0 + wave * 32;                  // first query of this wave
+    const int64_t qw = q0 + wave * 16 * QB;             // first query of this wave
 
     const uint8_t *kbase = (const uint8_t *)a.k + (b * (a.Hq / a.G) + hkv) * a.T * D * 2;
     const uint8_t *vbase = (const uint8_t *)a.v + (b * (a.Hq / a.G) + hkv) * a.T * D * 2;
@@ -96,28 +118,40 @@ __global__ __launch_bounds__(kPreThreads) void prefill_kernel(PrefillArgs a) {
     const int ntiles = (int)((kend + kPreKeys - 1) / kPreKeys);
 
     // ---- Q^T operands (B of S^T): query qw + 16 qb + n, channels 32 ks + 8 g ..
-    u32x4 Qb[2][NKS];
+    u32x4 Qb[QB][NKS];
     {
         const uint8_t *qbase = (const uint8_t *)a.q + bh * a.C * D * 2;
         const uint32_t q_bytes = (uint32_t)(a.C * D * 2);
         const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qbase, q_bytes);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
                 Qb[qb][ks] = buf_load16(qrs, (uint32_t)((qw + 16 * qb + n) * D + 32 * ks + 8 * g) * 2);
     }
 
-    // ---- staging of one K/V tile: thread chunks c = tid + 256 j -> (key, 8 channels)
-    u32x4 kreg[NLD], vreg[NLD];
+    // ---- staging of one K/V tile ------------------------------------------
+    // K: thread chunk c = tid + 256 j -> (key c / CPR, 8 channels), stored as is.
+    // V: thread (pair c % 32, channel chunk c / 32) loads keys 2 pair and
+    // 2 pair + 1 of one 8-channel chunk and stores each channel's two keys as
+    // one dword of V^T: consecutive lanes write consecutive dwords.
+    u32x4 kreg[NLD], vreg[NV][2];
     auto load_tile = [&](int t) {
+        const int64_t r0 = (int64_t)t * kPreKeys;
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
             const int c = tid + kPreThreads * j;
             const int key = c / CPR, col = (c % CPR) * 8;
-            const uint32_t off = (uint32_t)(((int64_t)t * kPreKeys + key) * D + col) * 2;
-            kreg[j] = buf_load16(krs, off);          // rows past T read as zeros
-            vreg[j] = buf_load16(vrs, off);
+            kreg[j] = buf_load16(krs, (uint32_t)((r0 + key) * D + col) * 2);   // rows past T read as zeros
+        }
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int c = tid + kPreThreads * j;
+            if (c < NVA) {
+                const int pair = c % (kPreKeys / 2), col = (c / (kPreKeys / 2)) * 8;
+                vreg[j][0] = buf_load16(vrs, (uint32_t)((r0 + 2 * pair) * D + col) * 2);
+                vreg[j][1] = buf_load16(vrs, (uint32_t)((r0 + 2 * pair + 1) * D + col) * 2);
+            }
         }
     };
     auto store_tile = [&]() {
@@ -126,20 +160,31 @@ __global__ __launch_bounds__(kPreThreads) void prefill_kernel(PrefillArgs a) {
             const int c = tid + kPreThreads * j;
             const int key = c / CPR, col = (c % CPR) * 8;
             *(u32x4 *)&k_lds[key * KSTR + col] = kreg[j];
+        }
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int c = tid + kPreThreads * j;
+            if (c >= NVA) continue;
+            const int pair = c % (kPreKeys / 2), col = (c / (kPreKeys / 2)) * 8;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                vt_lds[(col + 2 * e) * VSTR + key] = (uint16_t)(vreg[j][e] & 0xFFFFu);
-                vt_lds[(col + 2 * e + 1) * VSTR + key] = (uint16_t)(vreg[j][e] >> 16);
+                const uint32_t a0 = vreg[j][0][e], a1 = vreg[j][1][e];
+                *(uint32_t *)&vt_lds[(col + 2 * e) * VSTR + 2 * pair] = (a0 & 0xFFFFu) | (a1 << 16);
+                *(uint32_t *)&vt_lds[(col + 2 * e + 1) * VSTR + 2 * pair] = (a0 >> 16) | (a1 & 0xFFFF0000u);
             }
         }
     };
 
     // ---- running state per query (lane n of each block) ---------------------
-    float m_run[2] = {neg_inf(), neg_inf()};
-    float l_run[2] = {0.f, 0.f};                  // this lane's keys only; summed over g at the end
-    f32x4 acc[2][NCB];
+    float m_run[QB], l_run[QB];                   // l: this lane's keys only; summed over g at the end
+    f32x4 acc[QB][NCB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb) {
+        m_run[qb] = neg_inf();
+        l_run[qb] = 0.f;
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) acc[qb][cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
@@ -153,9 +198,9 @@ __global__ __launch_bounds__(kPreThreads) void prefill_kernel(PrefillArgs a) {
 
         const int64_t t0 = (int64_t)t * kPreKeys;
         // S^T blocks: keys 16 kb + 4 g + i of this tile, query n of block qb
-        f32x4 st[2][4];
+        f32x4 st[QB][4];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) st[qb][kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -164,55 +209,69 @@ __global__ __launch_bounds__(kPreThreads) void prefill_kernel(PrefillArgs a) {
             for (int ks = 0; ks < NKS; ++ks) {
                 const u32x4 ka = *(const u32x4 *)&k_lds[(16 * kb + n) * KSTR + 32 * ks + 8 * g];
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) st[qb][kb] = mfma16<F>(ka, Qb[qb][ks], st[qb][kb]);
+                for (int qb = 0; qb < QB; ++qb) st[qb][kb] = mfma16<F>(ka, Qb[qb][ks], st[qb][kb]);
             }
 
-        // online softmax per query; build P^T operands (hi and lo terms)
-        u32x4 ph[2][2], pl[2][2];                     // [qb][32-key step]
+        // online softmax per query; build P^T operands (hi and lo terms).
+        // The causal mask only matters on tiles that reach past the wave's
+        // first query (a wave-uniform test).  The running max is raised
+        // lazily: only when some query of the wave sees a score more than
+        // kLazy above its current max are that wave's accumulators rescaled;
+        // otherwise p = 2^(s - m) may reach 2^kLazy, which fp32 sums and the
+        // two 16-bit terms carry without loss.
+        const bool diag = t0 + kPreKeys - 1 > a.prefix + qw;
+        u32x4 ph[QB][2], pl[QB][2];                   // [qb][32-key step]
+        float mx[QB];                                 // raw (unscaled) tile max per query
+        bool up = false;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const int64_t qpos = a.prefix + qw + 16 * qb + n;
-            float s[4][4];
-            float mx = neg_inf();
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t kpos = t0 + 16 * kb + 4 * g + i;
-                    s[kb][i] = (kpos <= qpos) ? st[qb][kb][i] * sl2 : neg_inf();
-                    mx = fmaxf(mx, s[kb][i]);
-                }
-            mx = fmaxf(mx, shfl_xor(mx, 16));
-            mx = fmaxf(mx, shfl_xor(mx, 32));
-            const float mnew = fmaxf(m_run[qb], mx);
-            const float alpha = (mnew == m_run[qb]) ? 1.f : fast_exp2(m_run[qb] - mnew);
-            m_run[qb] = mnew;
-            float lsum = 0.f;
-            uint32_t hb[4][4], lb[4][4];
+        for (int qb = 0; qb < QB; ++qb) {
+            const int rel = (int)(a.prefix + qw - t0) + 16 * qb + n - 4 * g;   // qpos - (t0 + 4 g)
+            float m = neg_inf();
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float p = (s[kb][i] == neg_inf()) ? 0.f : fast_exp2(s[kb][i] - mnew);
-                    lsum += p;
-                    const uint32_t h = to16<F>(p);
-                    hb[kb][i] = h;
-                    lb[kb][i] = to16<F>(p - from16<F>(h));
+                    if (diag && 16 * kb + i > rel) st[qb][kb][i] = neg_inf();
+                    m = fmaxf(m, st[qb][kb][i]);
                 }
-            l_run[qb] = l_run[qb] * alpha + lsum;
-            if (alpha != 1.f) {
+            m = fmaxf(m, shfl_xor(m, 16));
+            mx[qb] = fmaxf(m, shfl_xor(m, 32));
+            up |= mx[qb] * sl2 > m_run[qb] + kLazy;
+        }
+        if (__builtin_amdgcn_ballot_w64(up) != 0) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const float mnew = fmaxf(m_run[qb], mx[qb] * sl2);
+                const float alpha = (mnew == m_run[qb]) ? 1.f : fast_exp2(m_run[qb] - mnew);
+                m_run[qb] = mnew;
+                l_run[qb] *= alpha;
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) acc[qb][cb] *= alpha;
             }
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float nm = -m_run[qb];
+            float lsum = 0.f;
+            uint32_t hw[4][2], lw[4][2];                  // [kb][pair of keys]
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int i2 = 0; i2 < 2; ++i2) {
+                    // 2^(s scale log2e - m); a masked s = -inf gives 0
+                    const float p0 = fast_exp2(fmaf(st[qb][kb][2 * i2], sl2, nm));
+                    const float p1 = fast_exp2(fmaf(st[qb][kb][2 * i2 + 1], sl2, nm));
+                    lsum += p0 + p1;
+                    const uint32_t h = pack16<F>(p0, p1);
+                    hw[kb][i2] = h;
+                    lw[kb][i2] = pack16<F>(p0 - lo16<F>(h), p1 - hi16<F>(h));
+                }
+            l_run[qb] += lsum;
             // step s2 covers keys 32 s2 .. 32 s2 + 31: slots 0-3 <- block 2 s2, 4-7 <- block 2 s2 + 1
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                ph[qb][s2] = (u32x4){hb[2 * s2][0] | (hb[2 * s2][1] << 16), hb[2 * s2][2] | (hb[2 * s2][3] << 16),
-                                     hb[2 * s2 + 1][0] | (hb[2 * s2 + 1][1] << 16),
-                                     hb[2 * s2 + 1][2] | (hb[2 * s2 + 1][3] << 16)};
-                pl[qb][s2] = (u32x4){lb[2 * s2][0] | (lb[2 * s2][1] << 16), lb[2 * s2][2] | (lb[2 * s2][3] << 16),
-                                     lb[2 * s2 + 1][0] | (lb[2 * s2 + 1][1] << 16),
-                                     lb[2 * s2 + 1][2] | (lb[2 * s2 + 1][3] << 16)};
+                ph[qb][s2] = (u32x4){hw[2 * s2][0], hw[2 * s2][1], hw[2 * s2 + 1][0], hw[2 * s2 + 1][1]};
+                pl[qb][s2] = (u32x4){lw[2 * s2][0], lw[2 * s2][1], lw[2 * s2 + 1][0], lw[2 * s2 + 1][1]};
             }
         }
 
@@ -226,7 +285,7 @@ __global__ __launch_bounds__(kPreThreads) void prefill_kernel(PrefillArgs a) {
                 const uint2 hi4 = *(const uint2 *)(vr + 16);    // keys 32 s2 + 16 + 4 g .. + 3
                 const u32x4 va = (u32x4){lo4.x, lo4.y, hi4.x, hi4.y};
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
+                for (int qb = 0; qb < QB; ++qb) {
                     acc[qb][cb] = mfma16<F>(va, ph[qb][s2], acc[qb][cb]);
                     acc[qb][cb] = mfma16<F>(va, pl[qb][s2], acc[qb][cb]);
                 }
@@ -235,7 +294,7 @@ __global__ __launch_bounds__(kPreThreads) void prefill_kernel(PrefillArgs a) {
 
     // ---- normalise and store: lane holds channels 16 cb + 4 g .. + 3 of query n
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
         float l = l_run[qb];
         l += shfl_xor(l, 16);
         l += shfl_xor(l, 32);
@@ -256,9 +315,13 @@ __global__ __launch_bounds__(kPreThreads) void prefill_kernel(PrefillArgs a) {
 
 using PrefillFn = void (*)(PrefillArgs);
 
+constexpr int kPreQB = 1;           // query blocks per wave (measured on MI355X)
+
 PrefillFn prefill_pick(int fmt, int D) {
-    if (fmt == FMT_BF16) return D == 64 ? prefill_kernel<FMT_BF16, 64> : (D == 128 ? prefill_kernel<FMT_BF16, 128> : nullptr);
-    if (fmt == FMT_F16) return D == 64 ? prefill_kernel<FMT_F16, 64> : (D == 128 ? prefill_kernel<FMT_F16, 128> : nullptr);
+    if (fmt == FMT_BF16)
+        return D == 64 ? prefill_kernel<FMT_BF16, 64, kPreQB> : (D == 128 ? prefill_kernel<FMT_BF16, 128, kPreQB> : nullptr);
+    if (fmt == FMT_F16)
+        return D == 64 ? prefill_kernel<FMT_F16, 64, kPreQB> : (D == 128 ? prefill_kernel<FMT_F16, 128, kPreQB> : nullptr);
     return nullptr;
 }
 
@@ -283,7 +346,7 @@ hipError_t launch_prefill(int fmt, int64_t B, int32_t Hq, int32_t Hkv, int D, in
     a.scale_log2 = scale_log2;
     const int64_t qblocks = (C + kPreQ - 1) / kPreQ;
     if (qblocks > 0x7FFFFFFF || B * Hq > 65535) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3((unsigned)qblocks, (unsigned)(B * Hq)), dim3(kPreThreads), 0, stream, a);
+    hipLaunchKernelGGL(fn, dim3((unsigned)qblocks, (unsigned)(B * Hq)), dim3(pre_threads<kPreQB>()), 0, stream, a);
     return hipGetLastError();
 }
 
