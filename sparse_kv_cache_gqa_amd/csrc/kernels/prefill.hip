@@ -29,7 +29,7 @@ namespace {
 
 using namespace dev;
 
-constexpr int kPreQ = 128;          // queries per workgroup
+constexpr int kPreQ = 256;          // queries per workgroup
 constexpr int kPreKeys = 64;        // keys per tile
 
 template <int F>
@@ -75,7 +75,11 @@ struct PrefillArgs {
     int32_t Hq, G;
     int64_t C, T, prefix;
     float scale_log2;
+    int32_t nqb;            // query blocks per head
+    int32_t xcd_map;        // 1: workgroups of one KV head share an XCD (see below)
 };
+
+constexpr int kXcds = 8;    // MI355X: 8 accelerator dies; workgroup i starts on die i mod 8
 
 // QB blocks of 16 queries per wave; kPreQ / (16 QB) waves per workgroup.
 template <int QB>
@@ -88,9 +92,12 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
     constexpr int VSTR = kPreKeys + 4;          // V^T row stride (elements; 8-byte rows for the reads)
     constexpr int NKS = D / 32;                 // 32-channel steps of S
     constexpr int NCB = D / 16;                 // 16-channel blocks of O
+    constexpr int NKB = kPreKeys / 16;          // 16-key blocks of a tile
+    constexpr int NS2 = kPreKeys / 32;          // 32-key steps of a tile
     constexpr int CPR = D / 8;                  // 16-byte chunks per row
-    constexpr int NLD = kPreKeys * CPR / kPreThreads;   // chunks per thread per tile
-    static_assert(NLD * kPreThreads == kPreKeys * CPR, "tile split");
+    constexpr int NKA = kPreKeys * CPR;                            // K (key, chunk) assignments
+    constexpr int NLD = NKA >= kPreThreads ? NKA / kPreThreads : 1; // per thread
+    static_assert(NKA % kPreThreads == 0 || NKA < kPreThreads, "K split");
     constexpr int NVA = kPreKeys / 2 * CPR;                        // V (key pair, chunk) assignments
     constexpr int NV = NVA >= kPreThreads ? NVA / kPreThreads : 1; // per thread
     static_assert(NVA % kPreThreads == 0 || NVA < kPreThreads, "V split");
@@ -101,10 +108,30 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, n = lane & 15;
-    const int64_t bh = blockIdx.y;                      // b * Hq + hq
+    // Workgroup -> (batch row, query head, query block).  With xcd_map, the
+    // workgroups of one (batch row, KV head) all sit on one die, so its L2
+    // serves their shared K/V tiles: die = unit mod 8; inside a unit the G
+    // query heads of one query block are consecutive (they read the same
+    // tiles at the same time) and the blocks run latest first (the longest
+    // first, for a shorter tail).  Otherwise: x = query block, y = b * Hq + hq.
+    int64_t bh, qblk;
+    if (a.xcd_map) {
+        const int64_t L = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+        const int64_t per_unit = (int64_t)a.G * a.nqb;
+        const int64_t kk = L / kXcds;
+        const int64_t unit = (L % kXcds) + kXcds * (kk / per_unit);   // b * Hkv + hkv
+        const int64_t r = kk % per_unit;
+        const int64_t Hkv = a.Hq / a.G;
+        const int64_t ub = unit / Hkv, uh = unit - ub * Hkv;
+        bh = ub * a.Hq + uh * a.G + r % a.G;
+        qblk = a.nqb - 1 - r / a.G;
+    } else {
+        bh = blockIdx.y;
+        qblk = blockIdx.x;
+    }
     const int64_t b = bh / a.Hq, hq = bh - b * a.Hq;
     const int64_t hkv = hq / a.G;
-    const int64_t q0 = (int64_t)blockIdx.x * kPreQ;     // first query of the workgroup (chunk-relative)
+    const int64_t q0 = qblk * kPreQ;                    // first query of the workgroup (chunk-relative)
     const int64_t qw = q0 + wave * 16 * QB;             // first query of this wave
 
     const uint8_t *kbase = (const uint8_t *)a.k + (b * (a.Hq / a.G) + hkv) * a.T * D * 2;
@@ -141,8 +168,10 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
             const int c = tid + kPreThreads * j;
-            const int key = c / CPR, col = (c % CPR) * 8;
-            kreg[j] = buf_load16(krs, (uint32_t)((r0 + key) * D + col) * 2);   // rows past T read as zeros
+            if (c < NKA) {
+                const int key = c / CPR, col = (c % CPR) * 8;
+                kreg[j] = buf_load16(krs, (uint32_t)((r0 + key) * D + col) * 2);   // rows past T read as zeros
+            }
         }
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
@@ -158,6 +187,7 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
             const int c = tid + kPreThreads * j;
+            if (c >= NKA) continue;
             const int key = c / CPR, col = (c % CPR) * 8;
             *(u32x4 *)&k_lds[key * KSTR + col] = kreg[j];
         }
@@ -198,13 +228,13 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
 
         const int64_t t0 = (int64_t)t * kPreKeys;
         // S^T blocks: keys 16 kb + 4 g + i of this tile, query n of block qb
-        f32x4 st[QB][4];
+        f32x4 st[QB][NKB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) st[qb][kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            for (int kb = 0; kb < NKB; ++kb) st[qb][kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const u32x4 ka = *(const u32x4 *)&k_lds[(16 * kb + n) * KSTR + 32 * ks + 8 * g];
@@ -220,7 +250,7 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
         // otherwise p = 2^(s - m) may reach 2^kLazy, which fp32 sums and the
         // two 16-bit terms carry without loss.
         const bool diag = t0 + kPreKeys - 1 > a.prefix + qw;
-        u32x4 ph[QB][2], pl[QB][2];                   // [qb][32-key step]
+        u32x4 ph[QB][NS2], pl[QB][NS2];               // [qb][32-key step]
         float mx[QB];                                 // raw (unscaled) tile max per query
         bool up = false;
 #pragma unroll
@@ -228,7 +258,7 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
             const int rel = (int)(a.prefix + qw - t0) + 16 * qb + n - 4 * g;   // qpos - (t0 + 4 g)
             float m = neg_inf();
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     if (diag && 16 * kb + i > rel) st[qb][kb][i] = neg_inf();
@@ -253,9 +283,9 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
         for (int qb = 0; qb < QB; ++qb) {
             const float nm = -m_run[qb];
             float lsum = 0.f;
-            uint32_t hw[4][2], lw[4][2];                  // [kb][pair of keys]
+            uint32_t hw[NKB][2], lw[NKB][2];              // [kb][pair of keys]
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int i2 = 0; i2 < 2; ++i2) {
                     // 2^(s scale log2e - m); a masked s = -inf gives 0
@@ -269,7 +299,7 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
             l_run[qb] += lsum;
             // step s2 covers keys 32 s2 .. 32 s2 + 31: slots 0-3 <- block 2 s2, 4-7 <- block 2 s2 + 1
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
+            for (int s2 = 0; s2 < NS2; ++s2) {
                 ph[qb][s2] = (u32x4){hw[2 * s2][0], hw[2 * s2][1], hw[2 * s2 + 1][0], hw[2 * s2 + 1][1]};
                 pl[qb][s2] = (u32x4){lw[2 * s2][0], lw[2 * s2][1], lw[2 * s2 + 1][0], lw[2 * s2 + 1][1]};
             }
@@ -279,7 +309,7 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
+            for (int s2 = 0; s2 < NS2; ++s2) {
                 const uint16_t *vr = &vt_lds[(16 * cb + n) * VSTR + 32 * s2 + 4 * g];
                 const uint2 lo4 = *(const uint2 *)vr;           // keys 32 s2 + 4 g .. + 3
                 const uint2 hi4 = *(const uint2 *)(vr + 16);    // keys 32 s2 + 16 + 4 g .. + 3
@@ -346,6 +376,8 @@ hipError_t launch_prefill(int fmt, int64_t B, int32_t Hq, int32_t Hkv, int D, in
     a.scale_log2 = scale_log2;
     const int64_t qblocks = (C + kPreQ - 1) / kPreQ;
     if (qblocks > 0x7FFFFFFF || B * Hq > 65535) return hipErrorInvalidValue;
+    a.nqb = (int32_t)qblocks;
+    a.xcd_map = (B * Hkv) % kXcds == 0;
     hipLaunchKernelGGL(fn, dim3((unsigned)qblocks, (unsigned)(B * Hq)), dim3(pre_threads<kPreQB>()), 0, stream, a);
     return hipGetLastError();
 }

@@ -38,6 +38,7 @@ CASES = [
     (1, 8, 8, 257, 1000, 128, "bf16"),    # MHA, longer prefix
     (1, 4, 1, 1, 500, 128, "bf16"),       # a single query: decode over 501 tokens
     (1, 2, 1, 64, 0, 128, "f16"),
+    (2, 8, 4, 600, 100, 64, "bf16"),      # 8 (batch, KV head) units: one die each
 ]
 
 
