@@ -7,10 +7,12 @@
 // Unlike decode this is a dense contraction with reuse (each K/V tile serves
 // 128 queries), so both products run on the matrix cores:
 //
-//   * One 256-thread workgroup per (b, query head, 128 queries); wave w owns
-//     queries 32w .. 32w + 31 (two blocks of 16).  K/V tiles of 64 keys are
-//     staged in LDS, V transposed while it is stored; the next tile's global
-//     loads are issued before the current tile is computed.
+//   * One 1024-thread workgroup per (b, query head, 256 queries); wave w owns
+//     queries 16w .. 16w + 15.  K/V tiles of 64 keys are staged in LDS, V
+//     transposed while it is stored (two keys per dword, so consecutive lanes
+//     write consecutive words); the next tile's global loads are issued
+//     before the current tile is computed.  The workgroups of one (b, KV
+//     head) share a die (its L2 holds their K/V tiles), latest blocks first.
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_{bf16,f16}: A = 16 keys of the K
 //     tile (LDS), B = 16 queries (registers, loaded once).  In the output
 //     layout a lane holds 4 keys of one query, so the softmax is per lane
@@ -21,7 +23,9 @@
 //     4g .. 4g + 3 of the two 16-key halves of a 32-key step; the V^T reads
 //     use the same key order).  P is split into two 16-bit terms (hi + lo),
 //     so the product is accurate to about 2^-16 of each weight.
-//   * Online softmax in base 2 per query; rows past the causal limit get -inf.
+//   * Online softmax in base 2 per query, the scale folded into the exp2
+//     argument; rows past the causal limit get -inf (only on tiles that reach
+//     the diagonal); the running max is raised lazily (see below).
 #include "common.h"
 
 namespace da {
