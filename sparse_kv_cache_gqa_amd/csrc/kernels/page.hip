@@ -5,17 +5,17 @@
 //   and max of the keys (the page's bounding box).  Exact: min/max of values
 //   of the storage type are values of that type.
 //
-// select_kernel: one 1024-thread workgroup per (batch row, head).
+// select_kernel: one workgroup per (batch row, head).
 //   1. Bound score r_j = sum_d (q_d M_{j,d} if q_d >= 0 else q_d m_{j,d}),
-//      written as q+ . M_j + q- . m_j with q+ = max(q, 0), q- = min(q, 0), so
-//      it is a dense contraction: two 16x16x32 MFMAs per 32 channels take 16
-//      pages as the N dimension, loading each page's M and m rows straight
-//      from HBM into the B operand.  Products of 16-bit values are exact in
-//      fp32; q in fp32 is split into 16-bit terms on the A rows.  Scores stay
-//      in LDS (and optionally go to page_score).
+//      written as q+ . M_j + q- . m_j with q+ = max(q, 0), q- = min(q, 0).
+//      The scan reads each page's M and m rows once; it is bound by HBM, so
+//      it runs on the VALU with whole-row loads: every lane owns a 16-byte
+//      piece of a row, accumulates its exact products (fma) and the lanes of
+//      a row add up by shuffles.  Scores stay in LDS (and optionally go to
+//      page_score).
 //      With EXACT the key rows themselves are read once and scored against q
-//      (q . k_i, one MFMA per 32 channels): token-level selection (FlexGen's
-//      top-10% sparse attention, section "方法细节").
+//      (q . k_i): token-level selection (FlexGen's top-10% sparse attention,
+//      section "方法细节").
 //   2. Top-K by a most-significant-digit radix select (4 passes of 8 bits)
 //      over an order-preserving uint32 image of the fp32 scores, one shared
 //      LDS histogram per pass.  Ties at the K-th score go to the lower page
@@ -120,6 +120,10 @@ enum SelMode : int { SEL_PAGES = 0, SEL_TOKENS = 1, SEL_ATTEND = 2 };
 // Threads per workgroup (measured on MI355X): 1024 for pages (P = 2048 at
 // the TinyServe shape), 512 for tokens (P = 1024 at the FlexGen shape).
 constexpr int sel_threads(int mode) { return mode == SEL_PAGES ? 1024 : 512; }
+// 16-byte loads per lane and array in flight per scoring trip (measured on
+// MI355X): 2 for pages (two arrays; more costs the 1024-thread workgroups
+// their second slot per CU), 4 for tokens.
+constexpr int sel_loads(int mode) { return mode == SEL_PAGES ? 2 : 4; }
 
 struct SelArgs {
     int64_t P = 0;                 // pages (or tokens) per (b, h)
@@ -269,9 +273,6 @@ __global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args)
     int32_t *__restrict__ page_idx = args.page_idx;
     float *__restrict__ page_score = args.page_score;
     constexpr int R = D * Elem<KF>::size;
-    constexpr int NCH = R / 64;
-    constexpr int NMF = KF == FMT_F32 ? 4 * NCH : NCH;
-    constexpr int SPL = (KF == FMT_F32 || QF == KF) ? 1 : (KF == FMT_BF16 ? 3 : 2);
 
     extern __shared__ float sc_lds[];              // [P] (SEL_ATTEND: then kept[top_k], w[top_k])
     __shared__ uint32_t hist[256];
@@ -279,115 +280,69 @@ __global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args)
     __shared__ uint32_t pick_digit, pick_need, pick_count;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int g4 = lane >> 4, n16 = lane & 15;
     const int64_t bh = blockIdx.x;
 
-    // A operands: row s holds the s-th split term of q+ (pos) or q- (neg);
-    // EXACT: of q itself (pos only)
-    u32x4 Apos[KF == FMT_F32 ? 1 : NMF], Aneg[KF == FMT_F32 ? 1 : NMF];
-    float Fpos[KF == FMT_F32 ? NMF : 1], Fneg[KF == FMT_F32 ? NMF : 1];
-    {
-        const int s = n16;
-        const bool rowok = s < SPL;
-        const int64_t qoff = bh * D;
+    // ---- 1. scores ----------------------------------------------------------
+    // Lanes own 16-byte pieces of a row: piece = lane mod PCS of row lane / PCS,
+    // so one load instruction covers TPI whole rows (whole 128-byte lines;
+    // measured on MI355X: non-temporal loads of whole lines stream ~15% faster
+    // than the 64-byte halves an MFMA operand layout would need).  Each lane
+    // keeps q+ and q- (EXACT: q) for its EPC channels, sums its exact products
+    // in two fma chains, and the PCS lanes of a row add up by lane shuffles.
+    constexpr int EPC = 16 / Elem<KF>::size;   // channels per piece
+    constexpr int PCS = R / 16;                // pieces per row
+    constexpr int TPI = 64 / PCS;              // rows per load instruction
+    constexpr int NI = sel_loads(MODE);            // load instructions per array per trip
+    constexpr int TPT = NI * TPI;              // rows per trip of one wave
+    static_assert(PCS >= 4 && PCS <= 64, "row layout");
+    const int piece = lane % PCS, rin = lane / PCS;
+    float qp[EPC], qn[EPC];
 #pragma unroll
-        for (int mf = 0; mf < NMF; ++mf) {
-            if constexpr (KF == FMT_F32) {
-                const float x = rowok ? load_scalar<QF>(q, qoff + qk_dim<KF>(mf, g4, 0)) : 0.f;
-                Fpos[mf] = EXACT ? x : fmaxf(x, 0.f);
-                Fneg[mf] = fminf(x, 0.f);
-            } else {
-                uint32_t hp[8], hn[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = rowok ? load_scalar<QF>(q, qoff + qk_dim<KF>(mf, g4, e)) : 0.f;
-                    hp[e] = rowok ? split_term<KF>(EXACT ? x : fmaxf(x, 0.f), s) : 0u;
-                    hn[e] = rowok ? split_term<KF>(fminf(x, 0.f), s) : 0u;
-                }
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    Apos[mf][e2] = hp[2 * e2] | (hp[2 * e2 + 1] << 16);
-                    Aneg[mf][e2] = hn[2 * e2] | (hn[2 * e2 + 1] << 16);
-                }
-            }
-        }
+    for (int e = 0; e < EPC; ++e) {
+        const float x = load_scalar<QF>(q, bh * D + piece * EPC + e);
+        qp[e] = EXACT ? x : fmaxf(x, 0.f);
+        qn[e] = fminf(x, 0.f);
     }
-
-    // ---- 1. bound scores --------------------------------------------------
-    const uint8_t *mxb = kmax + bh * P * R + 16 * g4;
-    const uint8_t *mnb = kmin + bh * P * R + 16 * g4;
-    // token modes: two groups of 16 rows per trip, both groups' loads issued
-    // before either is scored (measured: 162.5 -> 159 us at the FlexGen
-    // shape); page mode keeps one group per trip, since the second group's
-    // registers would cost it half its occupancy (55.7 -> 62.7 us)
-    auto load_group = [&](int64_t base, u32x4 (&Kx)[NCH], u32x4 (&Kn)[NCH]) {
-        const int64_t pg = base + n16;
-        const bool ok = pg < P;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            Kx[c] = ok ? *(const u32x4 *)(mxb + pg * R + 64 * c) : (u32x4){0u, 0u, 0u, 0u};
-            if constexpr (!EXACT) Kn[c] = ok ? *(const u32x4 *)(mnb + pg * R + 64 * c) : (u32x4){0u, 0u, 0u, 0u};
-        }
-    };
-    auto score_group = [&](int64_t base, const u32x4 (&Kx)[NCH], const u32x4 (&Kn)[NCH]) {
-        const int64_t pg = base + n16;
-        f32x4 cc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            if constexpr (KF == FMT_F32) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    cc = __builtin_amdgcn_mfma_f32_16x16x4f32(Fpos[4 * c + e], __uint_as_float(Kx[c][e]), cc, 0, 0, 0);
-                    if constexpr (!EXACT)
-                        cc = __builtin_amdgcn_mfma_f32_16x16x4f32(Fneg[4 * c + e], __uint_as_float(Kn[c][e]), cc, 0, 0, 0);
-                }
-            } else if constexpr (KF == FMT_BF16) {
-                cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Apos[c]),
-                                                             __builtin_bit_cast(bf16x8, Kx[c]), cc, 0, 0, 0);
-                if constexpr (!EXACT)
-                    cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Aneg[c]),
-                                                                 __builtin_bit_cast(bf16x8, Kn[c]), cc, 0, 0, 0);
-            } else {
-                cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, Apos[c]),
-                                                            __builtin_bit_cast(f16x8, Kx[c]), cc, 0, 0, 0);
-                if constexpr (!EXACT)
-                    cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, Aneg[c]),
-                                                                __builtin_bit_cast(f16x8, Kn[c]), cc, 0, 0, 0);
-            }
-        }
-        if (g4 == 0 && pg < P) {
-            float s = 0.f;
-#pragma unroll
-            for (int i = 0; i < SPL; ++i) s += cc[i];
-            if (s == 0.f) s = 0.f;
-            sc_lds[pg] = s;
-            if (page_score) page_score[bh * P + pg] = s;
-        }
-    };
+    // buffer resources over this head's rows: rows at or past P read as zeros
+    const uint32_t head_bytes = (uint32_t)(P * R);
+    const __amdgpu_buffer_rsrc_t mxr = make_rsrc(kmax + bh * P * R, head_bytes);
+    const __amdgpu_buffer_rsrc_t mnr = make_rsrc((EXACT ? kmax : kmin) + bh * P * R, head_bytes);
     {
-        const int64_t step = 16 * kSelWaves;
-        int64_t base = (int64_t)w * 16;
-        u32x4 Xa[NCH], Na[NCH], Xb[NCH], Nb[NCH];
-        if constexpr (EXACT) {
-            for (; base + step < P; base += 2 * step) {
-                load_group(base, Xa, Na);
-                load_group(base + step, Xb, Nb);
-                score_group(base, Xa, Na);
-                score_group(base + step, Xb, Nb);
+        const int64_t step = (int64_t)TPT * kSelWaves;
+        u32x4 X[NI], Nn[NI];
+        for (int64_t base = (int64_t)w * TPT; base < P; base += step) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const uint32_t off = (uint32_t)(base + i * TPI + rin) * R + 16 * piece;
+                X[i] = buf_load16(mxr, off);
+                if constexpr (!EXACT) Nn[i] = buf_load16(mnr, off);
             }
-        } else {
-            for (; base + step < P; base += step) {
-                load_group(base, Xa, Na);
-                score_group(base, Xa, Na);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                float fx[EPC];
+                unpack16<KF>(X[i], fx);
+                float sp = 0.f, sn = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) sp = fmaf(qp[e], fx[e], sp);
+                if constexpr (!EXACT) {
+                    float fn[EPC];
+                    unpack16<KF>(Nn[i], fn);
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) sn = fmaf(qn[e], fn[e], sn);
+                }
+                float s = EXACT ? sp : sp + sn;
+#pragma unroll
+                for (int o = 1; o < PCS; o <<= 1) s += __shfl_xor(s, o, 64);
+                const int64_t row = base + i * TPI + rin;
+                if (piece == 0 && row < P) {
+                    if (s == 0.f) s = 0.f;
+                    sc_lds[row] = s;
+                    if (page_score) page_score[bh * P + row] = s;
+                }
             }
-        }
-        if (base < P) {
-            load_group(base, Xa, Na);
-            score_group(base, Xa, Na);
         }
     }
     __syncthreads();
-
     // ---- 2. radix select of the top_k largest keys -------------------------
     // MSB-first, 8 bits per pass, one shared 256-bin histogram per pass.
     uint32_t prefix = 0, pmask = 0;
