@@ -114,6 +114,42 @@ struct Stage {
     uint32_t mk, sk, mv, sv;
 };
 
+// In-workgroup merge of the n_split (<= waves) partials in `mrg` ([wave][G]
+// [D + 4] fp32) into o.  The operations and their order are those of
+// attn_reduce_kernel for n_split <= 4: max; weights 2^(m_s - M); L = (w0 l0 +
+// w1 l1) + (w2 l2 + w3 l3) (its shuffle tree; adding to a +0 start is exact,
+// the terms are >= 0); O = fma chain over s; o = O / L.
+template <int G, int D>
+__device__ __forceinline__ void merge_in_workgroup(const AttnLaunch &a, const float *mrg, int b, int hkv, int wave,
+                                                   int lane) {
+    constexpr int PSTR = D + 4;
+    __syncthreads();
+    const int ns = a.n_split;
+    const int slot = G * PSTR;
+    float *ob = a.o + (int64_t)b * a.o_bstride + (int64_t)hkv * G * D;
+#pragma unroll 1
+    for (int idx = wave * 64 + lane; idx < G * D; idx += a.wpb * 64) {
+        const int h = idx / D, d = idx - h * D;
+        const float *ps = mrg + h * PSTR;
+        float M = neg_inf();
+#pragma unroll 1
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, ps[s * slot + D]);
+        float L01 = 0.f, L23 = 0.f, O0 = 0.f;
+        const float O1 = 0.f, O2 = 0.f, O3 = 0.f;
+#pragma unroll 1
+        for (int s = 0; s < ns; ++s) {
+            const float m = ps[s * slot + D];
+            const float w = (m == neg_inf()) ? 0.f : fast_exp2(m - M);
+            const float pl = fmaf(w, ps[s * slot + D + 1], 0.f);
+            if (s < 2) L01 += pl;
+            else L23 += pl;
+            O0 = fmaf(w, ps[s * slot + d], O0);
+        }
+        const float L = L01 + L23;
+        ob[h * D + d] = ((O0 + O1) + (O2 + O3)) / L;
+    }
+}
+
 // Each wave reduces one split of one (batch row, KV head) to a partial per
 // query head.  Loads of the next tile are issued before the current tile is
 // computed (two register stages).
@@ -561,38 +597,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     else if (split < a.n_split)
         emit(a.ws + ((int64_t)unit * G * a.n_split + split) * PSTR, (int64_t)a.n_split * PSTR);
 
-    // ---- in-workgroup merge of the n_split (<= waves) partials -------------
-    // The operations and their order are those of attn_reduce_kernel for
-    // n_split <= 4: max; weights 2^(m_s - M); L = (w0 l0 + w1 l1) + (w2 l2 +
-    // w3 l3) (its shuffle tree; adding to a +0 start is exact, the terms are
-    // >= 0); O = fma chain over s; o = O / L.
-    if (fused) {
-        __syncthreads();
-        const int ns = a.n_split;
-        const int slot = G * PSTR;
-        float *ob = a.o + (int64_t)b * a.o_bstride + (int64_t)hkv * G * D;
-#pragma unroll 1
-        for (int idx = wave * 64 + lane; idx < G * D; idx += a.wpb * 64) {
-            const int h = idx / D, d = idx - h * D;
-            const float *ps = mrg_lds + h * PSTR;
-            float M = neg_inf();
-#pragma unroll 1
-            for (int s = 0; s < ns; ++s) M = fmaxf(M, ps[s * slot + D]);
-            float L01 = 0.f, L23 = 0.f, O0 = 0.f;
-            const float O1 = 0.f, O2 = 0.f, O3 = 0.f;
-#pragma unroll 1
-            for (int s = 0; s < ns; ++s) {
-                const float m = ps[s * slot + D];
-                const float w = (m == neg_inf()) ? 0.f : fast_exp2(m - M);
-                const float pl = fmaf(w, ps[s * slot + D + 1], 0.f);
-                if (s < 2) L01 += pl;
-                else L23 += pl;
-                O0 = fmaf(w, ps[s * slot + d], O0);
-            }
-            const float L = L01 + L23;
-            ob[h * D + d] = ((O0 + O1) + (O2 + O3)) / L;
-        }
-    }
+    if (fused) merge_in_workgroup<G, D>(a, mrg_lds, b, hkv, wave, lane);
 }
 
 // Merge of the split partials of one query-head row (one block per row).
@@ -725,13 +730,16 @@ SplitKernel pick_one() {
 
 template <int KF, int QF, int D, bool PAGED>
 SplitKernel pick_g(int G) {
-    if constexpr (PAGED) return G == 1 ? pick_one<KF, QF, D, 1, PAGED>() : SplitKernel{};
-    switch (G) {
-    case 1: return pick_one<KF, QF, D, 1, PAGED>();
-    case 2: return pick_one<KF, QF, D, 2, PAGED>();
-    case 4: return pick_one<KF, QF, D, 4, PAGED>();
-    case 8: return pick_one<KF, QF, D, 8, PAGED>();
-    default: return {};
+    if constexpr (PAGED) {
+        return G == 1 ? pick_one<KF, QF, D, 1, PAGED>() : SplitKernel{};
+    } else {
+        switch (G) {
+        case 1: return pick_one<KF, QF, D, 1, PAGED>();
+        case 2: return pick_one<KF, QF, D, 2, PAGED>();
+        case 4: return pick_one<KF, QF, D, 4, PAGED>();
+        case 8: return pick_one<KF, QF, D, 8, PAGED>();
+        default: return {};
+        }
     }
 }
 
