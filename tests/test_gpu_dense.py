@@ -1,6 +1,6 @@
 """Dense / GQA decode attention on the GPU against the fp64 oracle.
 
-Tolerances: the spec bar is |err| <= 1e-3 absolute on the fp32 output;
+Tolerances: the required bar is |err| <= 1e-3 absolute on the fp32 output;
 on top of it these tests hold max|err| / rms(reference) <= 1e-4 (outputs of
 N(0,1) data are small, rms ~ sqrt(e/N)), and small shapes hold 1e-5 absolute.
 """

@@ -6,7 +6,7 @@ may carry either sign).  Dequantization is bit-exact.  Attention folds the
 dequantization into fp32 arithmetic (min * sum(q) + scale * sum(q * code)),
 which differs from the oracle's fp16-rounded values by at most half an fp16
 ulp (2^-11 relative) per element.  Against the oracle the bar is the
-spec 1e-3 absolute and max|err|/rms <= 3e-3 (random per-element
+required 1e-3 absolute and max|err|/rms <= 3e-3 (random per-element
 differences of up to 2^-11 |x| give a typical output error near
 2^-11 / sqrt(3) of rms, about 3e-4, and a maximum over a head a few times
 that; measured maxima are near 1.3e-3).  A second, tight check compares the
