@@ -689,8 +689,8 @@ def main(argv=None) -> int:
                          "traffic, for scaling hardware byte counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
-                                   "(multi-GPU sharding is a design note only)"}))
+        print(json.dumps({"error": "the library and this benchmark run on one GPU; --gpus must be 1 "
+                                   "(sharding across GPUs is described, not implemented)"}))
         return 2
 
     import numpy as np
