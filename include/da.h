@@ -333,11 +333,15 @@ da_status da_prefill_attention(const da_attn_shape *s, int64_t chunk,
  * da_stream_length / da_stream_set_length, 1 <= len <= cap), copying them
  * into a dense [batch][len][head_dim] buffer; the attention then equals
  * da_decode_attention over those len tokens.
- * da_stream_append: on `stream`, copies the new token's rows
+ * da_stream_append: on `stream`, writes the new token's rows
  *   k_new, v_new [n_layers][batch][n_kv_heads][head_dim] kv_dtype, device,
  * into row len of every host cache (head_dim values per (layer, head, batch
- * row), device to host), then sets len = len + 1 on the host.  Fails with
- * DA_E_INVALID when len == cap.  Give it the copy stream of the next
+ * row)) with one kernel per 32 layer-heads that stores to the page-locked
+ * caches directly, then sets len = len + 1 on the host.  Fails with
+ * DA_E_INVALID when len == cap, and with DA_E_NOT_PINNED (nothing enqueued)
+ * unless every cache is page-locked host memory that the device maps at its
+ * host address (hipHostMalloc).  The rows are in host memory once the
+ * kernels have completed; give it the copy stream of the next
  * da_stream_headwise (or order the streams), so the rows land first.
  * ------------------------------------------------------------------------ */
 typedef struct da_stream_ctx da_stream_ctx;

@@ -27,6 +27,7 @@ SOURCES = [
     "csrc/kernels/page.hip",
     "csrc/kernels/kv4.hip",
     "csrc/kernels/prefill.hip",
+    "csrc/kernels/append.hip",
 ]
 
 ARCH = "gfx950"

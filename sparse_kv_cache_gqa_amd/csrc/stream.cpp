@@ -8,13 +8,15 @@
 // HeadInfer also writes the previous head back device-to-host; a decode step
 // does not change the cached keys and values, so there is nothing to write
 // back and that copy is not issued.  What a step does add is the new token:
-// da_stream_append copies its key and value rows (head_dim values per head
-// and batch row) device-to-host into row `len` of every host cache and
-// extends the attended length.  The host caches hold `cap` rows per batch row
+// da_stream_append writes its key and value rows (head_dim values per head
+// and batch row) into row `len` of every host cache, with a kernel that
+// stores to the page-locked caches directly, and extends the attended
+// length.  The host caches hold `cap` rows per batch row
 // (the n_ctx given at creation); a step streams the first `len` rows of each
 // batch row into a dense [batch][len][head_dim] buffer.
 #include "host.h"
 
+#include <algorithm>
 #include <new>
 
 struct da_stream_ctx {
@@ -41,7 +43,9 @@ da_status check_hpc(const da_attn_shape *s, int32_t hpc) {
     return DA_OK;
 }
 
-da_status check_pinned(const void *p, const char *name, int64_t idx) {
+// Page-locked host memory; with `mapped`, also mapped at the same address on
+// the device.
+da_status check_pinned(const void *p, const char *name, int64_t idx, bool mapped = false) {
     if (!p) return fail(DA_E_INVALID, "%s[%lld] is NULL", name, (long long)idx);
     hipPointerAttribute_t attr;
     hipError_t e = hipPointerGetAttributes(&attr, p);
@@ -52,6 +56,13 @@ da_status check_pinned(const void *p, const char *name, int64_t idx) {
     }
     if (attr.type != hipMemoryTypeHost)
         return fail(DA_E_NOT_PINNED, "%s[%lld] is not page-locked host memory", name, (long long)idx);
+    if (mapped) {
+        // kernels store to such memory at its host address (one virtual
+        // address space for host and device); anything else is refused
+        if (!attr.hostPointer || attr.hostPointer != attr.devicePointer)
+            return fail(DA_E_NOT_PINNED, "%s[%lld] is not mapped at its host address on the device", name,
+                        (long long)idx);
+    }
     return DA_OK;
 }
 
@@ -202,26 +213,30 @@ da_status da_stream_append(da_stream_ctx *c, int32_t n_layers, const void *k_new
     DA_TRY(check_ptr(k_new, "k_new"));
     DA_TRY(check_ptr(v_new, "v_new"));
     const int64_t n_heads = (int64_t)n_layers * s->n_kv_heads;
+    if (n_heads > 0x7FFFFFFF) return fail(DA_E_INVALID, "too many layer-heads");
     for (int64_t i = 0; i < n_heads; ++i) {
-        DA_TRY(check_pinned(k_host[i], "k_host", i));
-        DA_TRY(check_pinned(v_host[i], "v_host", i));
+        DA_TRY(check_pinned(k_host[i], "k_host", i, true));
+        DA_TRY(check_pinned(v_host[i], "v_host", i, true));
     }
-    const size_t es = esize(s->kv_dtype);
-    const size_t row = (size_t)s->head_dim * es;                 // one token of one head
-    const size_t src_pitch = (size_t)s->n_kv_heads * row;        // new rows [L][B][Hkv][D]
-    const size_t dst_pitch = (size_t)s->n_ctx * row;             // host caches [B][cap][D]
+    // the rows go straight into the host caches, kAppendMaxHeads heads per launch
+    const int64_t row = (int64_t)s->head_dim * esize(s->kv_dtype);   // one token of one head
+    AppendArgs a;
+    a.k_new = (const uint8_t *)k_new;
+    a.v_new = (const uint8_t *)v_new;
+    a.Hkv = s->n_kv_heads;
+    a.batch = s->batch;
+    a.row = row;
+    a.dst_off = c->len * row;
+    a.dst_bstride = s->n_ctx * row;
     hipError_t e = hipSuccess;
-    for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
-        for (int h = 0; h < s->n_kv_heads && e == hipSuccess; ++h) {
-            const int64_t hi = (int64_t)l * s->n_kv_heads + h;
-            const size_t src = ((size_t)l * s->batch * s->n_kv_heads + h) * row;
-            const size_t dst = (size_t)c->len * row;
-            e = hipMemcpy2DAsync((char *)k_host[hi] + dst, dst_pitch, (const char *)k_new + src, src_pitch, row,
-                                 (size_t)s->batch, hipMemcpyDeviceToHost, stream);
-            if (e == hipSuccess)
-                e = hipMemcpy2DAsync((char *)v_host[hi] + dst, dst_pitch, (const char *)v_new + src, src_pitch, row,
-                                     (size_t)s->batch, hipMemcpyDeviceToHost, stream);
+    for (int64_t h0 = 0; h0 < n_heads && e == hipSuccess; h0 += kAppendMaxHeads) {
+        a.head0 = (int32_t)h0;
+        a.n_heads = (int32_t)std::min<int64_t>(kAppendMaxHeads, n_heads - h0);
+        for (int i = 0; i < a.n_heads; ++i) {
+            a.k_dst[i] = (uint8_t *)k_host[h0 + i];
+            a.v_dst[i] = (uint8_t *)v_host[h0 + i];
         }
+        e = launch_append(a, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "append");
     c->len += 1;
