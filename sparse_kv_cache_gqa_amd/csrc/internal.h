@@ -106,22 +106,6 @@ hipError_t launch_prefill(int fmt, int64_t B, int32_t Hq, int32_t Hkv, int D, in
                           float scale_log2, const void *q, const void *k, const void *v, float *o,
                           hipStream_t stream);
 
-// Append of one token's K and V rows to host caches (the per-step append of
-// head-wise streaming).  Heads head0 .. head0 + n_heads - 1 (global index
-// l * Hkv + h) of k_new / v_new [L][batch][Hkv][row bytes] go to row `len` of
-// their caches [batch][cap][row bytes], whose device-visible addresses (of
-// page-locked host memory) are k_dst[i] / v_dst[i].
-constexpr int kAppendMaxHeads = 32;
-struct AppendArgs {
-    const uint8_t *k_new = nullptr, *v_new = nullptr;
-    uint8_t *k_dst[kAppendMaxHeads] = {}, *v_dst[kAppendMaxHeads] = {};
-    int32_t head0 = 0, n_heads = 0, Hkv = 0, batch = 0;
-    int64_t row = 0;            // bytes per row, a multiple of 16, <= 1024
-    int64_t dst_off = 0;        // len * row
-    int64_t dst_bstride = 0;    // cap * row
-};
-hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
-
 // uint4 group quantization.
 hipError_t launch_quantize_kv4(int64_t n_groups, const void *x, uint8_t *codes,
                                void *gmin, void *gscale, hipStream_t stream);

@@ -7,6 +7,7 @@
 // of the head's page-locked host cache, through the cache's device-visible
 // address: one launch covers up to kAppendMaxHeads heads, instead of one
 // small device-to-host copy per (head, K or V).
+#include "append.h"
 #include "common.h"
 
 namespace da {

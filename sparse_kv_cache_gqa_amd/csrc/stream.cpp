@@ -15,6 +15,7 @@
 // (the n_ctx given at creation); a step streams the first `len` rows of each
 // batch row into a dense [batch][len][head_dim] buffer.
 #include "host.h"
+#include "append.h"
 
 #include <algorithm>
 #include <new>
