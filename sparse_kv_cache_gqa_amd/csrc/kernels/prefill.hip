@@ -7,14 +7,15 @@
 // Unlike decode this is a dense contraction with reuse (each K/V tile serves
 // 128 queries), so both products run on the matrix cores:
 //
-//   * One 1024-thread workgroup per (b, query head, 256 queries); wave w owns
-//     queries 16w .. 16w + 15.  K/V tiles of 64 keys are staged in LDS, V
+//   * One 512-thread workgroup per (b, query head, 256 queries); wave w owns
+//     two blocks of 16 queries, 32w .. 32w + 31, so every K and V^T operand
+//     it reads from LDS feeds two MFMAs.  K/V tiles of 64 keys are staged in LDS, V
 //     transposed while it is stored (two keys per dword, so consecutive lanes
 //     write consecutive words); the next tile's global loads are issued
 //     before the current tile is computed.  The workgroups of one (b, KV
 //     head) share a die (its L2 holds their K/V tiles), latest blocks first.
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_{bf16,f16}: A = 16 keys of the K
-//     tile (LDS), B = 16 queries (registers, loaded once).  In the output
+//     tile (LDS), B = 16 queries of a block (registers, loaded once).  In the output
 //     layout a lane holds 4 keys of one query, so the softmax is per lane
 //     plus two shuffles, and the probabilities already sit where the B
 //     operand of the next product wants them.
@@ -349,7 +350,7 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
 
 using PrefillFn = void (*)(PrefillArgs);
 
-constexpr int kPreQB = 1;           // query blocks per wave (measured on MI355X)
+constexpr int kPreQB = 2;           // query blocks per wave (measured on MI355X)
 
 PrefillFn prefill_pick(int fmt, int D) {
     if (fmt == FMT_BF16)
