@@ -16,12 +16,14 @@
 //      With EXACT the key rows themselves are read once and scored against q
 //      (q . k_i): token-level selection (FlexGen's top-10% sparse attention,
 //      section "方法细节").
-//   2. Top-K by a most-significant-digit radix select (4 passes of 8 bits)
-//      over an order-preserving uint32 image of the fp32 scores, one shared
-//      LDS histogram per pass.  Ties at the K-th score go to the lower page
-//      index: the equal keys are ranked by a block-wide prefix count in index
-//      order (skipped when every key equal to the K-th is kept).  The kept
-//      indices are compacted in index order, so they come out ascending.
+//   2. Top-K by a most-significant-digit radix select (3 passes: digits of 11,
+//      11 and 10 bits) over an order-preserving uint32 image of the fp32
+//      scores, one shared LDS histogram per pass (two buffers, so the next
+//      pass's is cleared while the current one counts: two barriers a
+//      pass).  Ties at the K-th score go to the lower page index: the equal
+//      keys are ranked by a block-wide prefix count in index order (skipped
+//      when every key equal to the K-th is kept).  The kept indices are
+//      compacted in index order, so they come out ascending.
 #include "common.h"
 
 namespace da {
@@ -275,7 +277,11 @@ __global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args)
     constexpr int R = D * Elem<KF>::size;
 
     extern __shared__ float sc_lds[];              // [P] (SEL_ATTEND: then kept[top_k], w[top_k])
-    __shared__ uint32_t hist[256];
+    // radix histograms: 2048 bins (11-bit digits), two buffers so that a pass
+    // can clear the next pass's while it counts; one pad word per 32 bins
+    // keeps the scan's reads (lane L: bins 32 L .. 32 L + 31) conflict-free
+    constexpr int kBins = 2048, kHist = kBins + kBins / 32;
+    __shared__ uint32_t hist[2][kHist];
     __shared__ uint32_t scan_buf[kSelWaves + 1];
     __shared__ uint32_t pick_digit, pick_need, pick_count;
 
@@ -342,49 +348,67 @@ __global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args)
             }
         }
     }
+    for (int i = tid; i < kHist; i += kSelThreads) hist[0][i] = 0u;
     __syncthreads();
     // ---- 2. radix select of the top_k largest keys -------------------------
-    // MSB-first, 8 bits per pass, one shared 256-bin histogram per pass.
+    // MSB-first, digits of 11, 11 and 10 bits, one shared histogram per pass.
     uint32_t prefix = 0, pmask = 0;
     uint32_t need = (uint32_t)top_k;
     uint32_t eq_count = 0;
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        if (tid < 256) hist[tid] = 0u;
-        __syncthreads();
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const uint32_t dmask = pass < 2 ? 0x7FFu : 0x3FFu;
+        uint32_t *const h = hist[pass & 1];
+        // the other buffer's last reader was the previous pass's scan, which
+        // finished before the barrier that ended that pass
+        if (pass < 2)
+            for (int i = tid; i < kHist; i += kSelThreads) hist[(pass + 1) & 1][i] = 0u;
         for (int64_t i = tid; i < P; i += kSelThreads) {
             const uint32_t key = order_key(sc_lds[i]);
-            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            if ((key & pmask) == prefix) {
+                const uint32_t bin = (key >> shift) & dmask;
+                atomicAdd(&h[bin + (bin >> 5)], 1u);
+            }
         }
         __syncthreads();
         if (w == 0) {
-            uint32_t c[4], loc = 0;
+            // lane L holds bins 32 L .. 32 L + 31; candidates in the bins above
+            // its range by a suffix sum over the lanes; the 32 bins of the one
+            // range that holds the need-th largest key are then scanned by 32
+            // lanes at once
+            const uint32_t *hl = h + 33 * lane;
+            uint32_t loc = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                c[j] = hist[lane * 4 + j];
-                loc += c[j];
-            }
-            // candidates in bins above this lane's four bins
+            for (int j = 0; j < 32; ++j) loc += hl[j];
             uint32_t suf = loc;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
                 const uint32_t y = __shfl_down(suf, o, 64);
                 if (lane + o < 64) suf += y;
             }
-            uint32_t cum = suf - loc;
+            const uint32_t cum = suf - loc;
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(cum < need && cum + loc >= need);
+            const int lc = __builtin_ctzll(hit);                       // the lane whose range holds it
+            const uint32_t base = __builtin_amdgcn_readlane(cum, lc);  // candidates above that range
+            // lanes 0..31 take its bins 31 - lane (descending), prefix sums in that order
+            const uint32_t cb = lane < 32 ? h[33 * lc + 31 - lane] : 0u;
+            uint32_t pre = cb;
 #pragma unroll
-            for (int j = 3; j >= 0; --j) {
-                if (cum < need && cum + c[j] >= need) {
-                    pick_digit = (uint32_t)(lane * 4 + j);
-                    pick_need = need - cum;
-                    pick_count = c[j];
-                }
-                cum += c[j];
+            for (int o = 1; o < 32; o <<= 1) {
+                const uint32_t y = __shfl_up(pre, o, 64);
+                if ((lane & 31) >= o) pre += y;
+            }
+            const uint32_t above = base + pre - cb;
+            if (lane < 32 && above < need && above + cb >= need) {
+                pick_digit = (uint32_t)(32 * lc + 31 - lane);
+                pick_need = need - above;
+                pick_count = cb;
             }
         }
         __syncthreads();
         prefix |= pick_digit << shift;
-        pmask |= 0xFFu << shift;
+        pmask |= dmask << shift;
         need = pick_need;
         eq_count = pick_count;
     }
