@@ -87,8 +87,8 @@ typedef enum da_dtype { DA_F32 = 0, DA_F16 = 1, DA_BF16 = 2 } da_dtype;
 
 /* Shape of one decode-attention call.
  *   batch >= 1; n_kv_heads >= 1; n_q_heads = G * n_kv_heads with
- *   G in {1, 2, 4, 8}; head_dim in {64, 128}; n_ctx >= 1 tokens per (batch
- *   row, KV head); scale > 0 (normally 1/sqrt(head_dim)); q_dtype is DA_F32
+ *   G in {1, 2, 4, 8}; head_dim in {64, 128}; 1 <= n_ctx <= 2^34 tokens per
+ *   (batch row, KV head); scale > 0 (normally 1/sqrt(head_dim)); q_dtype is DA_F32
  *   or kv_dtype; split_tokens is the number of tokens (dense) or selected
  *   token positions (paged) one workgroup reduces before the cross-split
  *   merge: 0 selects the entry point's default (dense and head-wise: the

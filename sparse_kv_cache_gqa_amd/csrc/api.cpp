@@ -61,7 +61,8 @@ da_status check_shape(const da_attn_shape *s, bool kv4) {
     if (kv4 ? s->head_dim != 128 : (s->head_dim != 64 && s->head_dim != 128))
         return fail(DA_E_UNSUPPORTED, "head_dim %d not supported", s->head_dim);
     if (s->n_ctx < 1) return fail(DA_E_INVALID, "n_ctx %lld < 1", (long long)s->n_ctx);
-    if (s->n_ctx > (1ll << 40)) return fail(DA_E_INVALID, "n_ctx %lld too large", (long long)s->n_ctx);
+    // n_ctx / 16 (the most splits any split size gives) must fit the int32 split count
+    if (s->n_ctx > (1ll << 34)) return fail(DA_E_INVALID, "n_ctx %lld > 2^34", (long long)s->n_ctx);
     if (!(s->scale > 0.f) || !isfinite(s->scale)) return fail(DA_E_INVALID, "scale must be finite and > 0");
     if (s->q_dtype < DA_F32 || s->q_dtype > DA_BF16) return fail(DA_E_INVALID, "q_dtype %d", s->q_dtype);
     if (!kv4) {

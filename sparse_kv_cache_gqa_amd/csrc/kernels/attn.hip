@@ -82,12 +82,6 @@ struct Cfg {
 __device__ __forceinline__ u32x4 ld_stream(const char *p) {
     return __builtin_nontemporal_load((const u32x4 *)p);
 }
-__device__ __forceinline__ uint32_t ld_stream32(const void *p) {
-    return __builtin_nontemporal_load((const uint32_t *)p);
-}
-__device__ __forceinline__ uint16_t ld_stream16(const uint16_t *p) {
-    return __builtin_nontemporal_load(p);
-}
 
 // One dword of 8 codes -> 8 fp16 values 0..15 in the order of qk_dim().
 __device__ __forceinline__ u32x4 u4_to_f16x8(uint32_t x) {

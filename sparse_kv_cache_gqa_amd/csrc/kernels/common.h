@@ -65,9 +65,6 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 2);
 }
-__device__ __forceinline__ uint16_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 2);
-}
 
 // Hide a value's known bits from the optimiser (no instruction is emitted).
 __device__ __forceinline__ uint32_t opaque(uint32_t x) {

@@ -73,6 +73,7 @@ def dense(lib, s, q=FAKE, k=FAKE, v=FAKE, o=FAKE, ws=FAKE, ws_bytes=1 << 40):
     (dict(head_dim=0), L.DA_E_INVALID),
     (dict(n_ctx=0), L.DA_E_INVALID),
     (dict(n_ctx=-5), L.DA_E_INVALID),
+    (dict(n_ctx=(1 << 34) + 1), L.DA_E_INVALID),     # the split count must fit int32
     (dict(scale=0.0), L.DA_E_INVALID),
     (dict(scale=float("nan")), L.DA_E_INVALID),
     (dict(scale=float("inf")), L.DA_E_INVALID),
