@@ -321,7 +321,8 @@ da_status da_prefill_attention(const da_attn_shape *s, int64_t chunk,
  *   buf0, buf1: device buffers of da_stream_buffer_bytes each;
  *   q [n_layers][batch][n_q_heads][head_dim] q_dtype, device;
  *   o [n_layers][batch][n_q_heads][head_dim] fp32, device (written);
- *   ws >= da_stream_workspace(ctx) bytes, device;
+ *   ws >= da_stream_workspace(ctx) bytes, device (that size covers every
+ *     attended length 1..n_ctx, so it stays valid as the length changes);
  *   compute != copy.  The output is complete when `compute` drains.
  * Each head's result is bitwise equal to da_decode_attention on the same
  * data with the same split_tokens.

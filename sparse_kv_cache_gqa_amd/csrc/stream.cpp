@@ -118,8 +118,17 @@ size_t da_stream_workspace(const da_stream_ctx *c) {
     if (!c) return 0;
     const da_attn_shape *s = &c->shape;
     const int G = s->n_q_heads / s->n_kv_heads;
-    return attn_ws_bytes((int64_t)s->batch * c->hpc * G, attn_n_split(s->n_ctx, split_tokens_of(s, SPLIT_DENSE), false, 0, 0),
-                         s->head_dim);
+    // a step attends len <= cap tokens, split by len's own split size, and
+    // the default split grows in steps with the length: the most splits over
+    // 1 <= len <= cap come at cap or at the last length of a smaller split
+    int32_t most = 0;
+    for (int64_t len = 1; len <= s->n_ctx; len *= 2) {
+        da_attn_shape t = *s;
+        t.n_ctx = len;
+        most = std::max(most, attn_n_split(len, split_tokens_of(&t, SPLIT_DENSE), false, 0, 0));
+    }
+    most = std::max(most, attn_n_split(s->n_ctx, split_tokens_of(s, SPLIT_DENSE), false, 0, 0));
+    return attn_ws_bytes((int64_t)s->batch * c->hpc * G, most, s->head_dim);
 }
 
 da_status da_stream_headwise(da_stream_ctx *c, int32_t n_layers, const void *const *k_host,

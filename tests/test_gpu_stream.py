@@ -163,3 +163,44 @@ def test_append_new_token_then_stream(da):
     with pytest.raises(da.DaError):
         hs.append(k_new.cuda(), v_new.cuda(), ks, vs, stream=cpy)
     hs.close()
+
+
+def test_workspace_covers_every_attended_length(da):
+    """The default split size grows in steps with the attended length, so a
+    shorter length can need more splits than the capacity (cap 4097: 9 splits
+    of 512; length 4096: 16 splits of 256).  The context's workspace size
+    covers every length: a call at length 4096 writes nothing past it (a
+    guard region after it keeps its pattern) and matches resident attention
+    over the same rows bitwise."""
+    import torch
+    spec = synth.small_headwise(n_layers=1, n_kv_heads=1, n_q_heads=4, batch=1, head_dim=128,
+                                n_ctx=4097, tag=52)
+    ks, vs, k64, v64 = host_heads(spec)
+    n = 4096
+    hs = da.HeadwiseStream(1, 4, 1, 128, spec.n_ctx, da.DA_F32, da.DA_BF16)
+    hs.set_length(n)
+    need_4096 = 4 * 16 * (128 + 4) * 4            # 4 query-head rows x 16 splits of 256
+    ws_bytes = hs.workspace_bytes
+    assert ws_bytes >= need_4096
+    guard = 1 << 16
+    ws_all = torch.full((ws_bytes + guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    ws = ws_all[:ws_bytes]
+    buf0 = torch.empty(hs.buffer_bytes, dtype=torch.uint8, device="cuda")
+    buf1 = torch.empty(hs.buffer_bytes, dtype=torch.uint8, device="cuda")
+    q = to_dev(spec.q(), "f32")
+    out = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
+    comp = torch.cuda.current_stream()
+    cpy = torch.cuda.Stream()
+    cpy.wait_stream(comp)
+    hs.da_stream_headwise(ks, vs, buf0, buf1, q, out, ws, comp, cpy)
+    torch.cuda.synchronize()
+    hs.close()
+    assert bool((ws_all[ws_bytes:] == 0xA5).all()), "written past the workspace"
+    ref = headwise_attention(as_f64(spec.q(), "f32"), [[k64[0][0][:, :n]]], [[v64[0][0][:, :n]]],
+                             1.0 / np.sqrt(128))
+    assert_close(out.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what="stream at length 4096 of 4097")
+    kl = ks[0][:, :n].unsqueeze(1).cuda().contiguous()
+    vl = vs[0][:, :n].unsqueeze(1).cuda().contiguous()
+    o = da.da_decode_attention(q[0].contiguous(), kl, vl)
+    torch.cuda.synchronize()
+    assert np.array_equal(o.cpu().numpy(), out.cpu().numpy()[0])
