@@ -9,11 +9,12 @@
 //
 //   * One 512-thread workgroup per (b, query head, 256 queries); wave w owns
 //     two blocks of 16 queries, 32w .. 32w + 31, so every K and V^T operand
-//     it reads from LDS feeds two MFMAs.  K/V tiles of 64 keys are staged in LDS, V
-//     transposed while it is stored (two keys per dword, so consecutive lanes
-//     write consecutive words); the next tile's global loads are issued
-//     before the current tile is computed.  The workgroups of one (b, KV
-//     head) share a die (its L2 holds their K/V tiles), latest blocks first.
+//     it reads from LDS feeds two MFMAs.  K/V tiles of 64 keys are staged in
+//     LDS, V transposed while it is stored (two keys per dword, in the key
+//     order of the P^T operand, so each V^T operand is one 16-byte read); the
+//     next tile's global loads are issued before the current tile is
+//     computed.  The workgroups of one (b, KV head) share a die (its L2 holds
+//     their K/V tiles), latest blocks first.
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_{bf16,f16}: A = 16 keys of the K
 //     tile (LDS), B = 16 queries of a block (registers, loaded once).  In the output
 //     layout a lane holds 4 keys of one query, so the softmax is per lane
@@ -21,12 +22,15 @@
 //     operand of the next product wants them.
 //   * O^T += V^T P^T on the same MFMA: A = 16 channels of V^T (LDS), B = P^T
 //     straight from the S^T registers (lane k-slots 0-3 / 4-7 = keys
-//     4g .. 4g + 3 of the two 16-key halves of a 32-key step; the V^T reads
-//     use the same key order).  P is split into two 16-bit terms (hi + lo),
-//     so the product is accurate to about 2^-16 of each weight.
+//     4g .. 4g + 3 of the two 16-key halves of a 32-key step; V^T rows hold
+//     those eight keys contiguously).  P is split into two 16-bit terms (hi +
+//     lo), so the product is accurate to about 2^-16 of each weight.
+//   * Only tiles that reach the diagonal run the causal mask (a wave-uniform
+//     branch); the first product of each S^T chain starts from a zero
+//     accumulator operand.
 //   * Online softmax in base 2 per query, the scale folded into the exp2
-//     argument; rows past the causal limit get -inf (only on tiles that reach
-//     the diagonal); the running max is raised lazily (see below).
+//     argument; rows past the causal limit get -inf; the running max is
+//     raised lazily (see below).
 #include "common.h"
 
 namespace da {
@@ -71,6 +75,14 @@ __device__ __forceinline__ float hi16(uint32_t w) {
     else return f16_to_f32(w >> 16);
 }
 
+// Position of key k (0..63 of a tile) inside a V^T row: within each 32-key
+// step, the eight keys that one lane's P^T operand slots hold (keys 4 g .. +3
+// and 16 + 4 g .. +3) are stored contiguously at 8 g, so the A operand is a
+// single 16-byte read.  Keys 2 j and 2 j + 1 stay adjacent.
+__device__ __forceinline__ int vt_pos(int k) {
+    return (k & ~31) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
+}
+
 constexpr float kLazy = 8.f;        // log2 headroom before the running max is raised
 
 struct PrefillArgs {
@@ -94,7 +106,7 @@ template <int F, int D, int QB>
 __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs a) {
     constexpr int kPreThreads = pre_threads<QB>();
     constexpr int KSTR = D + 8;                 // K tile row stride (elements)
-    constexpr int VSTR = kPreKeys + 4;          // V^T row stride (elements; 8-byte rows for the reads)
+    constexpr int VSTR = kPreKeys + 8;          // V^T row stride (elements; 16-byte aligned rows)
     constexpr int NKS = D / 32;                 // 32-channel steps of S
     constexpr int NCB = D / 16;                 // 16-channel blocks of O
     constexpr int NKB = kPreKeys / 16;          // 16-key blocks of a tile
@@ -107,8 +119,8 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
     constexpr int NV = NVA >= kPreThreads ? NVA / kPreThreads : 1; // per thread
     static_assert(NVA % kPreThreads == 0 || NVA < kPreThreads, "V split");
 
-    __shared__ uint16_t k_lds[kPreKeys * KSTR];
-    __shared__ uint16_t vt_lds[D * VSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[kPreKeys * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VSTR];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -201,11 +213,12 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
             const int c = tid + kPreThreads * j;
             if (c >= NVA) continue;
             const int pair = c % (kPreKeys / 2), col = (c / (kPreKeys / 2)) * 8;
+            const int kp = vt_pos(2 * pair);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t a0 = vreg[j][0][e], a1 = vreg[j][1][e];
-                *(uint32_t *)&vt_lds[(col + 2 * e) * VSTR + 2 * pair] = (a0 & 0xFFFFu) | (a1 << 16);
-                *(uint32_t *)&vt_lds[(col + 2 * e + 1) * VSTR + 2 * pair] = (a0 >> 16) | (a1 & 0xFFFF0000u);
+                *(uint32_t *)&vt_lds[(col + 2 * e) * VSTR + kp] = (a0 & 0xFFFFu) | (a1 << 16);
+                *(uint32_t *)&vt_lds[(col + 2 * e + 1) * VSTR + kp] = (a0 >> 16) | (a1 & 0xFFFF0000u);
             }
         }
     };
@@ -233,18 +246,16 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
 
         const int64_t t0 = (int64_t)t * kPreKeys;
         // S^T blocks: keys 16 kb + 4 g + i of this tile, query n of block qb
+        // (the first step of each chain starts from a zero accumulator operand)
         f32x4 st[QB][NKB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) st[qb][kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const u32x4 ka = *(const u32x4 *)&k_lds[(16 * kb + n) * KSTR + 32 * ks + 8 * g];
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) st[qb][kb] = mfma16<F>(ka, Qb[qb][ks], st[qb][kb]);
+                for (int qb = 0; qb < QB; ++qb)
+                    st[qb][kb] = mfma16<F>(ka, Qb[qb][ks], ks == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : st[qb][kb]);
             }
 
         // online softmax per query; build P^T operands (hi and lo terms).
@@ -258,17 +269,24 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
         u32x4 ph[QB][NS2], pl[QB][NS2];               // [qb][32-key step]
         float mx[QB];                                 // raw (unscaled) tile max per query
         bool up = false;
+        if (diag) {                                   // wave-uniform: only tiles on the diagonal
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const int rel = (int)(a.prefix + qw - t0) + 16 * qb + n - 4 * g;   // qpos - (t0 + 4 g)
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (16 * kb + i > rel) st[qb][kb][i] = neg_inf();
+            }
+        }
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const int rel = (int)(a.prefix + qw - t0) + 16 * qb + n - 4 * g;   // qpos - (t0 + 4 g)
             float m = neg_inf();
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (diag && 16 * kb + i > rel) st[qb][kb][i] = neg_inf();
-                    m = fmaxf(m, st[qb][kb][i]);
-                }
+                for (int i = 0; i < 4; ++i) m = fmaxf(m, st[qb][kb][i]);
             m = fmaxf(m, shfl_xor(m, 16));
             mx[qb] = fmaxf(m, shfl_xor(m, 32));
             up |= mx[qb] * sl2 > m_run[qb] + kLazy;
@@ -315,10 +333,8 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
             for (int s2 = 0; s2 < NS2; ++s2) {
-                const uint16_t *vr = &vt_lds[(16 * cb + n) * VSTR + 32 * s2 + 4 * g];
-                const uint2 lo4 = *(const uint2 *)vr;           // keys 32 s2 + 4 g .. + 3
-                const uint2 hi4 = *(const uint2 *)(vr + 16);    // keys 32 s2 + 16 + 4 g .. + 3
-                const u32x4 va = (u32x4){lo4.x, lo4.y, hi4.x, hi4.y};
+                // slots 0-3: keys 32 s2 + 4 g .. + 3; 4-7: keys 32 s2 + 16 + 4 g .. + 3
+                const u32x4 va = *(const u32x4 *)&vt_lds[(16 * cb + n) * VSTR + 32 * s2 + 8 * g];
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
                     acc[qb][cb] = mfma16<F>(va, ph[qb][s2], acc[qb][cb]);
