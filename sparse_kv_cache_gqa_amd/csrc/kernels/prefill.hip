@@ -28,6 +28,9 @@
 //   * Only tiles that reach the diagonal run the causal mask (a wave-uniform
 //     branch); the first product of each S^T chain starts from a zero
 //     accumulator operand.
+//   * Within a tile the softmax of query block 1 is independent of the P.V
+//     products of block 0; scheduling-group hints interleave the two, so the
+//     VALU and the matrix cores work at the same time within a wave.
 //   * Online softmax in base 2 per query, the scale folded into the exp2
 //     argument; rows past the causal limit get -inf; the running max is
 //     raised lazily (see below).
@@ -83,6 +86,7 @@ __device__ __forceinline__ int vt_pos(int k) {
     return (k & ~31) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
 }
 
+constexpr int kSgVa = 14, kSgVb = 3;   // scheduling groups, VALU counts (measured on MI355X)
 constexpr float kLazy = 8.f;        // log2 headroom before the running max is raised
 
 struct PrefillArgs {
@@ -302,8 +306,8 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
                 for (int cb = 0; cb < NCB; ++cb) acc[qb][cb] *= alpha;
             }
         }
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
+        // softmax of block qb: P^T operands (hi and lo terms) and the row sum
+        auto softmax_block = [&](int qb) {
             const float nm = -m_run[qb];
             float lsum = 0.f;
             uint32_t hw[NKB][2], lw[NKB][2];              // [kb][pair of keys]
@@ -326,21 +330,41 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
                 ph[qb][s2] = (u32x4){hw[2 * s2][0], hw[2 * s2][1], hw[2 * s2 + 1][0], hw[2 * s2 + 1][1]};
                 pl[qb][s2] = (u32x4){lw[2 * s2][0], lw[2 * s2][1], lw[2 * s2 + 1][0], lw[2 * s2 + 1][1]};
             }
-        }
-
-        // O^T += V^T P^T: A = channels 16 cb + m, keys in the P^T slot order
+        };
+        // O^T += V^T P^T of block qb: A = channels 16 cb + m, keys in the P^T slot order
+        auto pv_block = [&](int qb) {
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
+            for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-            for (int s2 = 0; s2 < NS2; ++s2) {
-                // slots 0-3: keys 32 s2 + 4 g .. + 3; 4-7: keys 32 s2 + 16 + 4 g .. + 3
-                const u32x4 va = *(const u32x4 *)&vt_lds[(16 * cb + n) * VSTR + 32 * s2 + 8 * g];
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
+                for (int s2 = 0; s2 < NS2; ++s2) {
+                    // slots 0-3: keys 32 s2 + 4 g .. + 3; 4-7: keys 32 s2 + 16 + 4 g .. + 3
+                    const u32x4 va = *(const u32x4 *)&vt_lds[(16 * cb + n) * VSTR + 32 * s2 + 8 * g];
                     acc[qb][cb] = mfma16<F>(va, ph[qb][s2], acc[qb][cb]);
                     acc[qb][cb] = mfma16<F>(va, pl[qb][s2], acc[qb][cb]);
                 }
+        };
+        // the products of block qb and the softmax of block qb + 1 are
+        // independent, so the matrix cores and the VALU can work side by side
+        softmax_block(0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            pv_block(qb);
+            if (qb + 1 < QB) softmax_block(qb + 1);
+        }
+        if constexpr (QB == 2) {
+            // instruction order for the scheduler: block 0's softmax, then
+            // block 0's products each followed by a few VALU instructions of
+            // block 1's softmax, then block 1's products
+#pragma unroll
+            for (int i = 0; i < kSgVa; ++i) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * NCB * NS2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, kSgVb, 0);
             }
+#pragma unroll
+            for (int i = 0; i < 2 * NCB * NS2; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
     }
 
     // ---- normalise and store: lane holds channels 16 cb + 4 g .. + 3 of query n
