@@ -53,12 +53,25 @@ def up(arr, dtype, torch, np):
     return t.cuda()
 
 
+MIN_WARM_S = 0.25   # the GPU clock ramps up over the first tens of ms of work
+
+
 def time_events(torch, fn, steps: int, warmup: int, stream=None) -> float:
-    """Average ms per call of fn(i), with HIP events on `stream` around all calls."""
+    """Average ms per call of fn(i), with HIP events on `stream` around all
+    calls, after `warmup` calls and at least MIN_WARM_S seconds of calls (in
+    doubling batches), so the timed region sees the steady-state clock."""
     stream = stream or torch.cuda.current_stream()
+    t0 = time.perf_counter()
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
+    n, i = 1, warmup
+    while time.perf_counter() - t0 < MIN_WARM_S:
+        for _ in range(n):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+        n *= 2
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record(stream)

@@ -92,10 +92,12 @@ typedef enum da_dtype { DA_F32 = 0, DA_F16 = 1, DA_BF16 = 2 } da_dtype;
  *   or kv_dtype; split_tokens is the number of tokens (dense) or selected
  *   token positions (paged) one workgroup reduces before the cross-split
  *   merge: 0 selects the entry point's default (dense and head-wise: the
- *   power of two nearest above n_ctx/16 within [256, 2048]; uint4 512;
- *   paged 512); otherwise a multiple of 16 in [16, 65536].  The
- *   split never depends on batch or head counts, so a call over one head and
- *   a call over all heads give bitwise-equal results for that head. */
+ *   power of two nearest above n_ctx/16 within [256, 2048]; paged 512;
+ *   uint4: the longest power of two from 256 that still gives at least
+ *   2048 (split, batch row, KV head) waves); otherwise a multiple of 16 in
+ *   [16, 65536].  The dense, head-wise and paged splits never depend on
+ *   batch or head counts, so there a call over one head and a call over all
+ *   heads give bitwise-equal results for that head. */
 typedef struct da_attn_shape {
     int32_t batch;
     int32_t n_q_heads;

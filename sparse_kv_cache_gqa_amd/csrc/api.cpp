@@ -82,7 +82,8 @@ da_status check_shape(const da_attn_shape *s, bool kv4) {
 int32_t split_tokens_of(const da_attn_shape *s, int mode) {
     if (s->split_tokens) return s->split_tokens;
     return mode == SPLIT_PAGED ? kDefaultSplitPaged
-                               : (mode == SPLIT_U4 ? kDefaultSplitU4 : default_split_dense(s->n_ctx));
+                               : (mode == SPLIT_U4 ? default_split_u4(s->n_ctx, (int64_t)s->batch * s->n_kv_heads)
+                                                   : default_split_dense(s->n_ctx));
 }
 
 da_status check_ptr(const void *p, const char *name) {

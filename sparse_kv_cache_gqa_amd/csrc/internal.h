@@ -17,7 +17,8 @@ enum Fmt : int { FMT_F32 = 0, FMT_F16 = 1, FMT_BF16 = 2, FMT_U4 = 3 };
 // small); uint4 and paged: fixed.
 constexpr int kDefaultSplitDenseMin = 256;
 constexpr int kDefaultSplitDense = 2048;
-constexpr int kDefaultSplitU4 = 512;
+constexpr int kDefaultSplitU4Min = 256;
+constexpr int64_t kU4MinWaves = 2048;    // two waves per SIMD
 constexpr int kDefaultSplitPaged = 512;
 
 // One attention launch (split-K partial pass + cross-split merge).
@@ -58,6 +59,7 @@ struct AttnLaunch {
 constexpr int kMaxWavesPerBlock = 4;
 
 int32_t default_split_dense(int64_t n_ctx);
+int32_t default_split_u4(int64_t n_ctx, int64_t units);
 
 // Number of splits and workspace bytes for a launch description.
 int32_t attn_n_split(int64_t n_ctx, int32_t split_tokens, bool paged,

@@ -83,15 +83,17 @@ __device__ __forceinline__ u32x4 ld_stream(const char *p) {
     return __builtin_nontemporal_load((const u32x4 *)p);
 }
 
-// One dword of 8 codes -> 8 fp16 values 0..15 in the order of qk_dim().
+// One dword of 8 codes -> 8 fp16 values 1 + c/16 (exact) in the order of
+// qk_dim(): output k moves nibbles k and k + 4 (bits 4k, 4k + 16) to mantissa
+// bits 6..9 of its two halves, under the exponent of 1.0.  A dot product with
+// them is sum(q) + sum(q c)/16, so sum(q c) = 16 (dot - sum(q)).
 __device__ __forceinline__ u32x4 u4_to_f16x8(uint32_t x) {
+    constexpr uint32_t kMant = 0x03C003C0u, kOne = 0x3C003C00u;
     u32x4 r;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t m = ((x >> (4 * k)) & 0x000F000Fu) | 0x64006400u;   // 1024 + c
-        f16x2 h = __builtin_bit_cast(f16x2, m) - (f16x2){(_Float16)1024.0f, (_Float16)1024.0f};
-        r[k] = __builtin_bit_cast(uint32_t, h);
-    }
+    r[0] = ((x << 6) & kMant) | kOne;
+    r[1] = ((x << 2) & kMant) | kOne;
+    r[2] = ((x >> 2) & kMant) | kOne;
+    r[3] = ((x >> 6) & kMant) | kOne;
     return r;
 }
 
@@ -159,6 +161,11 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     constexpr int MT = C::U4 ? FMT_F16 : KF;
     constexpr int PSTR = D + 4;        // floats per partial row: u[D], m, l, pad, pad
     constexpr int kTS = C::TS, kTile = C::TILE;
+    // uint4 with one query head per KV head: q fills every MFMA row, so every
+    // lane group receives scores; group g scores sub-tile g mod 2, and lane l
+    // holds stage token l mod 32, whose metadata it loaded itself
+    constexpr bool SOLO = C::U4 && G == 1;
+    static_assert(!SOLO || (kTS == 2 && kTile == 32), "one-head uint4 layout");
 
     __shared__ float p_all[kMaxWavesPerBlock][G > 1 ? kTile * G : 1];            // p exchange
     __shared__ int32_t pg_all[kMaxWavesPerBlock][PAGED ? kMaxPagesPerSplit : 1];  // page lists
@@ -285,7 +292,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     float Af[KF == FMT_F32 ? NMF : 1];
     {
         const int m = n16;
-        const int h = m / RPH, within = m % RPH;
+        const int h = SOLO ? 0 : m / RPH, within = m % RPH;
         const int grp = within / SPL, s = within % SPL;
         const bool rowok = h < G && within < SPL * NGRP;
 #pragma unroll
@@ -322,7 +329,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
                 float x = load_scalar<QF>(a.q, qoff + h * D + gr * 64 + lane);
 #pragma unroll
                 for (int o = 1; o < 64; o <<= 1) x += shfl_xor(x, o);
-                if (h / HPL == g4) qs[h % HPL][gr] = x;
+                if (SOLO || h / HPL == g4) qs[h % HPL][gr] = x;
             }
     }
 
@@ -385,7 +392,8 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
                         for (int s = 0; s < SPL; ++s) dot += cc[hh * RPH + gr * SPL + s];
                         const float mn = f16_to_f32((kmn2 >> (16 * gr)) & 0xFFFFu);
                         const float sg = f16_to_f32((ksc2 >> (16 * gr)) & 0xFFFFu);
-                        raw += mn * qs[hh][gr] + sg * dot;
+                        // q . (mn + c sg) = mn sum(q) + 16 sg (dot - sum(q))
+                        raw += mn * qs[hh][gr] + (16.f * sg) * (dot - qs[hh][gr]);
                     }
                 } else {
 #pragma unroll
@@ -529,31 +537,104 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         if constexpr (G > 1) wave_lds_sync();
     };
 
+    // ---- uint4, one query head: each lane scores stage token lane mod 32 ----
+    // am: sum of p * (V group minimum) over this lane's tokens, for V group
+    // lane / 32 (lanes 32..63 repeat the tokens of lanes 0..31)
+    float am = 0.f;
+    auto compute_tile_solo = [&](St &st) {
+        f32x4 cc[kTS];
+#pragma unroll
+        for (int ts = 0; ts < kTS; ++ts) {
+            cc[ts] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                cc[ts] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, Aq[u]),
+                                                                __builtin_bit_cast(f16x8, u4_to_f16x8(st.K[ts][0][u])),
+                                                                cc[ts], 0, 0, 0);
+        }
+        const bool odd = (g4 & 1) != 0;          // this lane group's sub-tile
+        float raw = 0.f;
+#pragma unroll
+        for (int gr = 0; gr < NGRP; ++gr) {
+            float dot = 0.f;
+#pragma unroll
+            for (int s = 0; s < SPL; ++s) dot += odd ? cc[1][gr * SPL + s] : cc[0][gr * SPL + s];
+            const float mn = f16_to_f32((st.mk >> (16 * gr)) & 0xFFFFu);
+            const float sg = f16_to_f32((st.sk >> (16 * gr)) & 0xFFFFu);
+            raw += mn * qs[0][gr] + (16.f * sg) * (dot - qs[0][gr]);
+        }
+        const float sc = (odd ? st.kok[1] : st.kok[0]) ? raw * sl2 : neg_inf();
+        const float rmax = row16_max(sc);
+        const float mn = fmaxf(m_run[0], fmaxf(readlane_f(rmax, 0), readlane_f(rmax, 16)));
+        if (mn != m_run[0]) {
+            const float alpha = fast_exp2(m_run[0] - mn);
+            am *= alpha;
+            l_part[0] *= alpha;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[0][c] *= alpha;
+            m_run[0] = mn;
+        }
+        const float p = (sc == neg_inf()) ? 0.f : fast_exp2(sc - m_run[0]);
+        if (lane < 32) l_part[0] += p;
+        // this lane's V group (lane / 32): its minimum and scale for the token
+        const int gsh = lane < 32 ? 0 : 16;
+        const float vmn1 = f16_to_f32((st.mv >> gsh) & 0xFFFFu);
+        const float vsc1 = f16_to_f32((st.sv >> gsh) & 0xFFFFu);
+        am = fmaf(p, vmn1, am);
+        const float pw = p * vsc1;
+        // P.V: the V lanes take p * scale of their token and group from the
+        // lane that scored it (lane = token + 32 * group)
+#pragma unroll
+        for (int ts = 0; ts < kTS; ++ts) {
+            const float wv = __shfl(pw, ts * kSub + vtok + 32 * (vcol / 32), 64);
+            const float wv16 = wv * 0.0625f;
+            const u32x4 x = st.V[ts][0];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t lo = opaque(x[u] & 0x0F0F0F0Fu);
+                const uint32_t hi = opaque(x[u] & 0xF0F0F0F0u);
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    acc[0][8 * u + 2 * bb] = fmaf(wv, ubyte_f32(lo, bb), acc[0][8 * u + 2 * bb]);
+                    acc[0][8 * u + 2 * bb + 1] = fmaf(wv16, ubyte_f32(hi, bb), acc[0][8 * u + 2 * bb + 1]);
+                }
+            }
+        }
+    };
+    auto compute = [&](St &st) {
+        if constexpr (SOLO) compute_tile_solo(st);
+        else compute_tile(st);
+    };
+
     // ---- main loop: two register stages -------------------------------------
     for (int t0 = 0; t0 < ntok; t0 += 2 * kTile) {
         const bool more = t0 + kTile < ntok;
         if (more) load_tile(sb, t0 + kTile);
-        compute_tile(sa);
+        compute(sa);
         if (!more) break;
         if (t0 + 2 * kTile < ntok) load_tile(sa, t0 + 2 * kTile);
-        compute_tile(sb);
+        compute(sb);
     }
 
     // ---- partial of this split ------------------------------------------------
 #pragma unroll
     for (int hh = 0; hh < HPL; ++hh) {
         float x = l_part[hh];
-        x += shfl_xor(x, 1);
-        x += shfl_xor(x, 2);
-        x += shfl_xor(x, 4);
-        x += shfl_xor(x, 8);
+#pragma unroll
+        for (int o = 1; o < (SOLO ? 32 : 16); o <<= 1) x += shfl_xor(x, o);
         l_part[hh] = x;
+    }
+    if constexpr (SOLO) {
+        // per V group: lanes 0..31 sum group 0, lanes 32..63 group 1
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) am += shfl_xor(am, o);
+        amin[0] = __shfl(am, 32 * (vcol / 32), 64);
     }
 #pragma unroll
     for (int mask = C::CH_LANES; mask < 64; mask <<= 1) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            if constexpr (C::U4) amin[h] += shfl_xor(amin[h], mask);
+            if constexpr (C::U4 && !SOLO) amin[h] += shfl_xor(amin[h], mask);
 #pragma unroll
             for (int c = 0; c < CPL; ++c) acc[h][c] += shfl_xor(acc[h][c], mask);
         }
@@ -788,6 +869,16 @@ int32_t default_split_dense(int64_t n_ctx) {
     int64_t want = (n_ctx + 15) / 16;
     int32_t s = kDefaultSplitDenseMin;
     while (s < kDefaultSplitDense && s < want) s <<= 1;
+    return s;
+}
+
+// uint4: the longest split (from 256 tokens, doubling) that still gives at
+// least kU4MinWaves waves over the units (batch rows x KV heads); measured on
+// MI355X at B64 H56 N1024: one 1024-token split per head (no merge) 92 us,
+// 512 (two splits and a merge) 99 us, 256 105 us.
+int32_t default_split_u4(int64_t n_ctx, int64_t units) {
+    int32_t s = kDefaultSplitU4Min;
+    while (s < n_ctx && s < 65536 && units * ((n_ctx + 2 * (int64_t)s - 1) / (2 * (int64_t)s)) >= kU4MinWaves) s <<= 1;
     return s;
 }
 

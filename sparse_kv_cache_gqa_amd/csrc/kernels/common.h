@@ -41,6 +41,23 @@ __device__ __forceinline__ T shfl_xor(T v, int mask) {
     return __shfl_xor(v, mask, 64);
 }
 
+// One data-parallel-primitive move: lane i takes `v` of the lane that the
+// row-local pattern CTRL names (VALU, no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Maximum over the 16 lanes of each row, left in every lane of the row: swap
+// neighbours, swap pairs, mirror within 8 lanes, mirror within 16 lanes.
+// Maximum is exact, so the result equals that of any reduction order.
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_mov<0xB1>(x));    // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp_mov<0x4E>(x));    // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_mov<0x141>(x));   // row_half_mirror
+    x = fmaxf(x, dpp_mov<0x140>(x));   // row_mirror
+    return x;
+}
+
 __device__ __forceinline__ float readlane_f(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }

@@ -197,7 +197,16 @@ def test_kv4_checks(lib):
     assert att(s64) == L.DA_E_UNSUPPORTED
     sbf = shape(batch=64, n_q_heads=56, n_kv_heads=56, head_dim=128, n_ctx=1024, q_dtype=L.DA_BF16)
     assert att(sbf) == L.DA_E_UNSUPPORTED
-    assert lib.da_decode_attention_kv4_workspace(ctypes.byref(s)) == 64 * 56 * 2 * 132 * 4
+    # default uint4 split: the longest power of two from 256 tokens that keeps
+    # >= 2048 waves -- one 1024-token split per head at B64 H56, 256-token
+    # splits for a single row of 4 heads, 2048 (two per head) for 1024 units
+    # at 4096 tokens
+    ws = lambda **kw: lib.da_decode_attention_kv4_workspace(ctypes.byref(shape(
+        head_dim=128, q_dtype=L.DA_F16, **kw)))
+    assert lib.da_decode_attention_kv4_workspace(ctypes.byref(s)) == 64 * 56 * 1 * 132 * 4
+    assert ws(batch=1, n_q_heads=4, n_kv_heads=4, n_ctx=1024) == 4 * 4 * 132 * 4
+    assert ws(batch=16, n_q_heads=64, n_kv_heads=64, n_ctx=4096) == 1024 * 2 * 132 * 4
+    assert ws(batch=16, n_q_heads=64, n_kv_heads=64, n_ctx=4096, split_tokens=1024) == 1024 * 4 * 132 * 4
 
 
 def test_headwise_sizes_match_the_pages_and_checks(lib):

@@ -102,7 +102,7 @@ KV4_CASES = [
     (2, 2, 2, 77, "f32", 16),         # fp32 q (two fp16 terms)
     (1, 4, 1, 513, "f32", 0),         # G = 4
     (1, 8, 1, 200, "f16", 64),        # G = 8
-    (4, 64, 64, 1000, "f16", 0),      # 256 heads x 2 splits merged in the workgroup
+    (4, 64, 64, 1000, "f16", 0),      # 256 heads x 4 splits merged in the workgroup
 ]
 
 
