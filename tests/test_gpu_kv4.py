@@ -103,6 +103,8 @@ KV4_CASES = [
     (1, 4, 1, 513, "f32", 0),         # G = 4
     (1, 8, 1, 200, "f16", 64),        # G = 8
     (4, 64, 64, 1000, "f16", 0),      # 256 heads x 4 splits merged in the workgroup
+    (3, 5, 5, 333, "f16", 512),       # one ragged split per head, written without a merge
+    (2, 3, 3, 45, "f32", 1024),       # one split shorter than a stage
 ]
 
 
