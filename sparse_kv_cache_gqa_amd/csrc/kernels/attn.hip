@@ -15,7 +15,11 @@
 //     operand hold the G query heads, each split into several bf16/fp16 terms
 //     (hi + mid + lo) when q is fp32, so the products are exact and the sum is
 //     fp32-accurate; for a uint4 cache the rows also separate the two
-//     64-channel quantization groups so their scales can be applied after.
+//     64-channel quantization groups so their scales can be applied after,
+//     and the codes enter as the exact fp16 values 1 + c/16.  With one query
+//     head per KV head (uint4, MHA) q fills all 16 rows, so every lane group
+//     receives scores and each lane scores the token whose min/scale words it
+//     loaded itself (no metadata shuffles; the tile max by DPP).
 //   * P.V runs on the VALU in fp32: each lane owns a fixed set of channels and
 //     accumulates them over the tokens it loads (16-byte coalesced loads).
 //   * Online softmax per 32-token tile in base 2 (exp2 with log2(e) folded

@@ -189,4 +189,3 @@ def test_in_workgroup_merge_equals_merge_kernel_bitwise(da, B, Hq, Hkv, D, N, qd
     b = two.cpu().numpy()
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     assert_close(a, oracle_of(c), atol=1e-5, rel_rms=1e-4, what=f"fused B{B} N{N}")
-
