@@ -53,6 +53,7 @@ def up(arr, dtype, torch, np):
     return t.cuda()
 
 
+READ_GROUPS = 2048  # workgroups of the plain streaming read (da_read_stream)
 MIN_WARM_S = 0.25   # the GPU clock ramps up over the first tens of ms of work
 
 
@@ -180,6 +181,16 @@ def bench_dense(args, torch, np, da, synth):
 
     ms_merge = time_each(torch, merge, args.steps)
 
+    # practical read ceiling: one pass over 1 GiB (the partial pass's size) per
+    # call, rotating over three buffers so the 256 MB last-level cache cannot
+    # serve a repeat; 2048 single-wave groups (measured best of 1024..16384)
+    bufs = [torch.empty(1 << 30, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    sink = torch.empty(READ_GROUPS, dtype=torch.int32, device="cuda")
+    ms_read = time_events(torch, lambda i: da.da_read_stream(bufs[i % 3], n_groups=READ_GROUPS, sink=sink),
+                          args.steps, args.warmup)
+    read_gbs = (1 << 30) / (ms_read * 1e-3) / 1e9
+    del bufs
+
     kv_bytes = 2 * B * Hkv * N * D * 2
     q_bytes = B * Hq * D * 4
     o_bytes = B * Hq * D * 4
@@ -192,9 +203,11 @@ def bench_dense(args, torch, np, da, synth):
         "step_bytes": step_bytes, "partial_ms": ms_partial, "partial_bytes": part_bytes,
         "partial_gbs": part_gbs, "merge_ms": ms_merge, "n_split": ns,
         "eager_ms_per_step": ms_eager, "launch": "eager" if args.no_graph else "hip-graph, 2 steps per replay",
+        "measured_read_peak_gbs": read_gbs,
     }
     log(f"dense: {ms * 1e3:.1f} us/step (eager {ms_eager * 1e3:.1f}), {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s); "
-        f"partial pass {ms_partial * 1e3:.1f} us ({part_gbs:.0f} GB/s), merge {ms_merge * 1e3:.1f} us")
+        f"partial pass {ms_partial * 1e3:.1f} us ({part_gbs:.0f} GB/s), merge {ms_merge * 1e3:.1f} us; "
+        f"plain streaming read {read_gbs:.0f} GB/s")
     return c, res
 
 
@@ -785,7 +798,9 @@ def main(argv=None) -> int:
                      "unit": "GB/s", "frac": dense["partial_gbs"] / HBM_PEAK_GBS,
                      "traffic": measured_traffic("attn_split_llama3_8b_32k", dense["partial_bytes"]),
                      "kernel": "attn_split_kernel (split-K partial pass)",
-                     "bytes_per_launch": dense["partial_bytes"], "avg_launch_ms": dense["partial_ms"]},
+                     "bytes_per_launch": dense["partial_bytes"], "avg_launch_ms": dense["partial_ms"],
+                     "measured_read_peak": dense["measured_read_peak_gbs"],
+                     "frac_of_measured_read_peak": dense["partial_gbs"] / dense["measured_read_peak_gbs"]},
         "cpu_baseline": cpu,
         "detail": {k: v for k, v in dense.items() if k not in ("gbs",)},
         "extra": extra,

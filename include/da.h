@@ -369,6 +369,21 @@ da_status da_stream_append(da_stream_ctx *c, int32_t n_layers,
                            hipStream_t stream);
 void da_stream_destroy(da_stream_ctx *c);
 
+/* ------------------------------------------------------------------------
+ * Measurement aid (not part of the attention method): the practical HBM read
+ * bandwidth that the decode kernels' byte rates are set against, beside the
+ * published peak.  da_read_stream reads `bytes` (a positive multiple of 16,
+ * at most 2^40) of device memory at `buf` (16-byte aligned) exactly once with
+ * non-temporal 16-byte loads, as n_groups single-wave workgroups (1..65535,
+ * at most bytes/16) that each stream one contiguous chunk of
+ * floor(bytes/16/n_groups) 16-byte units (the last also takes the rest), and
+ * writes the XOR of each chunk's 32-bit words to sink[g] (device, n_groups
+ * uint32, caller-owned).  Bad arguments: DA_E_INVALID; launch failure:
+ * DA_E_HIP.  Asynchronous on `stream`.
+ * ------------------------------------------------------------------------ */
+da_status da_read_stream(const void *buf, uint64_t bytes, int32_t n_groups,
+                         uint32_t *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

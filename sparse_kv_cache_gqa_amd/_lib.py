@@ -68,6 +68,7 @@ SIGNATURES = {
     "da_stream_set_length": (ctypes.c_int, [c_vp, ctypes.c_int64]),
     "da_stream_append": (ctypes.c_int, [c_vp, c_i32, c_vp, c_vp, _P(c_vp), _P(c_vp), c_vp]),
     "da_stream_destroy": (None, [c_vp]),
+    "da_read_stream": (ctypes.c_int, [c_vp, ctypes.c_uint64, c_i32, c_vp, c_vp]),
 }
 
 _lib = None

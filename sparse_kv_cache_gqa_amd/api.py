@@ -129,6 +129,20 @@ def da_decode_attention_partials(q, k, v, scale=None, split_tokens=0, ws=None, s
     return ws
 
 
+def da_read_stream(buf, n_groups=4096, sink=None, stream=None):
+    """Measurement aid: read every byte of the device tensor `buf` once
+    (non-temporal, n_groups contiguous chunks); returns sink [n_groups] uint32,
+    the XOR of each chunk's 32-bit words."""
+    lib = load()
+    _dev(buf, sink)
+    nb = _nbytes(buf)
+    if sink is None:
+        sink = torch.empty(n_groups, dtype=torch.int32, device=buf.device)
+    _expect(sink, (n_groups,), torch.int32, "sink")
+    check(lib.da_read_stream(_vp(buf), nb, n_groups, _vp(sink), _stream(stream)))
+    return sink
+
+
 def da_merge_partials(partials, out=None, stream=None):
     """partials [..., n_split, D+4] fp32 -> o [..., D] fp32."""
     lib = load()

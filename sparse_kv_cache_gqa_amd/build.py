@@ -28,6 +28,7 @@ SOURCES = [
     "csrc/kernels/kv4.hip",
     "csrc/kernels/prefill.hip",
     "csrc/kernels/append.hip",
+    "csrc/kernels/read_stream.hip",
 ]
 
 ARCH = "gfx950"

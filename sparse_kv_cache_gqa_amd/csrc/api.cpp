@@ -212,6 +212,18 @@ da_status da_merge_partials(int64_t rows, int32_t n_split, int32_t head_dim, con
     return ok();
 }
 
+da_status da_read_stream(const void *buf, uint64_t bytes, int32_t n_groups, uint32_t *sink, hipStream_t stream) {
+    if (bytes == 0 || bytes % 16 != 0) return fail(DA_E_INVALID, "bytes %llu: a positive multiple of 16", (unsigned long long)bytes);
+    if (bytes > (1ull << 40)) return fail(DA_E_INVALID, "bytes %llu > 2^40", (unsigned long long)bytes);
+    if (n_groups < 1 || n_groups > 65535 || (uint64_t)n_groups > bytes / 16)
+        return fail(DA_E_INVALID, "n_groups %d: in [1, 65535] and at most bytes / 16", n_groups);
+    DA_TRY(check_ptr(buf, "buf"));
+    if (!sink) return fail(DA_E_INVALID, "sink is NULL");
+    hipError_t e = launch_read_stream(buf, (int64_t)(bytes / 16), n_groups, sink, stream);
+    if (e != hipSuccess) return hip_fail(e, "read launch");
+    return ok();
+}
+
 da_status da_build_page_meta(const da_attn_shape *s, int32_t page_size, const void *k, void *kmin, void *kmax,
                              hipStream_t stream) {
     DA_TRY(check_shape(s, false));

@@ -109,6 +109,7 @@ hipError_t launch_prefill(int fmt, int64_t B, int32_t Hq, int32_t Hkv, int D, in
                           hipStream_t stream);
 
 // uint4 group quantization.
+hipError_t launch_read_stream(const void *buf, int64_t n16, int32_t n_groups, uint32_t *sink, hipStream_t stream);
 hipError_t launch_quantize_kv4(int64_t n_groups, const void *x, uint8_t *codes,
                                void *gmin, void *gscale, hipStream_t stream);
 hipError_t launch_dequantize_kv4(int64_t n_groups, const uint8_t *codes,

@@ -209,6 +209,19 @@ def test_kv4_checks(lib):
     assert ws(batch=16, n_q_heads=64, n_kv_heads=64, n_ctx=4096, split_tokens=1024) == 1024 * 4 * 132 * 4
 
 
+def test_read_stream_checks(lib):
+    r = lambda buf=FAKE, nb=1 << 20, g=16, sink=FAKE: lib.da_read_stream(buf, nb, g, sink, NULL)
+    assert r(nb=0) == L.DA_E_INVALID
+    assert r(nb=1000) == L.DA_E_INVALID                 # not a multiple of 16
+    assert r(nb=(1 << 40) + 16) == L.DA_E_INVALID
+    assert r(g=0) == L.DA_E_INVALID
+    assert r(g=65536) == L.DA_E_INVALID
+    assert r(nb=160, g=11) == L.DA_E_INVALID            # more groups than 16-byte units
+    assert r(buf=NULL) == L.DA_E_INVALID
+    assert r(buf=MISALIGNED) == L.DA_E_INVALID
+    assert r(sink=NULL) == L.DA_E_INVALID
+
+
 def test_headwise_sizes_match_the_pages_and_checks(lib):
     # Llama-3-8B, 1M tokens, bf16: one head's K+V is 512 MiB; a layer is 4 GiB
     s = shape(batch=1, n_ctx=1 << 20)
