@@ -91,13 +91,23 @@ __device__ __forceinline__ u32x4 ld_stream(const char *p) {
 // qk_dim(): output k moves nibbles k and k + 4 (bits 4k, 4k + 16) to mantissa
 // bits 6..9 of its two halves, under the exponent of 1.0.  A dot product with
 // them is sum(q) + sum(q c)/16, so sum(q c) = 16 (dot - sum(q)).
+// (m << SH) | one in one VALU instruction: the shift is an inline constant
+// and `one` a scalar register, so no vector register holds a constant
+template <int SH>
+__device__ __forceinline__ uint32_t lshl_or(uint32_t m, uint32_t one) {
+    uint32_t r;
+    asm("v_lshl_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "n"(SH), "s"(one));
+    return r;
+}
 __device__ __forceinline__ u32x4 u4_to_f16x8(uint32_t x) {
-    constexpr uint32_t kMant = 0x03C003C0u, kOne = 0x3C003C00u;
+    constexpr uint32_t kLo = 0x000F000Fu, kHi = 0x00F000F0u;
+    const uint32_t one = __builtin_amdgcn_readfirstlane(0x3C003C00u);
+    const uint32_t y = x >> 8;
     u32x4 r;
-    r[0] = ((x << 6) & kMant) | kOne;
-    r[1] = ((x << 2) & kMant) | kOne;
-    r[2] = ((x >> 2) & kMant) | kOne;
-    r[3] = ((x >> 6) & kMant) | kOne;
+    r[0] = lshl_or<6>(x & kLo, one);     // nibbles 0, 4
+    r[1] = lshl_or<2>(x & kHi, one);     // nibbles 1, 5
+    r[2] = lshl_or<6>(y & kLo, one);     // nibbles 2, 6
+    r[3] = lshl_or<2>(y & kHi, one);     // nibbles 3, 7
     return r;
 }
 
