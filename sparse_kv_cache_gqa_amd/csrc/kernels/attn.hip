@@ -120,7 +120,8 @@ struct Stage {
     bool kok[C::TS];
     // uint4: the fp16 (min, min) / (scale, scale) pairs of both groups of the
     // K and V rows of stage token (lane mod tile), one coalesced dword each;
-    // the lanes that use a token's pair fetch it with a lane shuffle
+    // with several query heads the lanes that use a token's pair fetch it
+    // with a lane shuffle, with one head each lane scores its own token
     uint32_t mk, sk, mv, sv;
 };
 
