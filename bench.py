@@ -320,9 +320,54 @@ def bench_sparse(args, torch, np, da, synth):
         f"gather {ms_gather * 1e3:.1f} us, dense on same cache {ms_dense * 1e3:.1f} us")
     if not args.no_sweep:
         res["page_size_sweep"] = sparse_sweep(args, torch, da, q, copies, B, H, D, N)
+        res["page_reuse_sweep"] = reuse_sweep(args, torch, np, da, q, copies[0], B, H, D, N, S, K)
     if host is not None:
         res["cpu_baseline"] = cpu_sparse(host, S, K, step_bytes / B)
     return res
+
+
+def reuse_lists(np, BH, P, K, overlap, seed):
+    """Two page lists per head (ascending, K of P pages each) sharing exactly
+    round(overlap * K) pages: the kept pages of list 0 plus fresh ones."""
+    rng = np.random.default_rng(seed)
+    a = np.empty((BH, K), dtype=np.int32)
+    b = np.empty((BH, K), dtype=np.int32)
+    keep = int(round(overlap * K))
+    for r in range(BH):
+        perm = rng.permutation(P)
+        first, rest = perm[:K], perm[K:]
+        a[r] = np.sort(first)
+        b[r] = np.sort(np.concatenate([first[:keep], rest[:K - keep]]))
+    return a, b
+
+
+def reuse_sweep(args, torch, np, da, q, kv, B, H, D, N, S, K):
+    """TinyServe's cross-step reuse: consecutive steps attend page lists that
+    share a fraction of their pages (the model loads only rho K pages anew,
+    rho = 1 - overlap).  Sparse attention alone, on one KV copy, the two lists
+    alternating, at the full batch (kept K/V 268 MB per step, above the
+    256 MB last-level cache)."""
+    rows = []
+    P = N // S
+    ws = torch.zeros(1 << 26, dtype=torch.uint8, device="cuda")
+    kk, vv = kv
+    for b in (B,):
+        qb, kb, vb = q[:b], kk[:b], vv[:b]
+        out = torch.empty((b, H, D), dtype=torch.float32, device="cuda")
+        for overlap in (1.0, 0.9, 0.5, 0.25, 0.0):
+            la, lb = reuse_lists(np, b * H, P, K, overlap, [42, 33, b, int(overlap * 100)])
+            lists = [torch.from_numpy(x.reshape(b, H, K)).cuda() for x in (la, lb)]
+
+            def step(i):
+                da.da_decode_attention_paged(qb, kb, vb, lists[i & 1], S, out=out, ws=ws)
+
+            ms = time_graph(torch, step, max(10, args.steps // 2), 4)
+            kv_bytes = b * H * 2 * K * S * D * 2
+            rows.append({"batch": b, "overlap": overlap, "rho": 1.0 - overlap, "ms_per_step": ms,
+                         "kept_kv_bytes": kv_bytes, "gbs_of_kept_kv": kv_bytes / (ms * 1e-3) / 1e9})
+    log("page-reuse sweep (sparse attention): " + ", ".join(
+        f"B{r['batch']} overlap {r['overlap']:.1f} {r['ms_per_step'] * 1e3:.1f}us" for r in rows))
+    return rows
 
 
 def sparse_sweep(args, torch, da, q, copies, B, H, D, N):
