@@ -272,14 +272,25 @@ def bench_sparse(args, torch, np, da, synth):
     wsz = 4 * B * H * D
     ws = torch.zeros(1 << 24, dtype=torch.uint8, device="cuda")
 
+    # the step: TinyServe's decode step in one call (bound scores, top-K
+    # pages, attention over them); the two-call route (da_select_pages, then
+    # da_decode_attention_paged) is timed beside it
     def step(i):
+        kk, vv = copies[i & 1]
+        mn, mx = metas[i & 1]
+        da.da_decode_attention_sparse(q, mn, mx, kk, vv, S, K, out=out)
+
+    ms_eager = time_events(torch, step, args.steps, args.warmup)
+    ms = ms_eager if args.no_graph else time_graph(torch, step, args.steps, args.warmup)
+    ms_kernel = time_each(torch, step, args.steps)
+
+    def two(i):
         kk, vv = copies[i & 1]
         mn, mx = metas[i & 1]
         da.da_select_pages(q, mn, mx, S, K, N, page_idx=idx)
         da.da_decode_attention_paged(q, kk, vv, idx, S, out=out, ws=ws)
 
-    ms_eager = time_events(torch, step, args.steps, args.warmup)
-    ms = ms_eager if args.no_graph else time_graph(torch, step, args.steps, args.warmup)
+    ms_two = time_graph(torch, two, args.steps, args.warmup)
 
     def sel(i):
         mn, mx = metas[i & 1]
@@ -292,6 +303,7 @@ def bench_sparse(args, torch, np, da, synth):
         da.da_decode_attention_paged(q, kk, vv, idx, S, out=out, ws=ws)
 
     ms_gather = time_each(torch, gather, args.steps)
+
     wsd = torch.zeros(1 << 26, dtype=torch.uint8, device="cuda")
 
     def dense(i):
@@ -301,7 +313,8 @@ def bench_sparse(args, torch, np, da, synth):
     ms_dense = time_events(torch, dense, max(5, args.steps // 4), 2)
     meta_bytes = 2 * B * H * P * D * 2
     sel_kv_bytes = 2 * B * H * K * S * D * 2
-    step_bytes = meta_bytes + sel_kv_bytes + B * H * D * 2 + wsz + 2 * B * H * K * 4
+    step_bytes = meta_bytes + sel_kv_bytes + B * H * D * 2 + wsz      # one call: no page list in HBM
+    two_bytes = step_bytes + 2 * B * H * K * 4                       # + page lists written and read
     gbs = step_bytes / (ms * 1e-3) / 1e9
     res = {
         "workload": "tinyserve-page-sparse B32 H16 D64 N32768 fp16 page16 top128",
@@ -311,13 +324,18 @@ def bench_sparse(args, torch, np, da, synth):
         "gather_attention_ms": ms_gather,
         "gather_gbs": (sel_kv_bytes + B * H * D * 6) / (ms_gather * 1e-3) / 1e9,
         "page_meta_ms": ms_meta, "dense_same_cache_ms": ms_dense, "eager_ms_per_step": ms_eager,
+        "kernel": "select_kernel (bound scores, top-K pages, attention over their tokens)",
+        "avg_launch_ms": ms_kernel, "kernel_gbs": step_bytes / (ms_kernel * 1e-3) / 1e9,
+        "two_call_ms_per_step": ms_two, "two_call_step_bytes": two_bytes,
+        "two_call_gbs": two_bytes / (ms_two * 1e-3) / 1e9,
         "speedup_vs_dense": ms_dense / ms,
-        "traffic": {"select": measured_traffic("select_tinyserve_32k", meta_bytes + B * H * D * 2),
+        "traffic": {"one_kernel": measured_traffic("page_attention_tinyserve_32k", step_bytes),
+                    "select": measured_traffic("select_tinyserve_32k", meta_bytes + B * H * D * 2),
                     "gather_attention": measured_traffic("attn_split_paged_tinyserve_32k",
                                                          sel_kv_bytes + B * H * D * 2)},
     }
-    log(f"sparse: {ms * 1e3:.1f} us/step ({gbs:.0f} GB/s), select {ms_sel * 1e3:.1f} us, "
-        f"gather {ms_gather * 1e3:.1f} us, dense on same cache {ms_dense * 1e3:.1f} us")
+    log(f"sparse: {ms * 1e3:.1f} us/step in one kernel ({gbs:.0f} GB/s); two calls {ms_two * 1e3:.1f} us "
+        f"(select {ms_sel * 1e3:.1f} us, gather {ms_gather * 1e3:.1f} us); dense on same cache {ms_dense * 1e3:.1f} us")
     if not args.no_sweep:
         res["page_size_sweep"] = sparse_sweep(args, torch, da, q, copies, B, H, D, N)
         res["page_reuse_sweep"] = reuse_sweep(args, torch, np, da, q, copies[0], B, H, D, N, S, K)

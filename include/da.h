@@ -246,6 +246,30 @@ da_status da_decode_attention_paged(const da_attn_shape *s, int32_t page_size,
                                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * TinyServe's whole decode step for one query (its Algorithm 1: given q, the
+ * page metadata and the KV cache, return o) in one kernel: per (batch row,
+ * head) the bound scores of all pages (as da_select_pages), the top_k of
+ * them, the exact scores q . k of the tokens of the kept pages, and
+ *   o = sum_t softmax(scale * q . k_t) v_t over those tokens only
+ * (as da_decode_attention_paged on the same page list; positions at or beyond
+ * n_ctx in a partial last page are skipped).  Reads the metadata once and
+ * only the kept pages' K and V rows.  No workspace.
+ *   q, k, v, o   as for da_decode_attention (n_q_heads == n_kv_heads)
+ *   kmin, kmax   as written by da_build_page_meta with this page_size
+ *   page_idx     [batch][n_q_heads][top_k] int32, device, or NULL (written
+ *                if given: the kept pages, ascending, as da_select_pages)
+ * Requires 1 <= top_k <= P = ceil(n_ctx / page_size) <= 8192 and
+ * P + top_k + 2 top_k page_size + 16 head_dim <= 16384 (page scores, the
+ * kept list and two floats per kept token stay in LDS); DA_E_UNSUPPORTED
+ * otherwise.
+ * ------------------------------------------------------------------------ */
+da_status da_decode_attention_sparse(const da_attn_shape *s, int32_t page_size,
+                                     int32_t top_k, const void *q,
+                                     const void *kmin, const void *kmax,
+                                     const void *k, const void *v, float *o,
+                                     int32_t *page_idx, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * uint4 group quantization (FlexGen 4-bit, groups of 64 along the hidden
  * dimension).  For each row and each group of 64 contiguous fp16 values:
  *   min = minimum, max = maximum,

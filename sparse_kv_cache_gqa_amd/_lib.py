@@ -69,6 +69,8 @@ SIGNATURES = {
     "da_stream_append": (ctypes.c_int, [c_vp, c_i32, c_vp, c_vp, _P(c_vp), _P(c_vp), c_vp]),
     "da_stream_destroy": (None, [c_vp]),
     "da_read_stream": (ctypes.c_int, [c_vp, ctypes.c_uint64, c_i32, c_vp, c_vp]),
+    "da_decode_attention_sparse": (ctypes.c_int, [SHAPE, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                                  c_vp]),
 }
 
 _lib = None

@@ -285,6 +285,31 @@ def da_decode_attention_paged(q, k, v, page_idx, page_size, scale=None, split_to
     return out
 
 
+def da_decode_attention_sparse(q, kmin, kmax, k, v, page_size, top_k, scale=None, out=None,
+                               page_idx=None, want_idx=False, stream=None):
+    """Page selection and attention over the kept pages in one kernel
+    (TinyServe's decode step); fp32 [B][H][D], and the kept pages
+    [B][H][top_k] int32 when want_idx (or page_idx) is given."""
+    lib = load()
+    _dev(q, kmin, kmax, k, v, out, page_idx)
+    s = _dense_shape(q, k, scale, 0)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must have the same shape and dtype")
+    B, H, N, D = k.shape
+    P = -(-N // page_size)
+    _expect(kmin, (B, H, P, D), k.dtype, "kmin")
+    _expect(kmax, (B, H, P, D), k.dtype, "kmax")
+    _expect(out, q.shape, torch.float32, "out")
+    _expect(page_idx, (q.shape[0], q.shape[1], top_k), torch.int32, "page_idx")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if page_idx is None and want_idx:
+        page_idx = torch.empty((q.shape[0], q.shape[1], top_k), dtype=torch.int32, device=q.device)
+    check(lib.da_decode_attention_sparse(ctypes.byref(s), page_size, top_k, _vp(q), _vp(kmin), _vp(kmax),
+                                         _vp(k), _vp(v), _vp(out), _vp(page_idx), _stream(stream)))
+    return (out, page_idx) if (want_idx or page_idx is not None) else out
+
+
 def da_quantize_kv4(x, codes=None, gmin=None, gscale=None, stream=None):
     """fp16 [..., R] -> (codes uint8 [..., R/2], min fp16 [..., R/64], scale fp16 [..., R/64])."""
     lib = load()

@@ -308,6 +308,37 @@ da_status da_decode_attention_topk(const da_attn_shape *s, int32_t top_k, const 
     return ok();
 }
 
+da_status da_decode_attention_sparse(const da_attn_shape *s, int32_t page_size, int32_t top_k, const void *q,
+                                     const void *kmin, const void *kmax, const void *k, const void *v, float *o,
+                                     int32_t *page_idx, hipStream_t stream) {
+    DA_TRY(check_shape(s, false));
+    DA_TRY(check_page(page_size));
+    if (s->n_q_heads != s->n_kv_heads)
+        return fail(DA_E_UNSUPPORTED, "page-sparse attention needs n_q_heads == n_kv_heads");
+    const int64_t P = n_pages(s, page_size);
+    if (top_k < 1 || top_k > P) return fail(DA_E_INVALID, "top_k %d not in [1, %lld]", top_k, (long long)P);
+    if (P > 8192) return fail(DA_E_UNSUPPORTED, "%lld pages > 8192 per head", (long long)P);
+    const int64_t lds = page_attention_lds_floats(P, top_k, ilog2(page_size), s->head_dim, 16);
+    if (lds > kPageAttnLdsFloats)
+        return fail(DA_E_UNSUPPORTED, "P + top_k + 2 top_k page_size + 16 head_dim = %lld > %lld", (long long)lds,
+                    (long long)kPageAttnLdsFloats);
+    if (s->batch == 0) return ok();
+    DA_TRY(check_ptr(q, "q"));
+    DA_TRY(check_ptr(kmin, "kmin"));
+    DA_TRY(check_ptr(kmax, "kmax"));
+    DA_TRY(check_ptr(k, "k"));
+    DA_TRY(check_ptr(v, "v"));
+    DA_TRY(check_ptr(o, "o"));
+    if (page_idx && !aligned16(page_idx)) return fail(DA_E_INVALID, "page_idx is not 16-byte aligned");
+    if (!select_supported(s->kv_dtype, s->q_dtype, s->head_dim))
+        return fail(DA_E_UNSUPPORTED, "no selection kernel for this dtype / head_dim");
+    hipError_t e = launch_page_attention(s->kv_dtype, s->q_dtype, (int64_t)s->batch * s->n_q_heads, s->n_ctx, P,
+                                         s->head_dim, ilog2(page_size), top_k, s->scale * 1.4426950408889634f, q,
+                                         kmin, kmax, k, v, o, page_idx, stream);
+    if (e != hipSuccess) return hip_fail(e, "page-sparse attention launch");
+    return ok();
+}
+
 da_status da_prefill_attention(const da_attn_shape *s, int64_t chunk, const void *q, const void *k, const void *v,
                                float *o, hipStream_t stream) {
     DA_TRY(check_shape(s, false));

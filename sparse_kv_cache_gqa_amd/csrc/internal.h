@@ -101,6 +101,19 @@ hipError_t launch_topk_attention(int kv_fmt, int q_fmt, int64_t BH, int64_t N, i
                                  float scale_log2, const void *q, const void *k, const void *v, float *o,
                                  int32_t *token_idx, hipStream_t stream);
 
+// Page selection fused with attention over the kept pages' tokens (one
+// 1024-thread workgroup per (b, h)): bound scores, top-K pages, exact scores
+// of their K * 2^log2_page token slots, softmax and the value rows; o
+// [BH][D] fp32; page_idx optional.  Dynamic LDS: P page scores, K page
+// indices, two floats per token slot, 16 * D partial sums.
+inline int64_t page_attention_lds_floats(int64_t P, int64_t top_k, int log2_page, int D, int n_waves) {
+    return P + top_k + 2 * (top_k << log2_page) + (int64_t)n_waves * D;
+}
+constexpr int64_t kPageAttnLdsFloats = 16384;   // 64 KiB of dynamic LDS
+hipError_t launch_page_attention(int kv_fmt, int q_fmt, int64_t BH, int64_t N, int64_t P, int D, int log2_page,
+                                 int top_k, float scale_log2, const void *q, const void *kmin, const void *kmax,
+                                 const void *k, const void *v, float *o, int32_t *page_idx, hipStream_t stream);
+
 // Chunked prefill attention: q [B][Hq][C][D], k/v [B][Hkv][T][D] (T = prefix
 // + C), o [B][Hq][C][D] fp32; q, k and v in `fmt` (bf16 or fp16).
 bool prefill_supported(int fmt, int D);

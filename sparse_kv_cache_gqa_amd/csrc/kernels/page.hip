@@ -117,15 +117,20 @@ __global__ __launch_bounds__(256) void page_meta_kernel(int64_t BH, int64_t N, i
 
 // Selection modes: bound scores over pages; exact scores over tokens; exact
 // scores over tokens followed by attention over the kept tokens.
-enum SelMode : int { SEL_PAGES = 0, SEL_TOKENS = 1, SEL_ATTEND = 2 };
+// SEL_PAGES: bound scores + top-K pages.  SEL_TOKENS: exact scores + top-K
+// tokens.  SEL_ATTEND: SEL_TOKENS, then attention over the kept tokens.
+// SEL_PAGE_ATTEND: SEL_PAGES, then attention over the tokens of the kept
+// pages (TinyServe's whole decode step for one head in one workgroup).
+enum SelMode : int { SEL_PAGES = 0, SEL_TOKENS = 1, SEL_ATTEND = 2, SEL_PAGE_ATTEND = 3 };
 
+constexpr bool sel_paged(int mode) { return mode == SEL_PAGES || mode == SEL_PAGE_ATTEND; }
 // Threads per workgroup (measured on MI355X): 1024 for pages (P = 2048 at
 // the TinyServe shape), 512 for tokens (P = 1024 at the FlexGen shape).
-constexpr int sel_threads(int mode) { return mode == SEL_PAGES ? 1024 : 512; }
+constexpr int sel_threads(int mode) { return sel_paged(mode) ? 1024 : 512; }
 // 16-byte loads per lane and array in flight per scoring trip (measured on
 // MI355X): 2 for pages (two arrays; more costs the 1024-thread workgroups
 // their second slot per CU), 4 for tokens.
-constexpr int sel_loads(int mode) { return mode == SEL_PAGES ? 2 : 4; }
+constexpr int sel_loads(int mode) { return sel_paged(mode) ? 2 : 4; }
 
 struct SelArgs {
     int64_t P = 0;                 // pages (or tokens) per (b, h)
@@ -137,6 +142,9 @@ struct SelArgs {
     const uint8_t *v = nullptr;    // SEL_ATTEND: value rows, laid out as the keys
     float *o = nullptr;            // SEL_ATTEND: [BH][D] fp32
     float scale_log2 = 0.f;        // SEL_ATTEND: softmax scale * log2(e)
+    const uint8_t *k = nullptr;    // SEL_PAGE_ATTEND: key rows [BH][N][D] (v likewise)
+    int64_t N = 0;                 // SEL_PAGE_ATTEND: tokens per head
+    int32_t log2_page = 0;         // SEL_PAGE_ATTEND: page = 2^log2_page tokens
 };
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -192,56 +200,64 @@ __device__ __forceinline__ float block_reduce(float x, float *buf) {
     return r;
 }
 
-// Attention of one (b, h) over its kept tokens (FlexGen's top-k sparse
-// attention, section "方法细节": only the V rows of the kept keys are read).
-// The exact scores of the kept tokens are still in LDS: with M their maximum,
-// w_i = 2^((s_i - M) * scale * log2 e), o = sum_i w_i v_i / sum_i w_i.
+// Attention of one (b, h) over n selected items: item i has its score
+// score(i) in LDS (the raw q . k; -inf for a slot that holds no token) and
+// its value row row_of(i).  With M the maximum score,
+// w_i = 2^((s_i - M) * scale * log2 e), o = sum_i w_i v_i / sum_i w_i (FlexGen's
+// top-k sparse attention, section "方法细节": only the kept tokens' V rows are
+// read; TinyServe, section "方法细节", SparseAttn over the selected pages).
 // Threads own 16-byte column chunks of the value rows; workgroup slots of CH
-// lanes walk the kept list; the slots are summed through LDS.
-template <int KF, int D, int NW>
-__device__ __forceinline__ void attend_kept(const SelArgs &args, int64_t bh, const int32_t *kept,
-                                            const float *sc_lds, uint32_t *scan_buf) {
+// lanes walk the items, four loads in flight per slot (the items of a slot in
+// ascending order, one fma chain per channel); the slots are summed by lane
+// shuffles within a wave and through LDS across waves.
+template <int KF, int D, int NW, typename ScoreF, typename RowF>
+__device__ __forceinline__ void attend_items(const SelArgs &args, int64_t bh, int n, int64_t rows_per_head,
+                                             ScoreF score, RowF row_of, float *wl, float *red,
+                                             uint32_t *scan_buf) {
     constexpr int R = D * Elem<KF>::size;
     constexpr int EPC = 16 / Elem<KF>::size;    // values per 16-byte chunk
     constexpr int CH = R / 16;                  // chunks (lanes) per row
     constexpr int NT = NW * 64;
     constexpr int SLOTS = NT / CH;
+    constexpr int UNR = 4;
     const int tid = threadIdx.x;
-    const int K = args.top_k;
-    const int64_t P = args.P;
-    float *wl = (float *)(kept + K);            // weights [K]
-    float *red = wl + K;                        // [NW][D]
     float *fbuf = (float *)scan_buf;
-    __syncthreads();                            // kept[] complete
+    __syncthreads();                            // the items and their scores are complete
 
-    // kept[] holds exactly K indices in [0, P); the clamp only guards memory
-    auto kept_at = [&](int i) -> int64_t {
-        const int32_t t = kept[i];
-        return (t >= 0 && t < P) ? t : 0;
-    };
     float m = -__builtin_inff();
-    for (int i = tid; i < K; i += NT) m = fmaxf(m, sc_lds[kept_at(i)]);
+    for (int i = tid; i < n; i += NT) m = fmaxf(m, score(i));
     const float M = block_reduce<NW, true>(m, fbuf);
     float lsum = 0.f;
-    for (int i = tid; i < K; i += NT) {
-        const float w = exp2f((sc_lds[kept_at(i)] - M) * args.scale_log2);
+    for (int i = tid; i < n; i += NT) {
+        const float w = exp2f((score(i) - M) * args.scale_log2);
         wl[i] = w;
         lsum += w;
     }
     const float L = block_reduce<NW, false>(lsum, fbuf);   // also orders wl[] before use
 
     const int ch = tid % CH, slot = tid / CH;
-    const uint8_t *vb = args.v + bh * P * R + 16 * ch;
+    const uint8_t *vb = args.v + bh * rows_per_head * R + 16 * ch;
     float acc[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
-    for (int i = slot; i < K; i += SLOTS) {
-        const u32x4 x = __builtin_nontemporal_load((const u32x4 *)(vb + kept_at(i) * R));
-        float f[EPC];
-        unpack16<KF>(x, f);
-        const float w = wl[i];
+    for (int i0 = slot; i0 < n; i0 += SLOTS * UNR) {
+        u32x4 x[UNR];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[e] = fmaf(w, f[e], acc[e]);
+        for (int u = 0; u < UNR; ++u) {
+            const int i = i0 + u * SLOTS;
+            x[u] = i < n ? __builtin_nontemporal_load((const u32x4 *)(vb + row_of(i) * R)) : (u32x4){0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int i = i0 + u * SLOTS;
+            if (i < n) {
+                float f[EPC];
+                unpack16<KF>(x[u], f);
+                const float w = wl[i];
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) acc[e] = fmaf(w, f[e], acc[e]);
+            }
+        }
     }
     // sum the slots of each wave (lanes with the same chunk), then the waves
 #pragma unroll
@@ -264,7 +280,7 @@ __device__ __forceinline__ void attend_kept(const SelArgs &args, int64_t bh, con
 
 template <int KF, int QF, int D, int MODE>
 __global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args) {
-    constexpr bool EXACT = MODE != SEL_PAGES;
+    constexpr bool EXACT = !sel_paged(MODE);
     constexpr int kSelThreads = sel_threads(MODE);
     constexpr int kSelWaves = kSelThreads / 64;
     const int64_t P = args.P;
@@ -447,12 +463,68 @@ __global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args)
             if (key == T) { sel = all_ties || r < need; ++r; }
             if (sel && pos < (uint32_t)top_k) {
                 if (out) out[pos] = (int32_t)i;
-                if constexpr (MODE == SEL_ATTEND) kept[pos] = (int32_t)i;
+                if constexpr (MODE == SEL_ATTEND || MODE == SEL_PAGE_ATTEND) kept[pos] = (int32_t)i;
                 ++pos;
             }
         }
     }
-    if constexpr (MODE == SEL_ATTEND) attend_kept<KF, D, kSelWaves>(args, bh, kept, sc_lds, scan_buf);
+    if constexpr (MODE == SEL_ATTEND) {
+        // kept[] holds exactly top_k indices in [0, P); the clamp only guards memory
+        auto row = [&](int i) -> int64_t {
+            const int32_t t = kept[i];
+            return (t >= 0 && t < P) ? t : 0;
+        };
+        float *wl = (float *)(kept + top_k);
+        attend_items<KF, D, kSelWaves>(args, bh, top_k, P, [&](int i) { return sc_lds[row(i)]; }, row, wl,
+                                       wl + top_k, scan_buf);
+    }
+    if constexpr (MODE == SEL_PAGE_ATTEND) {
+        // ---- 4. exact scores of the kept pages' tokens ---------------------
+        // slot t holds token kept[t / S] * S + t mod S; slots past n_ctx (the
+        // last page's tail) score -inf.  Same lane layout as the bound scan,
+        // with q itself (q+ + q-, one of them zero).
+        __syncthreads();                             // kept[] complete
+        const int lg = args.log2_page;
+        const int T = top_k << lg;
+        const int64_t N = args.N;
+        float *tsc = (float *)(kept + top_k);        // [T]
+        float qe[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) qe[e] = qp[e] + qn[e];
+        auto tok = [&](int t) -> int64_t {
+            const int32_t pg = kept[t >> lg];
+            const int64_t r = ((int64_t)(pg >= 0 && pg < P ? pg : 0) << lg) + (t & ((1 << lg) - 1));
+            return r < N ? r : -1;
+        };
+        const uint8_t *kb = args.k + bh * N * R + 16 * piece;
+        for (int base = w * TPT; base < T; base += TPT * kSelWaves) {
+            u32x4 X[NI];
+            int64_t rr[NI];
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int t = base + i * TPI + rin;
+                rr[i] = t < T ? tok(t) : -1;
+                X[i] = rr[i] >= 0 ? __builtin_nontemporal_load((const u32x4 *)(kb + rr[i] * R)) : (u32x4){0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                float fx[EPC];
+                unpack16<KF>(X[i], fx);
+                float s = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) s = fmaf(qe[e], fx[e], s);
+#pragma unroll
+                for (int o = 1; o < PCS; o <<= 1) s += __shfl_xor(s, o, 64);
+                const int t = base + i * TPI + rin;
+                if (piece == 0 && t < T) tsc[t] = rr[i] >= 0 ? s : -__builtin_inff();
+            }
+        }
+        // ---- 5. attention over them ----------------------------------------
+        float *wl = tsc + T;
+        attend_items<KF, D, kSelWaves>(args, bh, T, N, [&](int i) { return tsc[i]; },
+                                       [&](int i) -> int64_t { const int64_t r = tok(i); return r >= 0 ? r : 0; },
+                                       wl, wl + T, scan_buf);
+    }
 }
 
 using SelFn = void (*)(SelArgs);
@@ -485,6 +557,7 @@ SelFn sel_for(int mode, int kv, int qf, int D) {
     case SEL_PAGES: return sel_pick<SEL_PAGES>(kv, qf, D);
     case SEL_TOKENS: return sel_pick<SEL_TOKENS>(kv, qf, D);
     case SEL_ATTEND: return sel_pick<SEL_ATTEND>(kv, qf, D);
+    case SEL_PAGE_ATTEND: return sel_pick<SEL_PAGE_ATTEND>(kv, qf, D);
     default: return nullptr;
     }
 }
@@ -549,6 +622,30 @@ hipError_t launch_topk_attention(int kv_fmt, int q_fmt, int64_t BH, int64_t N, i
     const int nw = sel_threads(SEL_ATTEND) / 64;
     const size_t lds = ((size_t)N + 2 * (size_t)top_k + (size_t)nw * D) * sizeof(float);
     hipLaunchKernelGGL(fn, dim3((unsigned)BH), dim3(sel_threads(SEL_ATTEND)), lds, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_page_attention(int kv_fmt, int q_fmt, int64_t BH, int64_t N, int64_t P, int D, int log2_page,
+                                 int top_k, float scale_log2, const void *q, const void *kmin, const void *kmax,
+                                 const void *k, const void *v, float *o, int32_t *page_idx, hipStream_t stream) {
+    SelFn fn = sel_for(SEL_PAGE_ATTEND, kv_fmt, q_fmt, D);
+    if (!fn) return hipErrorInvalidValue;
+    SelArgs a;
+    a.P = P;
+    a.top_k = top_k;
+    a.q = q;
+    a.kmin = (const uint8_t *)kmin;
+    a.kmax = (const uint8_t *)kmax;
+    a.page_idx = page_idx;
+    a.k = (const uint8_t *)k;
+    a.v = (const uint8_t *)v;
+    a.o = o;
+    a.N = N;
+    a.log2_page = log2_page;
+    a.scale_log2 = scale_log2;
+    const int nw = sel_threads(SEL_PAGE_ATTEND) / 64;
+    const size_t lds = page_attention_lds_floats(P, top_k, log2_page, D, nw) * sizeof(float);
+    hipLaunchKernelGGL(fn, dim3((unsigned)BH), dim3(sel_threads(SEL_PAGE_ATTEND)), lds, stream, a);
     return hipGetLastError();
 }
 

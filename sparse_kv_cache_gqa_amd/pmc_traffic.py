@@ -23,6 +23,7 @@ COPY_KIB = 512 * 1024          # one calibration copy reads and writes 512 MiB
 KERNELS = {                    # short name -> substring of the mangled kernel name
     "attn_split_llama3_8b_32k": "attn_split_kernel<2, 0, 128, 4, false>",
     "select_tinyserve_32k": "select_kernel<1, 1, 64, 0>",
+    "page_attention_tinyserve_32k": "select_kernel<1, 1, 64, 3>",
     "attn_split_paged_tinyserve_32k": "attn_split_kernel<1, 1, 64, 1, true>",
     "attn_split_uint4_flexgen": "attn_split_kernel<3, 1, 128, 1, false>",
     "topk_attention_flexgen": "select_kernel<1, 1, 128, 2>",

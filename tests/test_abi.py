@@ -144,6 +144,17 @@ def test_page_checks(lib):
     need = lib.da_decode_attention_paged_workspace(ctypes.byref(s), 16, 128)
     assert need == 32 * 16 * 4 * 68 * 4           # 128 pages of 16 = 2048 positions / 512
     assert paged(s, 128, need - 4) == L.DA_E_WORKSPACE
+    sp = lambda sh, ps, k, q=FAKE, idx=NULL: lib.da_decode_attention_sparse(
+        ctypes.byref(sh), ps, k, q, FAKE, FAKE, FAKE, FAKE, FAKE, idx, NULL)
+    assert sp(s, 3, 128) == L.DA_E_INVALID                              # page size
+    assert sp(s, 16, 0) == L.DA_E_INVALID
+    assert sp(s, 16, 2049) == L.DA_E_INVALID                            # top_k > P
+    assert sp(mha(n_q_heads=32), 16, 128) == L.DA_E_UNSUPPORTED         # GQA
+    assert sp(mha(n_ctx=16 * 8193), 16, 128) == L.DA_E_UNSUPPORTED      # > 8192 pages
+    assert sp(s, 16, 500) == L.DA_E_UNSUPPORTED      # 2048 + 500 + 2 * 8000 + 16 * 64 > 16384
+    assert sp(s, 16, 128, q=MISALIGNED) == L.DA_E_INVALID
+    assert sp(s, 16, 128, idx=MISALIGNED) == L.DA_E_INVALID
+    assert sp(mha(batch=0), 16, 128) == L.DA_OK
 
 
 def test_token_selection_checks(lib):

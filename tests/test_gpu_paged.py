@@ -70,6 +70,66 @@ def test_select_and_sparse_attention(da, B, H, D, N, S, K, dt):
     assert_close(o.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what=f"sparse {dt} S{S} K{K}")
 
 
+@pytest.mark.parametrize("B,H,D,N,S,K,dt", SEL_CASES)
+def test_fused_select_and_attention(da, B, H, D, N, S, K, dt):
+    """da_decode_attention_sparse (selection and attention in one kernel):
+    the kept pages equal da_select_pages' bit for bit (same scores, same
+    radix select), and the output matches the oracle's sparse attention over
+    that set (tokens past n_ctx in a partial last page skipped)."""
+    import torch
+    c = synth.paged_case([201, B, H, D, N, S, K], B, H, D, N, S, K, dtype=dt)
+    q, k, v = to_dev(c.q, dt), to_dev(c.k, dt), to_dev(c.v, dt)
+    kmin, kmax = da.da_build_page_meta(k, S)
+    two = da.da_select_pages(q, kmin, kmax, S, K, N)
+    o, idx = da.da_decode_attention_sparse(q, kmin, kmax, k, v, S, K, scale=c.scale, want_idx=True)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    assert np.array_equal(idx, two.cpu().numpy())
+    q64, k64, v64 = as_f64(c.q, dt), as_f64(c.k, dt), as_f64(c.v, dt)
+    rmin, rmax = page_meta(k64, S)
+    check_selection(idx, bound_scores(q64, rmin, rmax), K)
+    ref = sparse_attention(q64, k64, v64, idx, S, c.scale)
+    assert_close(o.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what=f"fused sparse {dt} S{S} K{K}")
+
+
+def test_fused_without_page_list(da):
+    """page_idx may be NULL: the same output as with it."""
+    import torch
+    c = synth.paged_case([205], 2, 3, 64, 1000, 16, 5, dtype="f16")
+    q, k, v = to_dev(c.q, "f16"), to_dev(c.k, "f16"), to_dev(c.v, "f16")
+    kmin, kmax = da.da_build_page_meta(k, 16)
+    a = da.da_decode_attention_sparse(q, kmin, kmax, k, v, 16, 5)
+    b, _ = da.da_decode_attention_sparse(q, kmin, kmax, k, v, 16, 5, want_idx=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
+
+
+def test_workload3_fused_full_size_sampled(da):
+    """TinyServe shape in one kernel (as bench.py's fused step): the kept
+    pages equal the two-kernel path's, attention of sampled heads against the
+    oracle on that set."""
+    import torch
+    c = synth.workload3()
+    S, K = c.page_size, c.top_k
+    q, k, v = to_dev(c.q, "f16"), to_dev(c.k, "f16"), to_dev(c.v, "f16")
+    kmin, kmax = da.da_build_page_meta(k, S)
+    two = da.da_select_pages(q, kmin, kmax, S, K, 32768)
+    o, idx = da.da_decode_attention_sparse(q, kmin, kmax, k, v, S, K, want_idx=True)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    assert np.array_equal(idx, two.cpu().numpy())
+    o = o.cpu().numpy()
+    rng = np.random.default_rng(5)
+    picks = [(0, 0), (31, 15)] + [(int(b), int(h)) for b, h in
+                                  zip(rng.integers(0, 32, 6), rng.integers(0, 16, 6))]
+    for b, h in picks:
+        q64 = as_f64(c.q[b:b + 1, h:h + 1], "f16")
+        k64 = as_f64(c.k[b:b + 1, h:h + 1], "f16")
+        v64 = as_f64(c.v[b:b + 1, h:h + 1], "f16")
+        ref = sparse_attention(q64, k64, v64, idx[b:b + 1, h:h + 1], S, c.scale)
+        assert_close(o[b, h], ref[0, 0], atol=1e-3, rel_rms=1e-4, what=f"w3 fused b{b} h{h}")
+
+
 def torch_idx(idx):
     import torch
     return torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).cuda()
