@@ -24,6 +24,12 @@
 //      keys are ranked by a block-wide prefix count in index order (skipped
 //      when every key equal to the K-th is kept).  The kept indices are
 //      compacted in index order, so they come out ascending.
+//   3. Attend modes continue in the same workgroup: token mode weights the
+//      kept tokens' value rows by the softmax of their exact scores, still in
+//      LDS; page mode first scores the tokens of the kept pages exactly (the
+//      same lane layout), then does the same over them -- TinyServe's whole
+//      decode step (Algorithm 1) in one kernel, the kept set and every
+//      intermediate in LDS.
 #include "common.h"
 
 namespace da {
