@@ -502,18 +502,20 @@ __global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args)
             const int64_t r = ((int64_t)(pg >= 0 && pg < P ? pg : 0) << lg) + (t & ((1 << lg) - 1));
             return r < N ? r : -1;
         };
+        // one array here (the bound scan reads two): twice the loads per trip
+        constexpr int NI4 = 2 * NI, TPT4 = NI4 * TPI;
         const uint8_t *kb = args.k + bh * N * R + 16 * piece;
-        for (int base = w * TPT; base < T; base += TPT * kSelWaves) {
-            u32x4 X[NI];
-            int64_t rr[NI];
+        for (int base = w * TPT4; base < T; base += TPT4 * kSelWaves) {
+            u32x4 X[NI4];
+            int64_t rr[NI4];
 #pragma unroll
-            for (int i = 0; i < NI; ++i) {
+            for (int i = 0; i < NI4; ++i) {
                 const int t = base + i * TPI + rin;
                 rr[i] = t < T ? tok(t) : -1;
                 X[i] = rr[i] >= 0 ? __builtin_nontemporal_load((const u32x4 *)(kb + rr[i] * R)) : (u32x4){0u, 0u, 0u, 0u};
             }
 #pragma unroll
-            for (int i = 0; i < NI; ++i) {
+            for (int i = 0; i < NI4; ++i) {
                 float fx[EPC];
                 unpack16<KF>(X[i], fx);
                 float s = 0.f;
