@@ -9,6 +9,7 @@ taking torch tensors.
     kmin, kmax = da.da_build_page_meta(k, 16)            # page bounding boxes
     idx = da.da_select_pages(q, kmin, kmax, 16, 128, N)  # top-K pages
     o = da.da_decode_attention_paged(q, k, v, idx, 16)   # sparse attention
+    o = da.da_decode_attention_sparse(q, kmin, kmax, k, v, 16, 128)  # both in one kernel
     codes, mn, sc = da.da_quantize_kv4(x)                # uint4 groups of 64
     o = da.da_decode_attention_kv4(q, kc, kmn, ksc, vc, vmn, vsc)
     hs = da.HeadwiseStream(...)                          # head-wise streaming
