@@ -105,6 +105,7 @@ KV4_CASES = [
     (4, 64, 64, 1000, "f16", 0),      # 256 heads x 4 splits merged in the workgroup
     (3, 5, 5, 333, "f16", 512),       # one ragged split per head, written without a merge
     (2, 3, 3, 45, "f32", 1024),       # one split shorter than a stage
+    (1, 2, 2, 1, "f16", 0),           # a single token: o = its dequantized value row
 ]
 
 

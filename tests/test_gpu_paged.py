@@ -50,6 +50,7 @@ SEL_CASES = [
     (1, 2, 64, 640, 16, 40, "f32"),        # top_k = P: every page
     (32, 8, 64, 1024, 16, 24, "f16"),      # 256 heads, one split each
     (16, 16, 64, 4096, 16, 100, "f16"),    # 256 heads x 4 splits merged in the workgroup
+    (1, 2, 64, 3000, 1024, 2, "f16"),      # the largest pages: 3, the last 952 tokens
 ]
 
 
