@@ -178,14 +178,15 @@ da_status da_build_page_meta(const da_attn_shape *s, int32_t page_size,
  * Query-aware page selection (TinyServe relevance score and S_t = TopK):
  *   r_j = sum_d (q_d * kmax[j][d] if q_d >= 0 else q_d * kmin[j][d])
  * accumulated in fp32 (products of fp16/bf16 values are exact in fp32), then
- * the top_k largest r_j per (batch row, head); equal scores keep the lower
- * page index; the kept indices are written in ascending order.
+ * the top_k largest r_j per (batch row, query head); equal scores keep the
+ * lower page index; the kept indices are written in ascending order.  With
+ * grouped-query heads each query head j selects its own pages over the
+ * metadata of its KV head j / (n_q_heads / n_kv_heads).
  *   q          [batch][n_q_heads][head_dim]   q_dtype, device
- *   kmin, kmax as written by da_build_page_meta
+ *   kmin, kmax as written by da_build_page_meta ([batch][n_kv_heads][P][D])
  *   page_idx   [batch][n_q_heads][top_k] int32, device (written)
  *   page_score [batch][n_q_heads][P] fp32, device, or NULL (written if given)
- * Requires n_q_heads == n_kv_heads (one selection per head), 1 <= top_k <= P,
- * P <= 8192, page_size a power of two in [1, 1024].
+ * Requires 1 <= top_k <= P, P <= 8192, page_size a power of two in [1, 1024].
  * ------------------------------------------------------------------------ */
 da_status da_select_pages(const da_attn_shape *s, int32_t page_size,
                           int32_t top_k, const void *q, const void *kmin,
@@ -196,16 +197,17 @@ da_status da_select_pages(const da_attn_shape *s, int32_t page_size,
  * Token selection by exact score (FlexGen's top-10% sparse attention keeps,
  * per query, the indices of its best-scoring keys):
  *   s_i = q . k_i accumulated in fp32 (products of fp16/bf16 values exact),
- * then the top_k largest s_i per (batch row, head); equal scores keep the
- * lower token index; the kept indices are written in ascending order.  Reads
- * each key row once.  Attention over the kept tokens is
- * da_decode_attention_paged with page_size 1 and page_idx = token_idx.
+ * then the top_k largest s_i per (batch row, query head), k_i being the keys
+ * of the query head's KV head; equal scores keep the lower token index; the
+ * kept indices are written in ascending order.  Reads each key row once per
+ * query head.  Attention over the kept tokens is da_decode_attention_paged
+ * with page_size 1 and page_idx = token_idx.
  *   q           [batch][n_q_heads][head_dim]          q_dtype, device
  *   k           [batch][n_kv_heads][n_ctx][head_dim]  kv_dtype, device
  *   token_idx   [batch][n_q_heads][top_k] int32, device (written)
  *   token_score [batch][n_q_heads][n_ctx] fp32, device, or NULL (written if
  *               given; unscaled q . k)
- * Requires n_q_heads == n_kv_heads, 1 <= top_k <= n_ctx <= 8192.
+ * Requires 1 <= top_k <= n_ctx <= 8192.
  * ------------------------------------------------------------------------ */
 da_status da_select_tokens(const da_attn_shape *s, int32_t top_k,
                            const void *q, const void *k, int32_t *token_idx,
@@ -213,11 +215,12 @@ da_status da_select_tokens(const da_attn_shape *s, int32_t top_k,
 
 /* ------------------------------------------------------------------------
  * Token-level top-k sparse attention in one kernel (FlexGen's top-10% sparse
- * attention): per (batch row, head) the exact scores s_i = q . k_i of all
- * n_ctx tokens, the top_k of them (as da_select_tokens), then
+ * attention): per (batch row, query head) the exact scores s_i = q . k_i of
+ * all n_ctx tokens of its KV head, the top_k of them (as da_select_tokens),
+ * then
  *   o = sum_i softmax(scale * s_i) v_i over the kept tokens only,
  * reading only the value rows of the kept tokens.  No workspace.
- *   q, k, v, o  as for da_decode_attention (n_q_heads == n_kv_heads)
+ *   q, k, v, o  as for da_decode_attention
  *   token_idx   [batch][n_q_heads][top_k] int32, device, or NULL (written if
  *               given: the kept tokens, ascending)
  * Requires 1 <= top_k <= n_ctx and n_ctx + 2 top_k + 8 head_dim <= 16384
@@ -232,9 +235,10 @@ da_status da_decode_attention_topk(const da_attn_shape *s, int32_t top_k,
  * Sparse attention over the selected pages only (TinyServe SparseAttn):
  * softmax normalised over the tokens of the listed pages; positions at or
  * beyond n_ctx in a partial last page are skipped, and so is any listed page
- * index outside [0, P).
+ * index outside [0, P).  Each query head attends its own list over the
+ * rows of its KV head (grouped-query heads: one list per query head).
  *   page_idx [batch][n_q_heads][top_k] int32, device
- *   q, k, v, o as for da_decode_attention (n_q_heads == n_kv_heads)
+ *   q, k, v, o as for da_decode_attention
  *   ws >= da_decode_attention_paged_workspace(s, page_size, top_k) bytes
  * ------------------------------------------------------------------------ */
 size_t da_decode_attention_paged_workspace(const da_attn_shape *s,
@@ -248,13 +252,14 @@ da_status da_decode_attention_paged(const da_attn_shape *s, int32_t page_size,
 /* ------------------------------------------------------------------------
  * TinyServe's whole decode step for one query (its Algorithm 1: given q, the
  * page metadata and the KV cache, return o) in one kernel: per (batch row,
- * head) the bound scores of all pages (as da_select_pages), the top_k of
- * them, the exact scores q . k of the tokens of the kept pages, and
+ * query head) the bound scores of all pages of its KV head (as
+ * da_select_pages), the top_k of them, the exact scores q . k of the tokens
+ * of the kept pages, and
  *   o = sum_t softmax(scale * q . k_t) v_t over those tokens only
  * (as da_decode_attention_paged on the same page list; positions at or beyond
  * n_ctx in a partial last page are skipped).  Reads the metadata once and
  * only the kept pages' K and V rows.  No workspace.
- *   q, k, v, o   as for da_decode_attention (n_q_heads == n_kv_heads)
+ *   q, k, v, o   as for da_decode_attention
  *   kmin, kmax   as written by da_build_page_meta with this page_size
  *   page_idx     [batch][n_q_heads][top_k] int32, device, or NULL (written
  *                if given: the kept pages, ascending, as da_select_pages)

@@ -179,16 +179,19 @@ def da_build_page_meta(k, page_size, kmin=None, kmax=None, stream=None):
 
 def da_select_pages(q, kmin, kmax, page_size, top_k, n_ctx, page_idx=None, page_score=None,
                     want_scores=False, stream=None):
-    """Top-k pages by the bound score per (b, h), ascending int32 [B][H][top_k]."""
+    """Top-k pages by the bound score per (b, query head), ascending int32
+    [B][Hq][top_k]; kmin/kmax [B][Hkv][P][D] (query head j reads KV head
+    j / (Hq / Hkv))."""
     lib = load()
     _dev(q, kmin, kmax, page_idx, page_score)
     B, H, D = q.shape
+    Hkv = kmin.shape[1]
     P = -(-n_ctx // page_size)
-    _expect(kmin, (B, H, P, D), kmin.dtype, "kmin")
-    _expect(kmax, (B, H, P, D), kmin.dtype, "kmax")
+    _expect(kmin, (B, Hkv, P, D), kmin.dtype, "kmin")
+    _expect(kmax, (B, Hkv, P, D), kmin.dtype, "kmax")
     _expect(page_idx, (B, H, top_k), torch.int32, "page_idx")
     _expect(page_score, (B, H, P), torch.float32, "page_score")
-    s = attn_shape(B, H, H, D, n_ctx, None, _DT[q.dtype], _DT[kmin.dtype])
+    s = attn_shape(B, H, Hkv, D, n_ctx, None, _DT[q.dtype], _DT[kmin.dtype])
     if page_idx is None:
         page_idx = torch.empty((B, H, top_k), dtype=torch.int32, device=q.device)
     if want_scores and page_score is None:
@@ -199,15 +202,16 @@ def da_select_pages(q, kmin, kmax, page_size, top_k, n_ctx, page_idx=None, page_
 
 
 def da_select_tokens(q, k, top_k, token_idx=None, token_score=None, want_scores=False, stream=None):
-    """Top-k tokens by exact score q . k per (b, h), ascending int32 [B][H][top_k]."""
+    """Top-k tokens by exact score q . k per (b, query head), ascending int32
+    [B][Hq][top_k]; k [B][Hkv][N][D] (query head j reads KV head j / (Hq / Hkv))."""
     lib = load()
     _dev(q, k, token_idx, token_score)
     B, H, D = q.shape
-    N = k.shape[2]
-    _expect(k, (B, H, N, D), k.dtype, "k")
+    Hkv, N = k.shape[1], k.shape[2]
+    _expect(k, (B, Hkv, N, D), k.dtype, "k")
     _expect(token_idx, (B, H, top_k), torch.int32, "token_idx")
     _expect(token_score, (B, H, N), torch.float32, "token_score")
-    s = attn_shape(B, H, H, D, N, None, _DT[q.dtype], _DT[k.dtype])
+    s = attn_shape(B, H, Hkv, D, N, None, _DT[q.dtype], _DT[k.dtype])
     if token_idx is None:
         token_idx = torch.empty((B, H, top_k), dtype=torch.int32, device=q.device)
     if want_scores and token_score is None:

@@ -243,8 +243,6 @@ da_status da_select_pages(const da_attn_shape *s, int32_t page_size, int32_t top
                           hipStream_t stream) {
     DA_TRY(check_shape(s, false));
     DA_TRY(check_page(page_size));
-    if (s->n_q_heads != s->n_kv_heads)
-        return fail(DA_E_UNSUPPORTED, "page selection needs n_q_heads == n_kv_heads");
     const int64_t P = n_pages(s, page_size);
     if (top_k < 1 || top_k > P) return fail(DA_E_INVALID, "top_k %d not in [1, %lld]", top_k, (long long)P);
     if (P > 8192) return fail(DA_E_UNSUPPORTED, "%lld pages > 8192 per head", (long long)P);
@@ -256,7 +254,8 @@ da_status da_select_pages(const da_attn_shape *s, int32_t page_size, int32_t top
     if (page_score && !aligned16(page_score)) return fail(DA_E_INVALID, "page_score is not 16-byte aligned");
     if (!select_supported(s->kv_dtype, s->q_dtype, s->head_dim))
         return fail(DA_E_UNSUPPORTED, "no selection kernel for this dtype / head_dim");
-    hipError_t e = launch_select(s->kv_dtype, s->q_dtype, (int64_t)s->batch * s->n_q_heads, P, s->head_dim, top_k,
+    hipError_t e = launch_select(s->kv_dtype, s->q_dtype, (int64_t)s->batch * s->n_q_heads, s->n_q_heads,
+                                 s->n_q_heads / s->n_kv_heads, P, s->head_dim, top_k,
                                  q, kmin, kmax, page_idx, page_score, stream);
     if (e != hipSuccess) return hip_fail(e, "page selection launch");
     return ok();
@@ -265,8 +264,6 @@ da_status da_select_pages(const da_attn_shape *s, int32_t page_size, int32_t top
 da_status da_select_tokens(const da_attn_shape *s, int32_t top_k, const void *q, const void *k, int32_t *token_idx,
                            float *token_score, hipStream_t stream) {
     DA_TRY(check_shape(s, false));
-    if (s->n_q_heads != s->n_kv_heads)
-        return fail(DA_E_UNSUPPORTED, "token selection needs n_q_heads == n_kv_heads");
     if (top_k < 1 || top_k > s->n_ctx)
         return fail(DA_E_INVALID, "top_k %d not in [1, %lld]", top_k, (long long)s->n_ctx);
     if (s->n_ctx > 8192) return fail(DA_E_UNSUPPORTED, "%lld tokens > 8192 per head", (long long)s->n_ctx);
@@ -277,7 +274,8 @@ da_status da_select_tokens(const da_attn_shape *s, int32_t top_k, const void *q,
     if (token_score && !aligned16(token_score)) return fail(DA_E_INVALID, "token_score is not 16-byte aligned");
     if (!select_supported(s->kv_dtype, s->q_dtype, s->head_dim))
         return fail(DA_E_UNSUPPORTED, "no selection kernel for this dtype / head_dim");
-    hipError_t e = launch_select(s->kv_dtype, s->q_dtype, (int64_t)s->batch * s->n_q_heads, s->n_ctx, s->head_dim,
+    hipError_t e = launch_select(s->kv_dtype, s->q_dtype, (int64_t)s->batch * s->n_q_heads, s->n_q_heads,
+                                 s->n_q_heads / s->n_kv_heads, s->n_ctx, s->head_dim,
                                  top_k, q, k, k, token_idx, token_score, stream, true);
     if (e != hipSuccess) return hip_fail(e, "token selection launch");
     return ok();
@@ -286,8 +284,6 @@ da_status da_select_tokens(const da_attn_shape *s, int32_t top_k, const void *q,
 da_status da_decode_attention_topk(const da_attn_shape *s, int32_t top_k, const void *q, const void *k, const void *v,
                                    float *o, int32_t *token_idx, hipStream_t stream) {
     DA_TRY(check_shape(s, false));
-    if (s->n_q_heads != s->n_kv_heads)
-        return fail(DA_E_UNSUPPORTED, "top-k attention needs n_q_heads == n_kv_heads");
     if (top_k < 1 || top_k > s->n_ctx)
         return fail(DA_E_INVALID, "top_k %d not in [1, %lld]", top_k, (long long)s->n_ctx);
     if (s->n_ctx + 2 * (int64_t)top_k + 8 * (int64_t)s->head_dim > 16384)
@@ -301,7 +297,8 @@ da_status da_decode_attention_topk(const da_attn_shape *s, int32_t top_k, const 
     if (token_idx && !aligned16(token_idx)) return fail(DA_E_INVALID, "token_idx is not 16-byte aligned");
     if (!select_supported(s->kv_dtype, s->q_dtype, s->head_dim))
         return fail(DA_E_UNSUPPORTED, "no selection kernel for this dtype / head_dim");
-    hipError_t e = launch_topk_attention(s->kv_dtype, s->q_dtype, (int64_t)s->batch * s->n_q_heads, s->n_ctx,
+    hipError_t e = launch_topk_attention(s->kv_dtype, s->q_dtype, (int64_t)s->batch * s->n_q_heads, s->n_q_heads,
+                                         s->n_q_heads / s->n_kv_heads, s->n_ctx,
                                          s->head_dim, top_k, s->scale * 1.4426950408889634f, q, k, v, o,
                                          token_idx, stream);
     if (e != hipSuccess) return hip_fail(e, "top-k attention launch");
@@ -313,8 +310,6 @@ da_status da_decode_attention_sparse(const da_attn_shape *s, int32_t page_size, 
                                      int32_t *page_idx, hipStream_t stream) {
     DA_TRY(check_shape(s, false));
     DA_TRY(check_page(page_size));
-    if (s->n_q_heads != s->n_kv_heads)
-        return fail(DA_E_UNSUPPORTED, "page-sparse attention needs n_q_heads == n_kv_heads");
     const int64_t P = n_pages(s, page_size);
     if (top_k < 1 || top_k > P) return fail(DA_E_INVALID, "top_k %d not in [1, %lld]", top_k, (long long)P);
     if (P > 8192) return fail(DA_E_UNSUPPORTED, "%lld pages > 8192 per head", (long long)P);
@@ -332,7 +327,8 @@ da_status da_decode_attention_sparse(const da_attn_shape *s, int32_t page_size, 
     if (page_idx && !aligned16(page_idx)) return fail(DA_E_INVALID, "page_idx is not 16-byte aligned");
     if (!select_supported(s->kv_dtype, s->q_dtype, s->head_dim))
         return fail(DA_E_UNSUPPORTED, "no selection kernel for this dtype / head_dim");
-    hipError_t e = launch_page_attention(s->kv_dtype, s->q_dtype, (int64_t)s->batch * s->n_q_heads, s->n_ctx, P,
+    hipError_t e = launch_page_attention(s->kv_dtype, s->q_dtype, (int64_t)s->batch * s->n_q_heads, s->n_q_heads,
+                                         s->n_q_heads / s->n_kv_heads, s->n_ctx, P,
                                          s->head_dim, ilog2(page_size), top_k, s->scale * 1.4426950408889634f, q,
                                          kmin, kmax, k, v, o, page_idx, stream);
     if (e != hipSuccess) return hip_fail(e, "page-sparse attention launch");
@@ -374,8 +370,6 @@ da_status da_decode_attention_paged(const da_attn_shape *s, int32_t page_size, i
                                     void *ws, size_t ws_bytes, hipStream_t stream) {
     DA_TRY(check_shape(s, false));
     DA_TRY(check_page(page_size));
-    if (s->n_q_heads != s->n_kv_heads)
-        return fail(DA_E_UNSUPPORTED, "paged attention needs n_q_heads == n_kv_heads");
     const int64_t P = n_pages(s, page_size);
     if (top_k < 1 || top_k > P) return fail(DA_E_INVALID, "top_k %d not in [1, %lld]", top_k, (long long)P);
     if (s->batch == 0) return ok();
@@ -388,6 +382,10 @@ da_status da_decode_attention_paged(const da_attn_shape *s, int32_t page_size, i
     const size_t need = da_decode_attention_paged_workspace(s, page_size, top_k);
     if (ws_bytes < need) return fail(DA_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
     AttnLaunch a = dense_launch(s, s->kv_dtype, SPLIT_PAGED);
+    // each query head attends its own pages: one unit per query head
+    a.kv_group = a.G;
+    a.Hkv = s->n_q_heads;
+    a.G = 1;
     if (!attn_supported(a.kv_fmt, a.q_fmt, a.D, a.G, true))
         return fail(DA_E_UNSUPPORTED, "no paged kernel for this dtype / head_dim");
     a.page_idx = page_idx;

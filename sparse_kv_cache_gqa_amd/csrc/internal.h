@@ -40,9 +40,13 @@ struct AttnLaunch {
     // uint4 cache: per-row fp16 min and scale arrays, D/64 per row
     const void *kmin = nullptr, *kscale = nullptr, *vmin = nullptr, *vscale = nullptr;
 
-    // page-sparse: page list [B][Hkv][top_k] (Hq == Hkv), page = 2^log2_page tokens
+    // page-sparse: page list [B][Hkv][top_k], page = 2^log2_page tokens.
+    // Grouped-query heads run one unit per query head (Hkv = query heads,
+    // G = 1) with kv_group = query heads per KV head: unit h reads the rows of
+    // KV head h / kv_group.
     const int32_t *page_idx = nullptr;
     int32_t top_k = 0, log2_page = 0;
+    int32_t kv_group = 1;
 
     int32_t split_tokens = kDefaultSplitDense;
     int32_t n_split = 0;
@@ -89,7 +93,7 @@ hipError_t launch_page_meta(int kv_fmt, int64_t BH, int64_t N, int D,
 // Bound score + top-K per (b, h).  With `exact`, kmax holds the key rows
 // themselves (P = N tokens, kmin unused) and the score is q . k.
 bool select_supported(int kv_fmt, int q_fmt, int D);
-hipError_t launch_select(int kv_fmt, int q_fmt, int64_t BH, int64_t P, int D,
+hipError_t launch_select(int kv_fmt, int q_fmt, int64_t BH, int32_t Hq, int32_t G, int64_t P, int D,
                          int top_k, const void *q, const void *kmin,
                          const void *kmax, int32_t *page_idx, float *page_score,
                          hipStream_t stream, bool exact = false);
@@ -97,8 +101,8 @@ hipError_t launch_select(int kv_fmt, int q_fmt, int64_t BH, int64_t P, int D,
 // Exact-score token selection fused with attention over the kept tokens:
 // one workgroup per (b, h); o [BH][D] fp32; token_idx optional.  Dynamic
 // LDS holds N + 2 * top_k + 8 * D floats.
-hipError_t launch_topk_attention(int kv_fmt, int q_fmt, int64_t BH, int64_t N, int D, int top_k,
-                                 float scale_log2, const void *q, const void *k, const void *v, float *o,
+hipError_t launch_topk_attention(int kv_fmt, int q_fmt, int64_t BH, int32_t Hq, int32_t G, int64_t N, int D,
+                                 int top_k, float scale_log2, const void *q, const void *k, const void *v, float *o,
                                  int32_t *token_idx, hipStream_t stream);
 
 // Page selection fused with attention over the kept pages' tokens (one
@@ -110,9 +114,10 @@ inline int64_t page_attention_lds_floats(int64_t P, int64_t top_k, int log2_page
     return P + top_k + 2 * (top_k << log2_page) + (int64_t)n_waves * D;
 }
 constexpr int64_t kPageAttnLdsFloats = 16384;   // 64 KiB of dynamic LDS
-hipError_t launch_page_attention(int kv_fmt, int q_fmt, int64_t BH, int64_t N, int64_t P, int D, int log2_page,
-                                 int top_k, float scale_log2, const void *q, const void *kmin, const void *kmax,
-                                 const void *k, const void *v, float *o, int32_t *page_idx, hipStream_t stream);
+hipError_t launch_page_attention(int kv_fmt, int q_fmt, int64_t BH, int32_t Hq, int32_t G, int64_t N, int64_t P,
+                                 int D, int log2_page, int top_k, float scale_log2, const void *q, const void *kmin,
+                                 const void *kmax, const void *k, const void *v, float *o, int32_t *page_idx,
+                                 hipStream_t stream);
 
 // Chunked prefill attention: q [B][Hq][C][D], k/v [B][Hkv][T][D] (T = prefix
 // + C), o [B][Hq][C][D] fp32; q, k and v in `fmt` (bf16 or fp16).

@@ -216,7 +216,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         ntok = (int)max((int64_t)0, min((int64_t)a.split_tokens, a.N - s0));
     }
 
-    const int64_t kvoff = (int64_t)b * a.kv_bstride + (int64_t)hkv * a.kv_hstride;
+    const int64_t kvoff = (int64_t)b * a.kv_bstride + (int64_t)(hkv / a.kv_group) * a.kv_hstride;
     const char *kbase = (const char *)a.k + kvoff * R;
     const char *vbase = (const char *)a.v + kvoff * R;
     const uint16_t *kmn = nullptr, *ksc = nullptr, *vmn = nullptr, *vsc = nullptr;

@@ -151,6 +151,9 @@ struct SelArgs {
     const uint8_t *k = nullptr;    // SEL_PAGE_ATTEND: key rows [BH][N][D] (v likewise)
     int64_t N = 0;                 // SEL_PAGE_ATTEND: tokens per head
     int32_t log2_page = 0;         // SEL_PAGE_ATTEND: page = 2^log2_page tokens
+    // grouped-query heads: workgroup bh = b * Hq + j serves query head j; its
+    // metadata, key and value rows are those of KV head b * (Hq / G) + j / G
+    int32_t Hq = 1, G = 1;
 };
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -217,7 +220,8 @@ __device__ __forceinline__ float block_reduce(float x, float *buf) {
 // ascending order, one fma chain per channel); the slots are summed by lane
 // shuffles within a wave and through LDS across waves.
 template <int KF, int D, int NW, typename ScoreF, typename RowF>
-__device__ __forceinline__ void attend_items(const SelArgs &args, int64_t bh, int n, int64_t rows_per_head,
+__device__ __forceinline__ void attend_items(const SelArgs &args, int64_t bh, int64_t kvh, int n,
+                                             int64_t rows_per_head,
                                              ScoreF score, RowF row_of, float *wl, float *red,
                                              uint32_t *scan_buf) {
     constexpr int R = D * Elem<KF>::size;
@@ -242,7 +246,7 @@ __device__ __forceinline__ void attend_items(const SelArgs &args, int64_t bh, in
     const float L = block_reduce<NW, false>(lsum, fbuf);   // also orders wl[] before use
 
     const int ch = tid % CH, slot = tid / CH;
-    const uint8_t *vb = args.v + bh * rows_per_head * R + 16 * ch;
+    const uint8_t *vb = args.v + kvh * rows_per_head * R + 16 * ch;
     float acc[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
@@ -308,7 +312,8 @@ __global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args)
     __shared__ uint32_t pick_digit, pick_need, pick_count;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int64_t bh = blockIdx.x;
+    const int64_t bh = blockIdx.x;                 // (batch row, query head)
+    const int64_t kvh = (bh / args.Hq) * (args.Hq / args.G) + (bh % args.Hq) / args.G;   // its KV head
 
     // ---- 1. scores ----------------------------------------------------------
     // Lanes own 16-byte pieces of a row: piece = lane mod PCS of row lane / PCS,
@@ -333,8 +338,8 @@ __global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args)
     }
     // buffer resources over this head's rows: rows at or past P read as zeros
     const uint32_t head_bytes = (uint32_t)(P * R);
-    const __amdgpu_buffer_rsrc_t mxr = make_rsrc(kmax + bh * P * R, head_bytes);
-    const __amdgpu_buffer_rsrc_t mnr = make_rsrc((EXACT ? kmax : kmin) + bh * P * R, head_bytes);
+    const __amdgpu_buffer_rsrc_t mxr = make_rsrc(kmax + kvh * P * R, head_bytes);
+    const __amdgpu_buffer_rsrc_t mnr = make_rsrc((EXACT ? kmax : kmin) + kvh * P * R, head_bytes);
     {
         const int64_t step = (int64_t)TPT * kSelWaves;
         u32x4 X[NI], Nn[NI];
@@ -481,7 +486,7 @@ __global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args)
             return (t >= 0 && t < P) ? t : 0;
         };
         float *wl = (float *)(kept + top_k);
-        attend_items<KF, D, kSelWaves>(args, bh, top_k, P, [&](int i) { return sc_lds[row(i)]; }, row, wl,
+        attend_items<KF, D, kSelWaves>(args, bh, kvh, top_k, P, [&](int i) { return sc_lds[row(i)]; }, row, wl,
                                        wl + top_k, scan_buf);
     }
     if constexpr (MODE == SEL_PAGE_ATTEND) {
@@ -504,7 +509,7 @@ __global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args)
         };
         // one array here (the bound scan reads two): twice the loads per trip
         constexpr int NI4 = 2 * NI, TPT4 = NI4 * TPI;
-        const uint8_t *kb = args.k + bh * N * R + 16 * piece;
+        const uint8_t *kb = args.k + kvh * N * R + 16 * piece;
         for (int base = w * TPT4; base < T; base += TPT4 * kSelWaves) {
             u32x4 X[NI4];
             int64_t rr[NI4];
@@ -529,7 +534,7 @@ __global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args)
         }
         // ---- 5. attention over them ----------------------------------------
         float *wl = tsc + T;
-        attend_items<KF, D, kSelWaves>(args, bh, T, N, [&](int i) { return tsc[i]; },
+        attend_items<KF, D, kSelWaves>(args, bh, kvh, T, N, [&](int i) { return tsc[i]; },
                                        [&](int i) -> int64_t { const int64_t r = tok(i); return r >= 0 ? r : 0; },
                                        wl, wl + T, scan_buf);
     }
@@ -593,8 +598,8 @@ hipError_t launch_page_meta(int kv_fmt, int64_t BH, int64_t N, int D, int log2_p
 
 bool select_supported(int kv_fmt, int q_fmt, int D) { return sel_for(SEL_PAGES, kv_fmt, q_fmt, D) != nullptr; }
 
-hipError_t launch_select(int kv_fmt, int q_fmt, int64_t BH, int64_t P, int D, int top_k, const void *q,
-                         const void *kmin, const void *kmax, int32_t *page_idx, float *page_score,
+hipError_t launch_select(int kv_fmt, int q_fmt, int64_t BH, int32_t Hq, int32_t G, int64_t P, int D, int top_k,
+                         const void *q, const void *kmin, const void *kmax, int32_t *page_idx, float *page_score,
                          hipStream_t stream, bool exact) {
     const int mode = exact ? SEL_TOKENS : SEL_PAGES;
     SelFn fn = sel_for(mode, kv_fmt, q_fmt, D);
@@ -607,14 +612,16 @@ hipError_t launch_select(int kv_fmt, int q_fmt, int64_t BH, int64_t P, int D, in
     a.kmax = (const uint8_t *)kmax;
     a.page_idx = page_idx;
     a.page_score = page_score;
+    a.Hq = Hq;
+    a.G = G;
     const size_t lds = (size_t)P * sizeof(float);
     hipLaunchKernelGGL(fn, dim3((unsigned)BH), dim3(sel_threads(mode)), lds, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_topk_attention(int kv_fmt, int q_fmt, int64_t BH, int64_t N, int D, int top_k, float scale_log2,
-                                 const void *q, const void *k, const void *v, float *o, int32_t *token_idx,
-                                 hipStream_t stream) {
+hipError_t launch_topk_attention(int kv_fmt, int q_fmt, int64_t BH, int32_t Hq, int32_t G, int64_t N, int D,
+                                 int top_k, float scale_log2, const void *q, const void *k, const void *v, float *o,
+                                 int32_t *token_idx, hipStream_t stream) {
     SelFn fn = sel_for(SEL_ATTEND, kv_fmt, q_fmt, D);
     if (!fn) return hipErrorInvalidValue;
     SelArgs a;
@@ -627,15 +634,18 @@ hipError_t launch_topk_attention(int kv_fmt, int q_fmt, int64_t BH, int64_t N, i
     a.v = (const uint8_t *)v;
     a.o = o;
     a.scale_log2 = scale_log2;
+    a.Hq = Hq;
+    a.G = G;
     const int nw = sel_threads(SEL_ATTEND) / 64;
     const size_t lds = ((size_t)N + 2 * (size_t)top_k + (size_t)nw * D) * sizeof(float);
     hipLaunchKernelGGL(fn, dim3((unsigned)BH), dim3(sel_threads(SEL_ATTEND)), lds, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_page_attention(int kv_fmt, int q_fmt, int64_t BH, int64_t N, int64_t P, int D, int log2_page,
-                                 int top_k, float scale_log2, const void *q, const void *kmin, const void *kmax,
-                                 const void *k, const void *v, float *o, int32_t *page_idx, hipStream_t stream) {
+hipError_t launch_page_attention(int kv_fmt, int q_fmt, int64_t BH, int32_t Hq, int32_t G, int64_t N, int64_t P,
+                                 int D, int log2_page, int top_k, float scale_log2, const void *q, const void *kmin,
+                                 const void *kmax, const void *k, const void *v, float *o, int32_t *page_idx,
+                                 hipStream_t stream) {
     SelFn fn = sel_for(SEL_PAGE_ATTEND, kv_fmt, q_fmt, D);
     if (!fn) return hipErrorInvalidValue;
     SelArgs a;
@@ -651,6 +661,8 @@ hipError_t launch_page_attention(int kv_fmt, int q_fmt, int64_t BH, int64_t N, i
     a.N = N;
     a.log2_page = log2_page;
     a.scale_log2 = scale_log2;
+    a.Hq = Hq;
+    a.G = G;
     const int nw = sel_threads(SEL_PAGE_ATTEND) / 64;
     const size_t lds = page_attention_lds_floats(P, top_k, log2_page, D, nw) * sizeof(float);
     hipLaunchKernelGGL(fn, dim3((unsigned)BH), dim3(sel_threads(SEL_PAGE_ATTEND)), lds, stream, a);

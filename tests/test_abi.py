@@ -133,14 +133,14 @@ def test_page_checks(lib):
                                                 NULL, NULL)
     assert sel(s, 16, 0) == L.DA_E_INVALID
     assert sel(s, 16, 2049) == L.DA_E_INVALID
-    assert sel(mha(n_q_heads=32), 16, 128) == L.DA_E_UNSUPPORTED     # GQA
+    assert sel(mha(n_q_heads=24), 16, 128) == L.DA_E_INVALID         # 24 query heads over 16 KV heads
     assert sel(mha(n_ctx=16 * 8193), 16, 128) == L.DA_E_UNSUPPORTED   # > 8192 pages
     assert lib.da_select_pages(ctypes.byref(s), 16, 128, FAKE, FAKE, FAKE, MISALIGNED, NULL,
                                NULL) == L.DA_E_INVALID
     paged = lambda sh, k, ws_bytes=1 << 40: lib.da_decode_attention_paged(
         ctypes.byref(sh), 16, k, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, NULL)
     assert paged(s, 0) == L.DA_E_INVALID
-    assert paged(mha(n_q_heads=32), 128) == L.DA_E_UNSUPPORTED
+    assert paged(mha(n_q_heads=24), 128) == L.DA_E_INVALID
     need = lib.da_decode_attention_paged_workspace(ctypes.byref(s), 16, 128)
     assert need == 32 * 16 * 4 * 68 * 4           # 128 pages of 16 = 2048 positions / 512
     assert paged(s, 128, need - 4) == L.DA_E_WORKSPACE
@@ -149,7 +149,7 @@ def test_page_checks(lib):
     assert sp(s, 3, 128) == L.DA_E_INVALID                              # page size
     assert sp(s, 16, 0) == L.DA_E_INVALID
     assert sp(s, 16, 2049) == L.DA_E_INVALID                            # top_k > P
-    assert sp(mha(n_q_heads=32), 16, 128) == L.DA_E_UNSUPPORTED         # GQA
+    assert sp(mha(n_q_heads=24), 16, 128) == L.DA_E_INVALID            # not a multiple of n_kv_heads
     assert sp(mha(n_ctx=16 * 8193), 16, 128) == L.DA_E_UNSUPPORTED      # > 8192 pages
     assert sp(s, 16, 500) == L.DA_E_UNSUPPORTED      # 2048 + 500 + 2 * 8000 + 16 * 64 > 16384
     assert sp(s, 16, 128, q=MISALIGNED) == L.DA_E_INVALID
@@ -162,7 +162,7 @@ def test_token_selection_checks(lib):
     sel = lambda sh, k, score=NULL: lib.da_select_tokens(ctypes.byref(sh), k, FAKE, FAKE, FAKE, score, NULL)
     assert sel(s, 0) == L.DA_E_INVALID
     assert sel(s, 1025) == L.DA_E_INVALID
-    assert sel(mha(n_q_heads=32, n_ctx=1024), 100) == L.DA_E_UNSUPPORTED    # GQA
+    assert sel(mha(n_q_heads=24, n_ctx=1024), 100) == L.DA_E_INVALID       # not a multiple of n_kv_heads
     assert sel(mha(n_ctx=8193), 100) == L.DA_E_UNSUPPORTED                  # > 8192 tokens
     assert sel(s, 100, MISALIGNED) == L.DA_E_INVALID
     assert lib.da_select_tokens(ctypes.byref(s), 100, FAKE, NULL, FAKE, NULL, NULL) == L.DA_E_INVALID
@@ -176,7 +176,7 @@ def test_topk_attention_checks(lib):
                                                                idx, NULL)
     assert att(s, 0) == L.DA_E_INVALID
     assert att(s, 1025) == L.DA_E_INVALID
-    assert att(mha(n_q_heads=32, n_ctx=1024), 100) == L.DA_E_UNSUPPORTED     # GQA
+    assert att(mha(n_q_heads=24, n_ctx=1024), 100) == L.DA_E_INVALID        # not a multiple of n_kv_heads
     assert att(mha(n_ctx=8192, head_dim=128), 3585) == L.DA_E_UNSUPPORTED    # LDS budget
     assert att(s, 100, MISALIGNED) == L.DA_E_INVALID
     assert lib.da_decode_attention_topk(ctypes.byref(s), 100, FAKE, FAKE, NULL, FAKE, NULL,

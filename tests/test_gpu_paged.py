@@ -225,3 +225,32 @@ def test_selection_with_exact_ties(da, P, K):
     order = sorted(range(P), key=lambda j: (-float(s[0, 0, j]), j))
     assert idx.cpu().numpy()[0, 0].tolist() == sorted(order[:K])
     check_selection(idx.cpu().numpy(), r, K)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,N,S,K", [(2, 8, 2, 64, 1000, 16, 10), (1, 16, 2, 128, 4096, 16, 100),
+                                              (2, 4, 1, 64, 777, 4, 37)])
+def test_grouped_query_heads(da, B, Hq, Hkv, D, N, S, K):
+    """Grouped-query heads: page metadata per KV head; each query head selects
+    its own pages over its KV head's metadata (query head j -> KV head j / G)
+    and attends over them.  The oracle is the one-KV-head-per-query-head
+    definition on K/V repeated G times.  The two-call and one-kernel routes
+    keep the same pages."""
+    import torch
+    G = Hq // Hkv
+    c = synth.dense_case([206, B, Hq, Hkv, D, N], B, Hq, Hkv, D, N, "f16", "f16")
+    q, k, v = to_dev(c.q, "f16"), to_dev(c.k, "f16"), to_dev(c.v, "f16")
+    kmin, kmax = da.da_build_page_meta(k, S)
+    idx = da.da_select_pages(q, kmin, kmax, S, K, N)
+    o2 = da.da_decode_attention_paged(q, k, v, idx, S, scale=c.scale)
+    o1, idx1 = da.da_decode_attention_sparse(q, kmin, kmax, k, v, S, K, scale=c.scale, want_idx=True)
+    torch.cuda.synchronize()
+    idx, idx1 = idx.cpu().numpy(), idx1.cpu().numpy()
+    assert np.array_equal(idx, idx1)
+    q64 = as_f64(c.q, "f16")
+    k64 = np.repeat(as_f64(c.k, "f16"), G, axis=1)
+    v64 = np.repeat(as_f64(c.v, "f16"), G, axis=1)
+    rmin, rmax = page_meta(k64, S)
+    check_selection(idx, bound_scores(q64, rmin, rmax), K)
+    ref = sparse_attention(q64, k64, v64, idx, S, c.scale)
+    assert_close(o2.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what=f"GQA pages two calls G{G}")
+    assert_close(o1.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what=f"GQA pages one kernel G{G}")

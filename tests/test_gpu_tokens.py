@@ -130,3 +130,29 @@ def test_fused_topk_flexgen_shape_sampled(da):
         check_selection(idx[b:b + 1, h:h + 1], token_scores(q64, k64), K)
         ref = sparse_attention(q64, k64, v64, idx[b:b + 1, h:h + 1], 1, c.scale)
         assert_close(o[b, h], ref[0, 0], atol=1e-3, rel_rms=1e-4, what=f"w4 fused topk b{b} h{h}")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,K", [(2, 8, 2, 500, 50), (1, 8, 1, 1024, 0), (2, 4, 2, 300, 7)])
+def test_grouped_query_heads(da, B, Hq, Hkv, N, K):
+    """Grouped-query heads: each query head selects its own tokens among its
+    KV head's keys (query head j -> KV head j / G) and attends over them; the
+    oracle is the one-KV-head-per-query-head definition on K/V repeated G
+    times.  Selection, the two-call route and the one-kernel route."""
+    import torch
+    K = K or keep_count(N)
+    G = Hq // Hkv
+    c = synth.dense_case([402, B, Hq, Hkv, N, K], B, Hq, Hkv, 64, N, "f16", "f16")
+    q, k, v = to_dev(c.q, "f16"), to_dev(c.k, "f16"), to_dev(c.v, "f16")
+    idx = da.da_select_tokens(q, k, K)
+    o2 = da.da_decode_attention_paged(q, k, v, idx, 1, scale=c.scale)
+    o1, idx1 = da.da_decode_attention_topk(q, k, v, K, scale=c.scale, want_idx=True)
+    torch.cuda.synchronize()
+    idx, idx1 = idx.cpu().numpy(), idx1.cpu().numpy()
+    assert np.array_equal(idx, idx1)
+    q64 = as_f64(c.q, "f16")
+    k64 = np.repeat(as_f64(c.k, "f16"), G, axis=1)
+    v64 = np.repeat(as_f64(c.v, "f16"), G, axis=1)
+    check_selection(idx, token_scores(q64, k64), K)
+    ref = sparse_attention(q64, k64, v64, idx, 1, c.scale)
+    assert_close(o2.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what=f"GQA tokens two calls G{G}")
+    assert_close(o1.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what=f"GQA tokens one kernel G{G}")
