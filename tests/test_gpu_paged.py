@@ -254,3 +254,26 @@ def test_grouped_query_heads(da, B, Hq, Hkv, D, N, S, K):
     ref = sparse_attention(q64, k64, v64, idx, S, c.scale)
     assert_close(o2.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what=f"GQA pages two calls G{G}")
     assert_close(o1.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what=f"GQA pages one kernel G{G}")
+
+
+@pytest.mark.parametrize("S,N,K", [(2, 999, 120), (8, 3001, 90), (32, 5000, 40), (128, 20000, 25),
+                                   (512, 70000, 7)])
+def test_one_kernel_page_sizes(da, S, N, K):
+    """The one-kernel page step over page sizes 2..512 with a partial last
+    page: the kept pages equal da_select_pages', attention matches the
+    oracle on them."""
+    import torch
+    B, H, D = 1, 3, 64
+    c = synth.paged_case([207, S, N, K], B, H, D, N, S, K, dtype="f16")
+    q, k, v = to_dev(c.q, "f16"), to_dev(c.k, "f16"), to_dev(c.v, "f16")
+    kmin, kmax = da.da_build_page_meta(k, S)
+    two = da.da_select_pages(q, kmin, kmax, S, K, N)
+    o, idx = da.da_decode_attention_sparse(q, kmin, kmax, k, v, S, K, scale=c.scale, want_idx=True)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    assert np.array_equal(idx, two.cpu().numpy())
+    q64, k64, v64 = as_f64(c.q, "f16"), as_f64(c.k, "f16"), as_f64(c.v, "f16")
+    rmin, rmax = page_meta(k64, S)
+    check_selection(idx, bound_scores(q64, rmin, rmax), K)
+    ref = sparse_attention(q64, k64, v64, idx, S, c.scale)
+    assert_close(o.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what=f"one kernel S{S} N{N} K{K}")
