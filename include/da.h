@@ -153,7 +153,8 @@ da_status da_decode_attention(const da_attn_shape *s, const void *q,
  * da_merge_partials: o[r] = sum_i 2^(m_i - M) u_i / sum_i 2^(m_i - M) l_i,
  *   M = max_i m_i, for rows r < rows, partials [rows][n_split][head_dim+4]
  *   fp32 (device), o [rows][head_dim] fp32 (device).  A split with
- *   m = -inf contributes nothing.  head_dim in {64, 128}.
+ *   m = -inf contributes nothing; a row whose splits all have m = -inf
+ *   (no token) gets o = 0.  head_dim in {64, 128}.
  * ------------------------------------------------------------------------ */
 int32_t da_decode_attention_n_split(const da_attn_shape *s);
 da_status da_decode_attention_partials(const da_attn_shape *s, const void *q,
@@ -214,6 +215,16 @@ da_status da_select_tokens(const da_attn_shape *s, int32_t top_k,
                            float *token_score, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Number of tokens FlexGen's sparse attention keeps per query (FlexGen
+ * digest, section "方法细节": only the top 10% of the K cache by score are
+ * kept): ceil(n_ctx / 10), which is at least 1 and at most n_ctx for
+ * n_ctx >= 1.  Returns 0 when n_ctx < 1.  Pure host arithmetic (integer, no
+ * rounding); pass the result as top_k to da_select_tokens or
+ * da_decode_attention_topk.
+ * ------------------------------------------------------------------------ */
+int64_t da_token_keep_count(int64_t n_ctx);
+
+/* ------------------------------------------------------------------------
  * Token-level top-k sparse attention in one kernel (FlexGen's top-10% sparse
  * attention): per (batch row, query head) the exact scores s_i = q . k_i of
  * all n_ctx tokens of its KV head, the top_k of them (as da_select_tokens),
@@ -235,8 +246,10 @@ da_status da_decode_attention_topk(const da_attn_shape *s, int32_t top_k,
  * Sparse attention over the selected pages only (TinyServe SparseAttn):
  * softmax normalised over the tokens of the listed pages; positions at or
  * beyond n_ctx in a partial last page are skipped, and so is any listed page
- * index outside [0, P).  Each query head attends its own list over the
- * rows of its KV head (grouped-query heads: one list per query head).
+ * index outside [0, P).  A row whose list holds no page inside [0, P) has
+ * no token to attend, and its output is zero.  Each query head attends its
+ * own list over the rows of its KV head (grouped-query heads: one list per
+ * query head).  batch * n_q_heads <= 65535 (DA_E_UNSUPPORTED otherwise).
  *   page_idx [batch][n_q_heads][top_k] int32, device
  *   q, k, v, o as for da_decode_attention
  *   ws >= da_decode_attention_paged_workspace(s, page_size, top_k) bytes
@@ -294,7 +307,12 @@ da_status da_dequantize_kv4(int64_t n_rows, int32_t row_len,
                             const void *gscale, void *x, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * Decode attention over a uint4 cache, dequantizing while loading.
+ * Decode attention over a uint4 cache, dequantizing while loading (FlexGen
+ * digest, section "方法细节": the KV cache is stored as 4-bit integers with
+ * a min and a scale per group of 64 along the hidden dimension, and is
+ * dequantized back to FP16 before the attention arithmetic).  Per (batch
+ * row, query head) it computes the dense output above over the dequantized
+ * keys and values x_hat = min + code * scale of its KV head.
  * The dequantization is folded into the fp32 arithmetic
  * (q . (min + c*scale) = min * sum(q) + scale * sum(q*c) per group, and the
  * same for the value side), which differs from rounding each dequantized

@@ -73,16 +73,23 @@ def sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     """Attention of q[b,h] over the tokens of the listed pages only.
 
     q [B][H][D], k/v [B][H][N][D] float64 (one KV head per query head),
-    page_idx [B][H][K].  Tokens at or beyond N (partial last page) are skipped.
+    page_idx [B][H][K].  Tokens at or beyond N (partial last page) are skipped,
+    and so is a listed page index outside [0, ceil(N/S)): such a page holds no
+    token of the cache.  A list with no page inside the cache has nothing to
+    attend, and its output is zero.
     """
     B, H, D = q.shape
     N = k.shape[2]
     S = page_size
+    P = -(-N // S)
     o = np.empty((B, H, D), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            toks = [t for j in page_idx[b, h]
+            toks = [t for j in page_idx[b, h] if 0 <= int(j) < P
                     for t in range(int(j) * S, min((int(j) + 1) * S, N))]
+            if not toks:
+                o[b, h] = 0.0
+                continue
             kk = k[b, h, toks]
             vv = v[b, h, toks]
             s = scale * (kk @ q[b, h])

@@ -1,7 +1,7 @@
 """Turn two rocprofv3 PMC result databases (FETCH_SIZE pass, WRITE_SIZE pass)
 into calibrated HBM bytes per launch, keyed by kernel, for bench.py.
 
-    python -m sparse_kv_cache_gqa_amd.pmc_traffic FETCH_DB WRITE_DB OUT_JSON
+    python pmc_traffic.py FETCH_DB WRITE_DB OUT_JSON
 
 Both runs must include the 512 MiB device-to-device copies that
 `bench.py --copy-calibration` performs first (`__amd_rocclr_copyBuffer`):
@@ -18,7 +18,7 @@ import sqlite3
 import statistics
 import sys
 
-PKG = os.path.dirname(os.path.abspath(__file__))
+PKG = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_kv_cache_gqa_amd")
 COPY_KIB = 512 * 1024          # one calibration copy reads and writes 512 MiB
 KERNELS = {                    # short name -> substring of the mangled kernel name
     "attn_split_llama3_8b_32k": "attn_split_kernel<2, 0, 128, 4, false>",

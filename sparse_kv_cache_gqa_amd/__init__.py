@@ -25,5 +25,5 @@ from .api import (HeadwiseStream, attn_shape, da_build_page_meta,  # noqa: F401,
                   da_decode_attention_workspace, da_decode_attention_paged_workspace,
                   da_decode_attention_kv4_workspace,
                   da_dequantize_kv4, da_headwise_buffer_bytes, da_quantize_kv4,
-                  da_select_pages, da_select_tokens, da_decode_attention_topk, keep_count,
+                  da_select_pages, da_select_tokens, da_decode_attention_topk, da_token_keep_count,
                   da_prefill_attention, da_read_stream, da_decode_attention_sparse)

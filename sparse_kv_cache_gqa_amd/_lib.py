@@ -48,6 +48,7 @@ SIGNATURES = {
     "da_build_page_meta": (ctypes.c_int, [SHAPE, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "da_select_pages": (ctypes.c_int, [SHAPE, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "da_select_tokens": (ctypes.c_int, [SHAPE, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "da_token_keep_count": (c_i64, [c_i64]),
     "da_decode_attention_topk": (ctypes.c_int, [SHAPE, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "da_prefill_attention": (ctypes.c_int, [SHAPE, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "da_decode_attention_paged_workspace": (c_sz, [SHAPE, c_i32, c_i32]),

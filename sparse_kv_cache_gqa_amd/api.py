@@ -8,6 +8,7 @@ calls raise.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 
@@ -64,8 +65,25 @@ def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 
 
-def _ws(nbytes: int, device):
-    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+def _on(stream):
+    """Context for allocating the temporaries of a call that runs on `stream`:
+    the caching allocator then orders their reuse after the call's kernels
+    (a block freed on one stream is reused only by work on that stream)."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not hasattr(stream, "cuda_stream"):
+        stream = torch.cuda.ExternalStream(int(stream))
+    return torch.cuda.stream(stream)
+
+
+def _new(stream, shape, dtype, device):
+    """torch.empty allocated for use on `stream` (see _on)."""
+    with _on(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _ws(nbytes: int, device, stream):
+    return _new(stream, max(int(nbytes), 16), torch.uint8, device)
 
 
 # ---------------------------------------------------------------------------
@@ -79,9 +97,9 @@ def da_decode_attention(q, k, v, scale=None, split_tokens=0, out=None, ws=None, 
     need = lib.da_decode_attention_workspace(ctypes.byref(s))
     _expect(out, q.shape, torch.float32, "out")
     if out is None:
-        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        out = _new(stream, q.shape, torch.float32, q.device)
     if ws is None:
-        ws = _ws(need, q.device)
+        ws = _ws(need, q.device, stream)
     check(lib.da_decode_attention(ctypes.byref(s), _vp(q), _vp(k), _vp(v), _vp(out), _vp(ws),
                                   _nbytes(ws), _stream(stream)))
     return out
@@ -123,7 +141,7 @@ def da_decode_attention_partials(q, k, v, scale=None, split_tokens=0, ws=None, s
     shape = (q.shape[0], q.shape[1], ns, q.shape[2] + 4)
     _expect(ws, shape, torch.float32, "ws")
     if ws is None:
-        ws = torch.empty(shape, dtype=torch.float32, device=q.device)
+        ws = _new(stream, shape, torch.float32, q.device)
     check(lib.da_decode_attention_partials(ctypes.byref(s), _vp(q), _vp(k), _vp(v), _vp(ws),
                                            _nbytes(ws), _stream(stream)))
     return ws
@@ -137,7 +155,7 @@ def da_read_stream(buf, n_groups=4096, sink=None, stream=None):
     _dev(buf, sink)
     nb = _nbytes(buf)
     if sink is None:
-        sink = torch.empty(n_groups, dtype=torch.int32, device=buf.device)
+        sink = _new(stream, n_groups, torch.int32, buf.device)
     _expect(sink, (n_groups,), torch.int32, "sink")
     check(lib.da_read_stream(_vp(buf), nb, n_groups, _vp(sink), _stream(stream)))
     return sink
@@ -154,7 +172,7 @@ def da_merge_partials(partials, out=None, stream=None):
     rows = partials.numel() // (ns * (D + 4))
     _expect(out, lead + (D,), torch.float32, "out")
     if out is None:
-        out = torch.empty(lead + (D,), dtype=torch.float32, device=partials.device)
+        out = _new(stream, lead + (D,), torch.float32, partials.device)
     check(lib.da_merge_partials(rows, ns, D, _vp(partials), _vp(out), _stream(stream)))
     return out
 
@@ -169,9 +187,9 @@ def da_build_page_meta(k, page_size, kmin=None, kmax=None, stream=None):
     _expect(kmin, (B, H, P, D), k.dtype, "kmin")
     _expect(kmax, (B, H, P, D), k.dtype, "kmax")
     if kmin is None:
-        kmin = torch.empty((B, H, P, D), dtype=k.dtype, device=k.device)
+        kmin = _new(stream, (B, H, P, D), k.dtype, k.device)
     if kmax is None:
-        kmax = torch.empty((B, H, P, D), dtype=k.dtype, device=k.device)
+        kmax = _new(stream, (B, H, P, D), k.dtype, k.device)
     check(lib.da_build_page_meta(ctypes.byref(s), page_size, _vp(k), _vp(kmin), _vp(kmax),
                                  _stream(stream)))
     return kmin, kmax
@@ -193,9 +211,9 @@ def da_select_pages(q, kmin, kmax, page_size, top_k, n_ctx, page_idx=None, page_
     _expect(page_score, (B, H, P), torch.float32, "page_score")
     s = attn_shape(B, H, Hkv, D, n_ctx, None, _DT[q.dtype], _DT[kmin.dtype])
     if page_idx is None:
-        page_idx = torch.empty((B, H, top_k), dtype=torch.int32, device=q.device)
+        page_idx = _new(stream, (B, H, top_k), torch.int32, q.device)
     if want_scores and page_score is None:
-        page_score = torch.empty((B, H, P), dtype=torch.float32, device=q.device)
+        page_score = _new(stream, (B, H, P), torch.float32, q.device)
     check(lib.da_select_pages(ctypes.byref(s), page_size, top_k, _vp(q), _vp(kmin), _vp(kmax),
                               _vp(page_idx), _vp(page_score), _stream(stream)))
     return (page_idx, page_score) if want_scores else page_idx
@@ -213,18 +231,18 @@ def da_select_tokens(q, k, top_k, token_idx=None, token_score=None, want_scores=
     _expect(token_score, (B, H, N), torch.float32, "token_score")
     s = attn_shape(B, H, Hkv, D, N, None, _DT[q.dtype], _DT[k.dtype])
     if token_idx is None:
-        token_idx = torch.empty((B, H, top_k), dtype=torch.int32, device=q.device)
+        token_idx = _new(stream, (B, H, top_k), torch.int32, q.device)
     if want_scores and token_score is None:
-        token_score = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        token_score = _new(stream, (B, H, N), torch.float32, q.device)
     check(lib.da_select_tokens(ctypes.byref(s), top_k, _vp(q), _vp(k), _vp(token_idx),
                                _vp(token_score), _stream(stream)))
     return (token_idx, token_score) if want_scores else token_idx
 
 
-def keep_count(n_ctx, keep=0.1):
-    """Tokens kept per query by the top-k sparse attention: ceil(keep * n_ctx),
-    at least 1."""
-    return min(n_ctx, max(1, math.ceil(keep * n_ctx - 1e-9)))
+def da_token_keep_count(n_ctx) -> int:
+    """Tokens FlexGen's top-10% sparse attention keeps per query (computed by
+    the library: ceil(n_ctx / 10)); 0 if n_ctx < 1."""
+    return int(load().da_token_keep_count(int(n_ctx)))
 
 
 def da_decode_attention_topk(q, k, v, top_k, scale=None, token_idx=None, want_idx=False, out=None,
@@ -240,9 +258,9 @@ def da_decode_attention_topk(q, k, v, top_k, scale=None, token_idx=None, want_id
     _expect(out, q.shape, torch.float32, "out")
     _expect(token_idx, (B, H, top_k), torch.int32, "token_idx")
     if out is None:
-        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        out = _new(stream, q.shape, torch.float32, q.device)
     if want_idx and token_idx is None:
-        token_idx = torch.empty((B, H, top_k), dtype=torch.int32, device=q.device)
+        token_idx = _new(stream, (B, H, top_k), torch.int32, q.device)
     check(lib.da_decode_attention_topk(ctypes.byref(s), top_k, _vp(q), _vp(k), _vp(v), _vp(out),
                                        _vp(token_idx), _stream(stream)))
     return (out, token_idx) if want_idx else out
@@ -262,7 +280,7 @@ def da_prefill_attention(q, k, v, scale=None, out=None, stream=None):
     s = attn_shape(B, Hq, Hkv, D, T, scale, _DT[q.dtype], _DT[k.dtype])
     _expect(out, q.shape, torch.float32, "out")
     if out is None:
-        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        out = _new(stream, q.shape, torch.float32, q.device)
     check(lib.da_prefill_attention(ctypes.byref(s), C, _vp(q), _vp(k), _vp(v), _vp(out), _stream(stream)))
     return out
 
@@ -280,9 +298,9 @@ def da_decode_attention_paged(q, k, v, page_idx, page_size, scale=None, split_to
         raise ValueError("k and v must have the same shape and dtype")
     need = lib.da_decode_attention_paged_workspace(ctypes.byref(s), page_size, top_k)
     if out is None:
-        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        out = _new(stream, q.shape, torch.float32, q.device)
     if ws is None:
-        ws = _ws(need, q.device)
+        ws = _ws(need, q.device, stream)
     check(lib.da_decode_attention_paged(ctypes.byref(s), page_size, top_k, _vp(page_idx), _vp(q),
                                         _vp(k), _vp(v), _vp(out), _vp(ws), _nbytes(ws),
                                         _stream(stream)))
@@ -306,9 +324,9 @@ def da_decode_attention_sparse(q, kmin, kmax, k, v, page_size, top_k, scale=None
     _expect(out, q.shape, torch.float32, "out")
     _expect(page_idx, (q.shape[0], q.shape[1], top_k), torch.int32, "page_idx")
     if out is None:
-        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        out = _new(stream, q.shape, torch.float32, q.device)
     if page_idx is None and want_idx:
-        page_idx = torch.empty((q.shape[0], q.shape[1], top_k), dtype=torch.int32, device=q.device)
+        page_idx = _new(stream, (q.shape[0], q.shape[1], top_k), torch.int32, q.device)
     check(lib.da_decode_attention_sparse(ctypes.byref(s), page_size, top_k, _vp(q), _vp(kmin), _vp(kmax),
                                          _vp(k), _vp(v), _vp(out), _vp(page_idx), _stream(stream)))
     return (out, page_idx) if (want_idx or page_idx is not None) else out
@@ -327,11 +345,11 @@ def da_quantize_kv4(x, codes=None, gmin=None, gscale=None, stream=None):
     _expect(gmin, lead + (R // 64,), torch.float16, "gmin")
     _expect(gscale, lead + (R // 64,), torch.float16, "gscale")
     if codes is None:
-        codes = torch.empty(lead + (R // 2,), dtype=torch.uint8, device=x.device)
+        codes = _new(stream, lead + (R // 2,), torch.uint8, x.device)
     if gmin is None:
-        gmin = torch.empty(lead + (R // 64,), dtype=torch.float16, device=x.device)
+        gmin = _new(stream, lead + (R // 64,), torch.float16, x.device)
     if gscale is None:
-        gscale = torch.empty(lead + (R // 64,), dtype=torch.float16, device=x.device)
+        gscale = _new(stream, lead + (R // 64,), torch.float16, x.device)
     check(lib.da_quantize_kv4(n_rows, R, _vp(x), _vp(codes), _vp(gmin), _vp(gscale),
                               _stream(stream)))
     return codes, gmin, gscale
@@ -350,7 +368,7 @@ def da_dequantize_kv4(codes, gmin, gscale, out=None, stream=None):
     _expect(gscale, lead + (R // 64,), torch.float16, "gscale")
     _expect(out, lead + (R,), torch.float16, "out")
     if out is None:
-        out = torch.empty(lead + (R,), dtype=torch.float16, device=codes.device)
+        out = _new(stream, lead + (R,), torch.float16, codes.device)
     check(lib.da_dequantize_kv4(n_rows, R, _vp(codes), _vp(gmin), _vp(gscale), _vp(out),
                                 _stream(stream)))
     return out
@@ -373,9 +391,9 @@ def da_decode_attention_kv4(q, k_codes, k_min, k_scale, v_codes, v_min, v_scale,
     s = attn_shape(B, Hq, Hkv, D, N, scale, _DT[q.dtype], DA_F16, split_tokens)
     need = lib.da_decode_attention_kv4_workspace(ctypes.byref(s))
     if out is None:
-        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        out = _new(stream, q.shape, torch.float32, q.device)
     if ws is None:
-        ws = _ws(need, q.device)
+        ws = _ws(need, q.device, stream)
     check(lib.da_decode_attention_kv4(ctypes.byref(s), _vp(q), _vp(k_codes), _vp(k_min),
                                       _vp(k_scale), _vp(v_codes), _vp(v_min), _vp(v_scale),
                                       _vp(out), _vp(ws), _nbytes(ws), _stream(stream)))
@@ -400,6 +418,11 @@ class HeadwiseStream:
         self._ctx = ctypes.c_void_p()
         check(self._lib.da_stream_create(ctypes.byref(self.shape), heads_per_chunk,
                                          ctypes.byref(self._ctx)))
+
+    @staticmethod
+    def _check_dtype(t, want, name):
+        if _DT.get(t.dtype) != want:
+            raise ValueError(f"{name}: dtype {t.dtype} does not match the context's")
 
     @property
     def buffer_bytes(self) -> int:
@@ -429,6 +452,9 @@ class HeadwiseStream:
         qshape = (L, self.shape.batch, self.shape.n_q_heads, self.shape.head_dim)
         if tuple(q.shape) != qshape or tuple(out.shape) != qshape or out.dtype != torch.float32:
             raise ValueError(f"q and out must be {qshape} (out fp32)")
+        self._check_dtype(q, self.shape.q_dtype, "q")
+        for t in list(k_host) + list(v_host):
+            self._check_dtype(t, self.shape.kv_dtype, "host KV")
         kp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in k_host])
         vp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in v_host])
         check(self._lib.da_stream_headwise(self._ctx, n // self.shape.n_kv_heads, kp, vp,
@@ -456,9 +482,11 @@ class HeadwiseStream:
         for t in (k_new, v_new):
             if tuple(t.shape) != want or not t.is_contiguous():
                 raise ValueError(f"new rows must be contiguous {want}")
+            self._check_dtype(t, self.shape.kv_dtype, "new rows")
         for t in list(k_host) + list(v_host):
             if t.is_cuda or not t.is_contiguous():
                 raise ValueError("host KV tensors must be contiguous CPU tensors")
+            self._check_dtype(t, self.shape.kv_dtype, "host KV")
         kp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in k_host])
         vp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in v_host])
         check(self._lib.da_stream_append(self._ctx, L, _vp(k_new), _vp(v_new), kp, vp, _stream(stream)))

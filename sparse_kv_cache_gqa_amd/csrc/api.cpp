@@ -281,6 +281,12 @@ da_status da_select_tokens(const da_attn_shape *s, int32_t top_k, const void *q,
     return ok();
 }
 
+int64_t da_token_keep_count(int64_t n_ctx) {
+    if (n_ctx < 1) return 0;
+    // ceil(n_ctx / 10) in integers: no rounding of 0.1 * n_ctx to worry about
+    return n_ctx / 10 + (n_ctx % 10 != 0 ? 1 : 0);
+}
+
 da_status da_decode_attention_topk(const da_attn_shape *s, int32_t top_k, const void *q, const void *k, const void *v,
                                    float *o, int32_t *token_idx, hipStream_t stream) {
     DA_TRY(check_shape(s, false));
@@ -361,6 +367,7 @@ da_status da_prefill_attention(const da_attn_shape *s, int64_t chunk, const void
 size_t da_decode_attention_paged_workspace(const da_attn_shape *s, int32_t page_size, int32_t top_k) {
     if (check_shape(s, false) != DA_OK || check_page(page_size) != DA_OK) return 0;
     if (top_k < 1 || top_k > n_pages(s, page_size)) return 0;
+    if ((int64_t)s->batch * s->n_q_heads > 65535) return 0;
     const int32_t ns = attn_n_split(s->n_ctx, split_tokens_of(s, SPLIT_PAGED), true, top_k, ilog2(page_size));
     return attn_ws_bytes((int64_t)s->batch * s->n_q_heads, ns, s->head_dim);
 }
@@ -372,6 +379,9 @@ da_status da_decode_attention_paged(const da_attn_shape *s, int32_t page_size, i
     DA_TRY(check_page(page_size));
     const int64_t P = n_pages(s, page_size);
     if (top_k < 1 || top_k > P) return fail(DA_E_INVALID, "top_k %d not in [1, %lld]", top_k, (long long)P);
+    // one unit per query head: the grid's second dimension is batch * n_q_heads
+    if ((int64_t)s->batch * s->n_q_heads > 65535)
+        return fail(DA_E_UNSUPPORTED, "batch * n_q_heads %lld > 65535", (long long)s->batch * s->n_q_heads);
     if (s->batch == 0) return ok();
     DA_TRY(check_ptr(page_idx, "page_idx"));
     DA_TRY(check_ptr(q, "q"));

@@ -157,7 +157,8 @@ __device__ __forceinline__ void merge_in_workgroup(const AttnLaunch &a, const fl
             O0 = fmaf(w, ps[s * slot + d], O0);
         }
         const float L = L01 + L23;
-        ob[h * D + d] = ((O0 + O1) + (O2 + O3)) / L;
+        // L == 0: no split saw a token (every listed page out of range)
+        ob[h * D + d] = L > 0.f ? ((O0 + O1) + (O2 + O3)) / L : 0.f;
     }
 }
 
@@ -756,7 +757,7 @@ __global__ __launch_bounds__(128) void attn_reduce_kernel(const float *__restric
                 O0 = fmaf(f, p[(int64_t)s * PSTR + d], O0);
             }
         }
-        o[(int64_t)b * o_bstride + (int64_t)hq * D + d] = ((O0 + O1) + (O2 + O3)) / L;
+        o[(int64_t)b * o_bstride + (int64_t)hq * D + d] = L > 0.f ? ((O0 + O1) + (O2 + O3)) / L : 0.f;
     }
 }
 
@@ -801,7 +802,7 @@ __global__ __launch_bounds__(256) void attn_reduce_small_kernel(const float *__r
 #pragma unroll
     for (int j = 0; j < kMergeSmall; ++j)
         if (j < n_split) O0 = fmaf(w[j], p[j * PSTR + d], O0);
-    o[b * o_bstride + hq * D + d] = ((O0 + O1) + (O2 + O3)) / L;
+    o[b * o_bstride + hq * D + d] = L > 0.f ? ((O0 + O1) + (O2 + O3)) / L : 0.f;
 }
 
 using SplitFn = void (*)(AttnLaunch);

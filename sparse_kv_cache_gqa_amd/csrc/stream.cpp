@@ -3,7 +3,9 @@
 // device buffers alternate: while attention runs on one (compute stream), the
 // next chunk of heads is copied host-to-device into the other (copy stream).
 // Ordering uses two events per buffer: `ready` (copy done -> compute may
-// start) and `freed` (compute done -> the buffer may be overwritten).
+// start) and `freed` (compute done -> the buffer may be overwritten).  Every
+// copy into a buffer waits for that buffer's last `freed`, also across calls,
+// so back-to-back calls on one context need no ordering by the caller.
 //
 // HeadInfer also writes the previous head back device-to-host; a decode step
 // does not change the cached keys and values, so there is nothing to write
@@ -27,6 +29,11 @@ struct da_stream_ctx {
     int device;
     hipEvent_t ready[2];
     hipEvent_t freed[2];
+    // freed[i] has been recorded (by this call or an earlier one): every
+    // later copy into buffer i must wait for it, including the first two
+    // copies of the next call, whose buffers the previous call's last two
+    // attentions may still be reading
+    bool freed_recorded[2];
 };
 
 namespace da {
@@ -180,7 +187,7 @@ da_status da_stream_headwise(da_stream_ctx *c, int32_t n_layers, const void *con
             const int slot = (int)(u & 1);
             char *kb = (char *)bufs[slot];
             char *vb = kb + (size_t)c->hpc * hb;
-            if (u >= 2) e = hipStreamWaitEvent(copy, c->freed[slot], 0);
+            if (c->freed_recorded[slot]) e = hipStreamWaitEvent(copy, c->freed[slot], 0);
             for (int i = 0; i < c->hpc && e == hipSuccess; ++i) {
                 const int64_t hi = (int64_t)l * s->n_kv_heads + (int64_t)ch * c->hpc + i;
                 e = h2d(kb + i * hb, k_host[hi]);
@@ -196,6 +203,7 @@ da_status da_stream_headwise(da_stream_ctx *c, int32_t n_layers, const void *con
             a.v = vb;
             e = launch_attention(a, compute);
             if (e == hipSuccess) e = hipEventRecord(c->freed[slot], compute);
+            if (e == hipSuccess) c->freed_recorded[slot] = true;
         }
     }
     if (e != hipSuccess) return hip_fail(e, "head-wise streaming");

@@ -20,9 +20,10 @@ def report(got: np.ndarray, ref: np.ndarray) -> dict:
             "max_rel_rms": float(err.max() / rms) if rms > 0 else float(err.max())}
 
 
-def assert_close(got, ref, atol, rel_rms=None, what=""):
+def assert_close(got, ref, atol, rel_rms=None, what="", quiet=False):
     r = report(got, ref)
-    print(f"[parity] {what} {r}", flush=True)
+    if not quiet:
+        print(f"[parity] {what} {r}", flush=True)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     assert r["max_abs"] <= atol, f"{what}: max |err| {r['max_abs']:.3e} > {atol:.1e}"
     if rel_rms is not None:
@@ -60,3 +61,16 @@ def check_selection(got_idx: np.ndarray, r: np.ndarray, top_k: int, rel_band: fl
                     f"({b},{h}) page {j}: score {r[b, h, j]!r} vs k-th {sK!r}"
                 n_diff += 1
     return n_diff
+
+
+def each_row(fn, n: int):
+    """fn(0) .. fn(n-1) on a thread pool (the oracle's NumPy work releases the
+    GIL), in order; for full-size checks computed one batch row at a time."""
+    import concurrent.futures as cf
+    import os
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    with cf.ThreadPoolExecutor(max(1, min(16, cores))) as ex:
+        return list(ex.map(fn, range(n)))

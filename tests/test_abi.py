@@ -20,6 +20,11 @@ NULL = ctypes.c_void_p(0)
 
 @pytest.fixture(scope="module")
 def lib():
+    # DA_ABI_LIB names another build of the same sources to check instead
+    # (the host-sanitizer build that tests/test_abi_sanitized.py makes)
+    alt = os.environ.get("DA_ABI_LIB")
+    if alt:
+        return L.load(alt)
     if not os.path.exists(L.LIB_PATH):
         pytest.fail("libda.so is not built (run __graft_entry__.build())")
     return L.load()
@@ -144,6 +149,12 @@ def test_page_checks(lib):
     need = lib.da_decode_attention_paged_workspace(ctypes.byref(s), 16, 128)
     assert need == 32 * 16 * 4 * 68 * 4           # 128 pages of 16 = 2048 positions / 512
     assert paged(s, 128, need - 4) == L.DA_E_WORKSPACE
+    # one unit per query head: batch * n_q_heads must fit the grid's second
+    # dimension (here 8192 * 16 = 131072 with batch * n_kv_heads = 16384)
+    big = mha(batch=8192, n_q_heads=16, n_kv_heads=2)
+    assert lib.da_decode_attention_paged_workspace(ctypes.byref(big), 16, 128) == 0
+    assert paged(big, 128) == L.DA_E_UNSUPPORTED
+    assert b"65535" in lib.da_last_error()
     sp = lambda sh, ps, k, q=FAKE, idx=NULL: lib.da_decode_attention_sparse(
         ctypes.byref(sh), ps, k, q, FAKE, FAKE, FAKE, FAKE, FAKE, idx, NULL)
     assert sp(s, 3, 128) == L.DA_E_INVALID                              # page size
@@ -253,3 +264,16 @@ def test_headwise_sizes_match_the_pages_and_checks(lib):
     assert lib.da_stream_buffer_bytes(None) == 0
     assert lib.da_stream_workspace(None) == 0
     lib.da_stream_destroy(None)
+
+
+def test_token_keep_count_matches_the_oracle(lib):
+    """FlexGen's kept-token count (ceil of 10% of the context) as the library
+    computes it, against the oracle's rule, for every context 1..20000."""
+    from oracle import keep_count
+    for n in range(1, 20001):
+        assert lib.da_token_keep_count(n) == keep_count(n), n
+    assert lib.da_token_keep_count(1024) == 103
+    assert lib.da_token_keep_count(0) == 0
+    assert lib.da_token_keep_count(-3) == 0
+    assert lib.da_token_keep_count(1 << 40) == -(-(1 << 40) // 10)
+

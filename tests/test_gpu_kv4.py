@@ -19,7 +19,7 @@ import synth
 from oracle import dequantize_kv4, kv4_attention, quantize_kv4, decode_attention
 from oracle.kv4 import unpack_codes
 from oracle.numerics import as_f64
-from gpu_util import assert_close, to_dev
+from gpu_util import assert_close, each_row, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -136,27 +136,31 @@ def test_kv4_integer_data_equals_dense(da):
     assert_close(o, ref, atol=1e-5, rel_rms=1e-5, what="kv4 integer data")
 
 
-def test_workload4_full_size_sampled(da):
-    """FlexGen shape (B64 H56 D128 N1024): codes of sampled rows bit-exact,
-    attention of sampled heads, in the benchmark's launch configuration."""
+def test_workload4_full_size_every_row(da):
+    """FlexGen shape (B64 H56 D128 N1024) in the benchmark's launch
+    configuration: the codes, minima and scales of every row bit-exact, and
+    the attention of every (batch row, head) against the oracle, one batch
+    row at a time."""
     c = synth.workload4()
     o, kq, vq = run_kv4(da, c)
-    rng = np.random.default_rng(4)
-    picks = [(0, 0), (63, 55)] + [(int(b), int(h)) for b, h in
-                                  zip(rng.integers(0, 64, 6), rng.integers(0, 56, 6))]
-    for b, h in picks:
-        want_k = quantize_kv4(c.k[b, h])
-        want_v = quantize_kv4(c.v[b, h])
-        assert_quant_equal([t[b, h] for t in kq], want_k)
-        assert_quant_equal([t[b, h] for t in vq], want_v)
-        ref = kv4_attention(as_f64(c.q[b:b + 1, h:h + 1], "f16"),
-                            *[t[None, None] for t in want_k], *[t[None, None] for t in want_v],
-                            c.scale)
-        assert_close(o[b, h], ref[0, 0], atol=1e-3, rel_rms=3e-3, what=f"w4 b{b} h{h}")
-        fold = decode_attention(as_f64(c.q[b:b + 1, h:h + 1], "f16"),
-                                unrounded(*want_k)[None, None], unrounded(*want_v)[None, None],
-                                c.scale)
-        assert_close(o[b, h], fold[0, 0], atol=1e-5, rel_rms=1e-4, what="  vs unrounded dequant")
+
+    def row(b):
+        want_k = quantize_kv4(c.k[b:b + 1])
+        want_v = quantize_kv4(c.v[b:b + 1])
+        assert_quant_equal([t[b:b + 1] for t in kq], want_k)
+        assert_quant_equal([t[b:b + 1] for t in vq], want_v)
+        q64 = as_f64(c.q[b:b + 1], "f16")
+        ref = kv4_attention(q64, *want_k, *want_v, c.scale)
+        fold = decode_attention(q64, unrounded(*want_k), unrounded(*want_v), c.scale)
+        e1 = max(assert_close(o[b, h], ref[0, h], atol=1e-3, rel_rms=3e-3, what=f"w4 b{b} h{h}", quiet=True)
+                 ["max_abs"] for h in range(ref.shape[1]))
+        e2 = max(assert_close(o[b, h], fold[0, h], atol=1e-5, rel_rms=1e-4, what=f"w4 fold b{b} h{h}",
+                              quiet=True)["max_abs"] for h in range(ref.shape[1]))
+        return e1, e2
+
+    rs = each_row(row, c.q.shape[0])
+    print(f"[parity] w4 all 64x56 heads: max |err| {max(r[0] for r in rs):.2e} vs oracle, "
+          f"{max(r[1] for r in rs):.2e} vs unrounded dequantization", flush=True)
 
 
 @pytest.mark.parametrize("qd", ["f16", "f32"])

@@ -13,7 +13,7 @@ import pytest
 import synth
 from oracle import bound_scores, decode_attention, page_meta, sparse_attention
 from oracle.numerics import as_f64
-from gpu_util import assert_close, check_selection, from_dev, to_dev
+from gpu_util import assert_close, check_selection, each_row, from_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -105,10 +105,11 @@ def test_fused_without_page_list(da):
     assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
 
 
-def test_workload3_fused_full_size_sampled(da):
-    """TinyServe shape in one kernel (as bench.py's fused step): the kept
-    pages equal the two-kernel path's, attention of sampled heads against the
-    oracle on that set."""
+def test_workload3_fused_full_size_every_row(da):
+    """TinyServe shape in one kernel (as bench.py's step): the kept pages of
+    every (batch row, head) equal the two-kernel path's and pass the selection
+    rule against the oracle's bound scores; attention of every head against
+    the oracle on that set.  The oracle runs one batch row at a time."""
     import torch
     c = synth.workload3()
     S, K = c.page_size, c.top_k
@@ -120,15 +121,16 @@ def test_workload3_fused_full_size_sampled(da):
     idx = idx.cpu().numpy()
     assert np.array_equal(idx, two.cpu().numpy())
     o = o.cpu().numpy()
-    rng = np.random.default_rng(5)
-    picks = [(0, 0), (31, 15)] + [(int(b), int(h)) for b, h in
-                                  zip(rng.integers(0, 32, 6), rng.integers(0, 16, 6))]
-    for b, h in picks:
-        q64 = as_f64(c.q[b:b + 1, h:h + 1], "f16")
-        k64 = as_f64(c.k[b:b + 1, h:h + 1], "f16")
-        v64 = as_f64(c.v[b:b + 1, h:h + 1], "f16")
-        ref = sparse_attention(q64, k64, v64, idx[b:b + 1, h:h + 1], S, c.scale)
-        assert_close(o[b, h], ref[0, 0], atol=1e-3, rel_rms=1e-4, what=f"w3 fused b{b} h{h}")
+    del q, k, v, kmin, kmax
+
+    def row(b):
+        q64, k64, v64 = (as_f64(x[b:b + 1], "f16") for x in (c.q, c.k, c.v))
+        check_selection(idx[b:b + 1], bound_scores(q64, *page_meta(k64, S)), K)
+        ref = sparse_attention(q64, k64, v64, idx[b:b + 1], S, c.scale)
+        return max(assert_close(o[b:b + 1, h], ref[:, h], atol=1e-3, rel_rms=1e-4, what=f"w3 fused b{b} h{h}", quiet=True)
+                   ["max_abs"] for h in range(ref.shape[1]))
+
+    print(f"[parity] w3 fused all 32x16 heads: max |err| {max(each_row(row, c.q.shape[0])):.2e}", flush=True)
 
 
 def torch_idx(idx):
@@ -151,14 +153,26 @@ def test_out_of_range_pages_are_skipped(da):
     idx = np.array([[[0, 3, 6, 99]], [[-1, 2, 5, 1000]]], dtype=np.int32).reshape(1, 2, 4)
     q, k, v = to_dev(c.q, "f16"), to_dev(c.k, "f16"), to_dev(c.v, "f16")
     o = da.da_decode_attention_paged(q, k, v, torch_idx(idx), 16).cpu().numpy()
-    ref0 = sparse_attention(as_f64(c.q, "f16")[:, :1], as_f64(c.k, "f16")[:, :1],
-                            as_f64(c.v, "f16")[:, :1], np.array([[[0, 3, 6]]], dtype=np.int32),
-                            16, c.scale)
-    ref1 = sparse_attention(as_f64(c.q, "f16")[:, 1:], as_f64(c.k, "f16")[:, 1:],
-                            as_f64(c.v, "f16")[:, 1:], np.array([[[2, 5]]], dtype=np.int32),
-                            16, c.scale)
-    assert_close(o[:, :1], ref0, atol=1e-5, what="skip >= P")
-    assert_close(o[:, 1:], ref1, atol=1e-5, what="skip < 0")
+    # the oracle takes the raw lists and skips the same indices itself
+    ref = sparse_attention(as_f64(c.q, "f16"), as_f64(c.k, "f16"), as_f64(c.v, "f16"), idx, 16, c.scale)
+    assert_close(o[:, :1], ref[:, :1], atol=1e-5, what="skip >= P")
+    assert_close(o[:, 1:], ref[:, 1:], atol=1e-5, what="skip < 0")
+
+
+@pytest.mark.parametrize("split", [0, 32, 16])
+def test_all_pages_out_of_range_gives_zero(da, split):
+    """A list with no page inside the cache attends nothing: the output is
+    zero (not 0/0) on all three merge routes -- in the workgroup (one split
+    of 512 positions), the small merge kernel (3 splits of 2 pages) and the
+    block merge kernel (6 splits of 1 page) -- beside a row with valid pages."""
+    c = synth.paged_case([205], 1, 2, 64, 100, 16, 6, dtype="f16")   # P = 7
+    idx = np.array([[[-3, 7, 99, 1 << 20, 8, -100]], [[1, 7, 4, -1, 6, 2]]],
+                   dtype=np.int32).reshape(1, 2, 6)
+    q, k, v = to_dev(c.q, "f16"), to_dev(c.k, "f16"), to_dev(c.v, "f16")
+    o = da.da_decode_attention_paged(q, k, v, torch_idx(idx), 16, split_tokens=split).cpu().numpy()
+    ref = sparse_attention(as_f64(c.q, "f16"), as_f64(c.k, "f16"), as_f64(c.v, "f16"), idx, 16, c.scale)
+    assert not np.any(ref[:, 0]) and np.all(o[:, 0] == 0.0), "empty list: output must be zero"
+    assert_close(o, ref, atol=1e-5, what=f"empty and valid lists, split {split}")
 
 
 def test_split_sizes_agree_paged(da):
@@ -173,10 +187,11 @@ def test_split_sizes_agree_paged(da):
         assert_close(o, ref, atol=1e-5, rel_rms=1e-4, what=f"paged split {st}")
 
 
-def test_workload3_full_size_sampled(da):
-    """TinyServe shape (B32 H16 D64 N32768 fp16, page 16, top-128), in the
-    benchmark's launch configuration; selection and attention checked on
-    sampled (row, head) pairs, metadata on sampled pages."""
+def test_workload3_full_size_every_row(da):
+    """TinyServe shape (B32 H16 D64 N32768 fp16, page 16, top-128) as two
+    calls, in the benchmark's launch configuration: the metadata of every
+    page equal by value, the selection of every (batch row, head) within the
+    rule, and attention of every head against the oracle on the GPU's set."""
     import torch
     c = synth.workload3()
     S, K = c.page_size, c.top_k
@@ -185,22 +200,24 @@ def test_workload3_full_size_sampled(da):
     idx = da.da_select_pages(q, kmin, kmax, S, K, 32768)
     o = da.da_decode_attention_paged(q, k, v, idx, S)
     torch.cuda.synchronize()
-    idx = idx.cpu().numpy()
-    o = o.cpu().numpy()
-    kmin = kmin.cpu().numpy()
-    rng = np.random.default_rng(3)
-    picks = [(0, 0), (31, 15)] + [(int(b), int(h)) for b, h in
-                                  zip(rng.integers(0, 32, 6), rng.integers(0, 16, 6))]
-    for b, h in picks:
-        q64 = as_f64(c.q[b:b + 1, h:h + 1], "f16")
-        k64 = as_f64(c.k[b:b + 1, h:h + 1], "f16")
-        v64 = as_f64(c.v[b:b + 1, h:h + 1], "f16")
+    idx, o = idx.cpu().numpy(), o.cpu().numpy()
+    kmin, kmax = kmin.cpu().numpy(), kmax.cpu().numpy()
+    del q, k, v
+
+    def row(b):
+        q64, k64, v64 = (as_f64(x[b:b + 1], "f16") for x in (c.q, c.k, c.v))
         rmin, rmax = page_meta(k64, S)
-        assert np.array_equal(kmin[b:b + 1, h:h + 1].astype(np.float64), rmin)
-        r = bound_scores(q64, rmin, rmax)
-        check_selection(idx[b:b + 1, h:h + 1], r, K)
-        ref = sparse_attention(q64, k64, v64, idx[b:b + 1, h:h + 1], S, c.scale)
-        assert_close(o[b, h], ref[0, 0], atol=1e-3, rel_rms=1e-4, what=f"w3 b{b} h{h}")
+        assert np.array_equal(kmin[b:b + 1].astype(np.float64), rmin), f"kmin row {b}"
+        assert np.array_equal(kmax[b:b + 1].astype(np.float64), rmax), f"kmax row {b}"
+        n_diff = check_selection(idx[b:b + 1], bound_scores(q64, rmin, rmax), K)
+        ref = sparse_attention(q64, k64, v64, idx[b:b + 1], S, c.scale)
+        err = max(assert_close(o[b:b + 1, h], ref[:, h], atol=1e-3, rel_rms=1e-4, what=f"w3 b{b} h{h}", quiet=True)
+                  ["max_abs"] for h in range(ref.shape[1]))
+        return err, n_diff
+
+    rs = each_row(row, c.q.shape[0])
+    print(f"[parity] w3 all 32x16 heads: max |err| {max(r[0] for r in rs):.2e}, "
+          f"{sum(r[1] for r in rs)} pages swapped inside the tie band", flush=True)
 
 
 @pytest.mark.parametrize("P,K", [(64, 10), (300, 77), (2048, 128)])

@@ -123,6 +123,24 @@ def test_sparse_single_page_is_attention_over_that_page():
     np.testing.assert_allclose(o[0, 0], want, atol=1e-14)
 
 
+def test_sparse_out_of_range_pages_hold_no_tokens():
+    """Listed page indices outside [0, P) name no token of the cache: with them
+    the result is attention over the in-range pages, computed by hand; a list
+    of out-of-range pages only attends nothing and gives zero."""
+    rng = np.random.default_rng(16)
+    q = rng.standard_normal((1, 2, 4))
+    k = rng.standard_normal((1, 2, 10, 4))
+    v = rng.standard_normal((1, 2, 10, 4))
+    idx = np.array([[[-1, 1, 3, 40], [-7, 3, 4, 1 << 30]]], dtype=np.int32)   # P = 3 (page 4)
+    o = sparse_attention(q, k, v, idx, 4, 1.0)
+    # head 0: page 1 = tokens 4..7; pages -1, 3 and 40 are outside the cache
+    s = [float(q[0, 0] @ k[0, 0, t]) for t in range(4, 8)]
+    w = [math.exp(x - max(s)) for x in s]
+    want = sum(wi * v[0, 0, t] for wi, t in zip(w, range(4, 8))) / sum(w)
+    np.testing.assert_allclose(o[0, 0], want, atol=1e-14)
+    assert np.all(o[0, 1] == 0.0)
+
+
 def test_planted_page_is_selected():
     c = synth.paged_case(97, 1, 2, 16, 256, 16, 3, boost_frac=0.0)
     q = as_f64(c.q, "f16")
