@@ -138,6 +138,26 @@ da_status da_decode_attention(const da_attn_shape *s, const void *q,
                               void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * da_decode_attention without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc).  Same kernels, split and result bit for bit as
+ * da_decode_attention; the split-K partials go to a fixed array of
+ * da_decode_attention_noalloc_max_scratch() bytes (16 MiB) that the library
+ * holds on each GPU it runs on until the process ends.  A shape whose
+ * da_decode_attention_workspace exceeds that size is refused with
+ * DA_E_UNSUPPORTED (nothing enqueued).  The call allocates nothing (no
+ * hipMalloc or hipFree); the first call on a device looks up the array's
+ * device address once.  Every call on one GPU shares that array: calls that
+ * may overlap on one GPU (different streams, or host threads without
+ * ordering) race and must not be issued; calls ordered on one stream are
+ * safe.  Nothing in the array needs to start zeroed.
+ * ------------------------------------------------------------------------ */
+size_t da_decode_attention_noalloc_max_scratch(void);
+da_status da_decode_attention_noalloc(const da_attn_shape *s, const void *q,
+                                      const void *k, const void *v, float *o,
+                                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * The two halves of da_decode_attention, for callers that merge partials
  * themselves (for example partials computed over different token ranges, on
  * different devices, of one sequence) or time the passes apart.

@@ -20,7 +20,7 @@ from ._lib import (DA_BF16, DA_E_HIP, DA_E_INVALID, DA_E_NOT_PINNED,  # noqa: F4
 
 
 from .api import (HeadwiseStream, attn_shape, da_build_page_meta,  # noqa: F401,E402
-                  da_decode_attention, da_decode_attention_kv4, da_decode_attention_n_split,
+                  da_decode_attention, da_decode_attention_noalloc, da_decode_attention_kv4, da_decode_attention_n_split,
                   da_decode_attention_paged, da_decode_attention_partials, da_merge_partials,
                   da_decode_attention_workspace, da_decode_attention_paged_workspace,
                   da_decode_attention_kv4_workspace,

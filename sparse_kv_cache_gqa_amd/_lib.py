@@ -43,6 +43,8 @@ SIGNATURES = {
     "da_decode_attention_workspace": (c_sz, [SHAPE]),
     "da_decode_attention": (ctypes.c_int, [SHAPE, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "da_decode_attention_n_split": (c_i32, [SHAPE]),
+    "da_decode_attention_noalloc_max_scratch": (c_sz, []),
+    "da_decode_attention_noalloc": (ctypes.c_int, [SHAPE, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "da_decode_attention_partials": (ctypes.c_int, [SHAPE, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "da_merge_partials": (ctypes.c_int, [c_i64, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "da_build_page_meta": (ctypes.c_int, [SHAPE, c_i32, c_vp, c_vp, c_vp, c_vp]),

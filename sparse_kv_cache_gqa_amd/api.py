@@ -105,6 +105,21 @@ def da_decode_attention(q, k, v, scale=None, split_tokens=0, out=None, ws=None, 
     return out
 
 
+def da_decode_attention_noalloc(q, k, v, out, scale=None, split_tokens=0, stream=None):
+    """da_decode_attention with the split-K partials in the library's fixed
+    per-GPU scratch array: no workspace, and `out` (fp32 [B][Hq][D]) is the
+    caller's, so the call allocates nothing."""
+    lib = load()
+    _dev(q, k, v, out)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must have the same shape and dtype")
+    s = _dense_shape(q, k, scale, split_tokens)
+    _expect(out, q.shape, torch.float32, "out")
+    check(lib.da_decode_attention_noalloc(ctypes.byref(s), _vp(q), _vp(k), _vp(v), _vp(out),
+                                          _stream(stream)))
+    return out
+
+
 def da_decode_attention_workspace(batch, n_q_heads, n_kv_heads, head_dim, n_ctx, q_dtype=DA_F32,
                                   kv_dtype=DA_BF16, split_tokens=0) -> int:
     s = attn_shape(batch, n_q_heads, n_kv_heads, head_dim, n_ctx, None, q_dtype, kv_dtype,

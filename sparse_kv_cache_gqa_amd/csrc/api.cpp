@@ -171,6 +171,37 @@ da_status da_decode_attention(const da_attn_shape *s, const void *q, const void 
     return ok();
 }
 
+size_t da_decode_attention_noalloc_max_scratch(void) { return kNoAllocScratchBytes; }
+
+da_status da_decode_attention_noalloc(const da_attn_shape *s, const void *q, const void *k, const void *v,
+                                      float *o, hipStream_t stream) {
+    DA_TRY(check_shape(s, false));
+    if (s->batch == 0) return ok();
+    DA_TRY(check_ptr(q, "q"));
+    DA_TRY(check_ptr(k, "k"));
+    DA_TRY(check_ptr(v, "v"));
+    DA_TRY(check_ptr(o, "o"));
+    const size_t need = da_decode_attention_workspace(s);
+    if (need > kNoAllocScratchBytes)
+        return fail(DA_E_UNSUPPORTED, "this shape needs %zu bytes of split-K scratch, more than the %zu bytes "
+                    "the allocation-free entry point holds; use da_decode_attention with a workspace",
+                    need, (size_t)kNoAllocScratchBytes);
+    AttnLaunch a = dense_launch(s, s->kv_dtype, SPLIT_DENSE);
+    if (!attn_supported(a.kv_fmt, a.q_fmt, a.D, a.G, false))
+        return fail(DA_E_UNSUPPORTED, "no kernel for this dtype / head_dim / group combination");
+    float *scr = nullptr;
+    hipError_t e = noalloc_scratch(&scr);
+    if (e != hipSuccess) return hip_fail(e, "scratch address");
+    a.q = q;
+    a.o = o;
+    a.k = k;
+    a.v = v;
+    a.ws = scr;
+    e = launch_attention(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "decode attention launch");
+    return ok();
+}
+
 da_status da_decode_attention_partials(const da_attn_shape *s, const void *q, const void *k, const void *v,
                                        void *ws, size_t ws_bytes, hipStream_t stream) {
     DA_TRY(check_shape(s, false));

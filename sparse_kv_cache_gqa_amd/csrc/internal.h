@@ -126,6 +126,13 @@ hipError_t launch_prefill(int fmt, int64_t B, int32_t Hq, int32_t Hkv, int D, in
                           float scale_log2, const void *q, const void *k, const void *v, float *o,
                           hipStream_t stream);
 
+// Allocation-free decode attention: the split-K partials go to a fixed
+// device array of kNoAllocScratchBytes per GPU.  noalloc_scratch returns its
+// device address on the current GPU (looked up with hipGetSymbolAddress on
+// the first call on each device; later calls allocate and look up nothing).
+constexpr size_t kNoAllocScratchBytes = 16u << 20;
+hipError_t noalloc_scratch(float **out);
+
 // uint4 group quantization.
 hipError_t launch_read_stream(const void *buf, int64_t n16, int32_t n_groups, uint32_t *sink, hipStream_t stream);
 hipError_t launch_quantize_kv4(int64_t n_groups, const void *x, uint8_t *codes,

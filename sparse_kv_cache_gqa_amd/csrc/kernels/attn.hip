@@ -35,6 +35,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace da {
 namespace {
 
@@ -879,7 +881,37 @@ SplitKernel pick(int kv, int qf, int D, int G, bool paged) {
     }
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+// Split-K partials of the allocation-free entry point: a fixed device array
+// (one per GPU the library runs on, held until the process ends) instead of
+// a caller workspace.  Host code never passes `scratch` itself to a kernel --
+// in host code the name stands for a host-side shadow, not a device address;
+// it passes the device address that hipGetSymbolAddress returns for the
+// current GPU, looked up once per device.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+hipError_t noalloc_scratch(float **out) {
+    *out = nullptr;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));      // this device's copy
+        if (e != hipSuccess) return e;
+        if (!p || ((uintptr_t)p & 255u) != 0) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = (float *)p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 int32_t default_split_dense(int64_t n_ctx) {
     int64_t want = (n_ctx + 15) / 16;

@@ -277,3 +277,18 @@ def test_token_keep_count_matches_the_oracle(lib):
     assert lib.da_token_keep_count(-3) == 0
     assert lib.da_token_keep_count(1 << 40) == -(-(1 << 40) // 10)
 
+
+def test_noalloc_checks(lib):
+    """The allocation-free entry point refuses, before anything is enqueued,
+    a shape whose split-K partials exceed its fixed scratch array, as well as
+    the usual bad arguments."""
+    assert lib.da_decode_attention_noalloc_max_scratch() == 16 << 20
+    call = lambda s, q=FAKE, o=FAKE: lib.da_decode_attention_noalloc(ctypes.byref(s), q, FAKE, FAKE, o, NULL)
+    big = shape(batch=64, n_ctx=1 << 20)          # 64 x 32 rows x 512 splits x 132 floats
+    assert lib.da_decode_attention_workspace(ctypes.byref(big)) > (16 << 20)
+    assert call(big) == L.DA_E_UNSUPPORTED
+    assert b"scratch" in lib.da_last_error()
+    assert call(shape(head_dim=96)) == L.DA_E_UNSUPPORTED
+    assert call(shape(), q=MISALIGNED) == L.DA_E_INVALID
+    assert call(shape(), o=NULL) == L.DA_E_INVALID
+    assert call(shape(batch=0)) == L.DA_OK
