@@ -196,11 +196,20 @@ def bench_dense(args, torch, np, da, synth):
     def step(i):
         da.da_decode_attention(q, ks[i & 1], vs[i & 1], scale=c.scale, out=out, ws=ws)
 
-    ms_eager = time_events(torch, step, args.steps, args.warmup)
-    ms = ms_eager if args.no_graph else time_graph(torch, step, args.steps, args.warmup)
-
     def partial(i):
         da.da_decode_attention_partials(q, ks[i & 1], vs[i & 1], scale=c.scale, ws=ws_p)
+
+    if args.trace_step:
+        # profiling runs: only the headline step, as its two kernels back to
+        # back, with the in-step events of the live figure
+        ms_partial, ms_in_step = time_in_step(torch, partial, lambda i: da.da_merge_partials(ws_p, out=out),
+                                              args.steps)
+        log(f"trace-step: partial pass in the step {ms_partial * 1e3:.1f} us, step {ms_in_step * 1e3:.1f} us "
+            f"({args.steps} timed steps after the warm-up)")
+        return c, None
+
+    ms_eager = time_events(torch, step, args.steps, args.warmup)
+    ms = ms_eager if args.no_graph else time_graph(torch, step, args.steps, args.warmup)
 
     for i in range(3):
         partial(i)
@@ -828,6 +837,9 @@ def main(argv=None) -> int:
     ap.add_argument("--only", default="",
                     help="comma list of dense,sparse,kv4,topk,prefill,stream (profiling runs; no JSON line "
                          "unless dense is included)")
+    ap.add_argument("--trace-step", action="store_true",
+                    help="profiling runs: time only the headline step's two kernels in back-to-back steps "
+                         "(warm-up, then --steps steps); no JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run three 512 MiB device-to-device copies (a kernel of known "
                          "traffic, for scaling hardware byte counters)")
@@ -869,6 +881,8 @@ def main(argv=None) -> int:
         return 0
 
     c, dense = bench_dense(args, torch, np, da, synth)
+    if args.trace_step:
+        return 0
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle on a sample")

@@ -693,26 +693,40 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     if (fused) merge_in_workgroup<G, D>(a, mrg_lds, b, hkv, wave, lane);
 }
 
-// Merge of the split partials of one query-head row (one block per row).
-// Partial row: [u(D), m, l, pad, pad].  Weights 2^(m_s - M) are computed once
-// per split into LDS, then every thread sums its channel over the splits.
-constexpr int kMergeMaxLds = 8192;
+// Merge of the split partials of query-head rows: two rows per block, D
+// threads per row (one per output channel).  Partial row: [u(D), m, l, pad,
+// pad].  Weights 2^(m_s - M) are computed once per split into LDS, then every
+// thread sums its channel over the splits.  (Two rows per block rather than
+// one: measured on MI355X at 256 rows x 16 splits, the partial pass that
+// follows the merge in the next decode step ran 166 us after this shape and
+// 172-175 us after one-row blocks of the same arithmetic, or after an empty
+// kernel of that grid -- the grid of the preceding kernel changes how the
+// next one's single-wave workgroups land on the SIMDs.)
+constexpr int kMergeRowsPerBlock = 2;
+constexpr int kMergeMaxLds = 4096;       // weights per row kept in LDS
 
-__global__ __launch_bounds__(128) void attn_reduce_kernel(const float *__restrict__ ws, float *__restrict__ o,
-                                                          int n_split, int D, int HG, int64_t o_bstride) {
-    __shared__ float w_lds[kMergeMaxLds];
-    __shared__ float red[4];
-    const int row = blockIdx.x;                 // b * HG + hq
-    const int b = row / HG, hq = row - b * HG;
-    const int tid = threadIdx.x, nt = blockDim.x;
+__global__ __launch_bounds__(256) void attn_reduce_kernel(const float *__restrict__ ws, float *__restrict__ o,
+                                                          int n_split, int D, int HG, int64_t o_bstride,
+                                                          int64_t rows) {
+    __shared__ float w_all[kMergeRowsPerBlock][kMergeMaxLds];
+    __shared__ float red_all[kMergeRowsPerBlock][4];
+    const int half = threadIdx.x / D;              // row of this block
+    const int tid = threadIdx.x - half * D, nt = D;
+    const int64_t row = (int64_t)blockIdx.x * kMergeRowsPerBlock + half;   // b * HG + hq
+    const bool live = row < rows;
+    const int64_t b = row / HG, hq = row - b * HG;
     const int PSTR = D + 4;
-    const float *p = ws + (int64_t)row * n_split * PSTR;
+    const float *p = ws + row * n_split * PSTR;
+    float *w_lds = w_all[half];
+    float *red = red_all[half];
+    const int wv = tid >> 6;                       // wave within the row
 
     float M = neg_inf();
-    for (int s = tid; s < n_split; s += nt) M = fmaxf(M, p[(int64_t)s * PSTR + D]);
+    if (live)
+        for (int s = tid; s < n_split; s += nt) M = fmaxf(M, p[(int64_t)s * PSTR + D]);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, shfl_xor(M, off));
-    if ((tid & 63) == 0) red[tid >> 6] = M;
+    if ((tid & 63) == 0) red[wv] = M;
     __syncthreads();
     M = red[0];
     for (int w = 1; w < (nt + 63) / 64; ++w) M = fmaxf(M, red[w]);
@@ -720,20 +734,22 @@ __global__ __launch_bounds__(128) void attn_reduce_kernel(const float *__restric
 
     const bool use_lds = n_split <= kMergeMaxLds;
     float L = 0.f;
-    for (int s = tid; s < n_split; s += nt) {
-        const float m = p[(int64_t)s * PSTR + D];
-        const float f = (m == neg_inf()) ? 0.f : fast_exp2(m - M);
-        if (use_lds) w_lds[s] = f;
-        L = fmaf(f, p[(int64_t)s * PSTR + D + 1], L);
-    }
+    if (live)
+        for (int s = tid; s < n_split; s += nt) {
+            const float m = p[(int64_t)s * PSTR + D];
+            const float f = (m == neg_inf()) ? 0.f : fast_exp2(m - M);
+            if (use_lds) w_lds[s] = f;
+            L = fmaf(f, p[(int64_t)s * PSTR + D + 1], L);
+        }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) L += shfl_xor(L, off);
-    if ((tid & 63) == 0) red[tid >> 6] = L;
+    if ((tid & 63) == 0) red[wv] = L;
     __syncthreads();
     L = red[0];
     for (int w = 1; w < (nt + 63) / 64; ++w) L += red[w];
 
     __syncthreads();   // w_lds complete
+    if (!live) return;
     for (int d = tid; d < D; d += nt) {
         float O0 = 0.f, O1 = 0.f, O2 = 0.f, O3 = 0.f;
         int s = 0;
@@ -759,7 +775,7 @@ __global__ __launch_bounds__(128) void attn_reduce_kernel(const float *__restric
                 O0 = fmaf(f, p[(int64_t)s * PSTR + d], O0);
             }
         }
-        o[(int64_t)b * o_bstride + (int64_t)hq * D + d] = L > 0.f ? ((O0 + O1) + (O2 + O3)) / L : 0.f;
+        o[b * o_bstride + hq * D + d] = L > 0.f ? ((O0 + O1) + (O2 + O3)) / L : 0.f;
     }
 }
 
@@ -973,8 +989,9 @@ hipError_t launch_merge(int64_t rows, int32_t heads_per_row, int32_t n_split, in
                            D, heads_per_row, o_bstride, total);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(attn_reduce_kernel, dim3((unsigned)rows), dim3(D), 0, stream, ws, o, n_split, D,
-                       heads_per_row, o_bstride);
+    const int64_t blocks = (rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock;
+    hipLaunchKernelGGL(attn_reduce_kernel, dim3((unsigned)blocks), dim3(kMergeRowsPerBlock * D), 0, stream, ws, o,
+                       n_split, D, heads_per_row, o_bstride, rows);
     return hipGetLastError();
 }
 
