@@ -521,9 +521,42 @@ def bench_kv4(args, torch, np, da, synth):
            "tokens_per_s": B / (ms * 1e-3), "quantize_k_ms": ms_quant, "eager_ms_per_step": ms_eager,
            "traffic": measured_traffic("attn_split_uint4_flexgen", code_bytes + ms_bytes + B * H * D * 2)}
     log(f"kv4: {ms * 1e3:.1f} us/step ({gbs:.0f} GB/s)")
+    del copies
+    if not args.no_sweep:
+        res["grouped_query_sweep"] = kv4_gqa_sweep(args, torch, np, da, synth)
     if host is not None:
         res["cpu_baseline"] = cpu_kv4(host, step_bytes / B)
     return res
+
+
+def kv4_gqa_sweep(args, torch, np, da, synth):
+    """uint4 cache under grouped query heads: B8, 8 KV heads, 32768 tokens,
+    G = 1, 2, 4, 8 query heads per KV head (fp16 q); the same cache bytes
+    each time (codes 268 MB + min/scale 33.6 MB)."""
+    rows = []
+    B, Hkv, N, D = 8, 8, 32768, 128
+    c = synth.dense_case([44, 0], B, Hkv, Hkv, D, N, "f16", "f16")
+    k = up(c.k, "f16", torch, np)
+    v = up(c.v, "f16", torch, np)
+    del c
+    copies = [da.da_quantize_kv4(k) + da.da_quantize_kv4(v) for _ in range(2)]
+    del k, v
+    ws = torch.zeros(1 << 26, dtype=torch.uint8, device="cuda")
+    cache_bytes = 2 * B * Hkv * N * D // 2 + 2 * 2 * B * Hkv * N * (D // 64) * 2
+    for G in (1, 2, 4, 8):
+        q = up(synth.dense_case([44, G], B, G * Hkv, Hkv, D, 1, "f16", "f16").q, "f16", torch, np)
+        out = torch.empty((B, G * Hkv, D), dtype=torch.float32, device="cuda")
+
+        def step(i):
+            da.da_decode_attention_kv4(q, *copies[i & 1], out=out, ws=ws)
+
+        ms = time_graph(torch, step, args.steps, args.warmup)
+        nbytes = cache_bytes + B * G * Hkv * D * (2 + 4)
+        rows.append({"G": G, "n_q_heads": G * Hkv, "ms_per_step": ms, "step_bytes": nbytes,
+                     "gbs": nbytes / (ms * 1e-3) / 1e9, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+    log("kv4 grouped-query sweep (B8 Hkv8 N32768): " + ", ".join(
+        f"G{r['G']} {r['ms_per_step'] * 1e3:.1f}us {r['gbs'] / 1e3:.2f}TB/s" for r in rows))
+    return rows
 
 
 def cpu_kv4(host, bytes_per_row):

@@ -68,7 +68,10 @@ struct Cfg {
                              : (QF == KF || (U4 && QF == FMT_F16)) ? 1
                              : (KF == FMT_BF16 ? (G <= 4 ? 3 : 2) : 2);
     static constexpr int RPH0 = SPL * NGRP;            // A rows used per head
-    static constexpr int RPH = RPH0 <= 1 ? 1 : (RPH0 <= 2 ? 2 : 4);
+    // uint4 with 2 or 4 query heads: four rows per head (two of them zero),
+    // so each lane group scores one head and the per-head work after the
+    // scores (softmax, P.V weights) spreads over the lane groups
+    static constexpr int RPH = RPH0 <= 1 ? 1 : (RPH0 <= 2 ? ((U4 && G > 1 && G <= 4) ? 4 : 2) : 4);
     static constexpr int HPL = 4 / RPH;                 // heads per 16-lane group
     static constexpr int NCH = R / 64;                  // 16-byte K chunks per lane per sub-tile
     static constexpr int NMF = KF == FMT_F32 ? 4 * NCH : (U4 ? 4 * NCH : NCH);
@@ -111,6 +114,57 @@ __device__ __forceinline__ u32x4 u4_to_f16x8(uint32_t x) {
     r[2] = lshl_or<6>(y & kLo, one);     // nibbles 2, 6
     r[3] = lshl_or<2>(y & kHi, one);     // nibbles 3, 7
     return r;
+}
+
+// (x shifted) & mask | one in two VALU instructions: the shift, then
+// v_and_or_b32 with the exponent bits in a scalar register
+__device__ __forceinline__ uint32_t and_or(uint32_t m, uint32_t mask, uint32_t one) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(mask), "s"(one));
+    return r;
+}
+
+// One dword of 8 codes -> 8 bf16 values 1 + c/16 (exact; bf16 keeps 7
+// mantissa bits) as the pairs (nibble k, nibble k + 4), k = 0..3: output k
+// puts nibbles k and k + 4 at mantissa bits 3..6 of its two halves.
+__device__ __forceinline__ u32x4 u4_to_bf16x8(uint32_t x) {
+    const uint32_t one = __builtin_amdgcn_readfirstlane(0x3F803F80u);
+    const uint32_t mask = 0x00780078u;        // mantissa bits 3..6 of both halves
+    u32x4 r;
+    r[0] = and_or(x << 3, mask, one);
+    r[1] = and_or(x >> 1, mask, one);
+    r[2] = and_or(x >> 5, mask, one);
+    r[3] = and_or(x >> 9, mask, one);
+    return r;
+}
+
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+#define DA_LDS __attribute__((address_space(3)))
+
+// gfx950 LDS transpose read of 4-bit elements: within each group of 16
+// lanes, every lane reads 8 bytes (16 nibbles) at its own address, and lane d
+// receives nibble d of lane s's 8 bytes in nibble slot s (bits 4s .. 4s + 3
+// of the 64-bit result), s = 0..15 (lane layout measured on MI355X).
+__device__ __forceinline__ v2i32 lds_read_tr4(const uint32_t *lds, int byte_off) {
+    return __builtin_amdgcn_ds_read_tr4_b64_v2i32((DA_LDS v2i32 *)((DA_LDS char *)lds + byte_off));
+}
+
+// gfx950 LDS transpose read of 16-bit elements: within each group of 16
+// lanes, every lane reads 4 elements at its own address, and lane d receives
+// element d mod 4 of lane 4 j + d / 4 in slot j, j = 0..3 (measured on
+// MI355X).
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *lds, int half_off) {
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS v4i16 *)((DA_LDS char *)lds + 2 * half_off));
+    return make_uint2((uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16),
+                      (uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16));
+}
+
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+// two floats rounded to bf16 (nearest, ties to even) in one instruction, low then high
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, bf16x2v));
 }
 
 // Registers of one pipeline stage: the K and V of TS sub-tiles of 16 tokens.
@@ -185,8 +239,16 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     constexpr bool SOLO = C::U4 && G == 1;
     static_assert(!SOLO || (kTS == 2 && kTile == 32), "one-head uint4 layout");
 
-    __shared__ float p_all[kMaxWavesPerBlock][G > 1 ? kTile * G : 1];            // p exchange
+    // uint4 with grouped query heads: P.V runs on the matrix cores (see
+    // pv_stage below); with one query head per KV head it stays on the VALU,
+    // where the one-head layout needs fewer registers (measured on MI355X)
+    constexpr bool PVM = C::U4 && G > 1;
+    __shared__ float p_all[kMaxWavesPerBlock][(G > 1 && !PVM) ? kTile * G : 1];   // p exchange
     __shared__ int32_t pg_all[kMaxWavesPerBlock][PAGED ? kMaxPagesPerSplit : 1];  // page lists
+    // uint4: a stage's V codes [32 tokens][64 B], and its P.V weights as bf16
+    // [V group][32 tokens][A row = 2 head + term]
+    __shared__ __attribute__((aligned(16))) uint32_t pvv_all[PVM ? kMaxWavesPerBlock : 1][PVM ? kTile * 16 : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t pvp_all[PVM ? kMaxWavesPerBlock : 1][PVM ? 2 * 16 * kTile : 1];
     extern __shared__ float mrg_lds[];                                            // merge slots
 
     const int lane = threadIdx.x & 63;
@@ -358,14 +420,110 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     float l_part[HPL];
 #pragma unroll
     for (int hh = 0; hh < HPL; ++hh) l_part[hh] = 0.f;
-    float acc[G][CPL];
+    float acc[PVM ? 1 : G][PVM ? 1 : CPL];
     float amin[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        amin[h] = 0.f;
+    for (int h = 0; h < G; ++h) amin[h] = 0.f;
+    if constexpr (!PVM) {
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[h][c] = 0.f;
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[h][c] = 0.f;
     }
+    // uint4: P.V accumulators, one 16x16 MFMA output per 16-channel block:
+    // lane (g4, n) holds rows 4 g4 + i = (head 2 g4 + i / 2, bf16 term i mod 2)
+    // of channel 16 nb + n; amg[hh][g]: sum of p * (V group minimum) of head
+    // g4 * HPL + hh over this lane's tokens (one-head layout: am below)
+    f32x4 acc2[PVM ? 8 : 1];
+#pragma unroll
+    for (int nb = 0; nb < (PVM ? 8 : 1); ++nb) acc2[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    float amg[HPL][2];
+#pragma unroll
+    for (int hh = 0; hh < HPL; ++hh) amg[hh][0] = amg[hh][1] = 0.f;
+    if constexpr (PVM) {
+        // rows of the weights that no head writes stay zero for the whole call
+        u32x4 *z = (u32x4 *)pvp_all[wave];
+        for (int i = lane; i < 2 * 16 * kTile / 8; i += 64) z[i] = (u32x4){0u, 0u, 0u, 0u};
+        wave_lds_sync();
+    }
+    // P.V of one stage on the matrix cores: O += P V over the stage's 32
+    // tokens, per 16-channel block nb (V group nb / 4), as
+    //   C += W (1 + c/16)  then  C += W (-1),
+    // W = p * (V group scale) as two bf16 terms (A rows 2 h, 2 h + 1), the
+    // codes as the exact bf16 values 1 + c/16 (B); the second product takes
+    // the offset back out right away, so the fp32 accumulator never carries
+    // it and C = sum W c / 16.  The codes reach the B layout (8 tokens of one
+    // channel per lane) through LDS: stored as loaded, read back transposed.
+    auto pv_stage = [&](St &st) {
+      if constexpr (PVM) {
+        uint32_t *vl = pvv_all[wave];
+#pragma unroll
+        for (int ts = 0; ts < kTS; ++ts)
+            *(u32x4 *)&vl[(ts * kSub + vtok) * 16 + 4 * (lane & 3)] = st.V[ts][0];
+        wave_lds_sync();
+        // A operands, rows = (head, term), in the B operand's token order:
+        // k-slots 0..7 of lane group g4 hold tokens 8 g4 + {0,4,1,5,2,6,3,7};
+        // source lane 4 j + r of a transposed read supplies token slot j, rows
+        // 4 r .. 4 r + 3
+        const uint16_t *pl = pvp_all[wave];
+        const int jr = n16 >> 2, rr = n16 & 3;
+        const int t_lo = 8 * g4 + (jr >> 1) + 4 * (jr & 1);       // slots 0..3: tokens 0, 4, 1, 5
+        const u32x4 mones = {0xBF80BF80u, 0xBF80BF80u, 0xBF80BF80u, 0xBF80BF80u};   // bf16 -1
+        // source lane (g4, s) of a code read: token 8 g4 + s mod 8, 16-channel
+        // chunk 2 j + s / 8 (blocks 2 j and 2 j + 1, V group j / 2)
+        const int tok = 8 * g4 + (n16 & 7);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const uint2 x0 = lds_read_tr16(pl, (g * kTile + t_lo) * 16 + 4 * rr);
+            const uint2 x1 = lds_read_tr16(pl, (g * kTile + t_lo + 2) * 16 + 4 * rr);   // 2, 6, 3, 7
+            const u32x4 Aw = {x0.x, x0.y, x1.x, x1.y};
+#pragma unroll
+            for (int j = 2 * g; j < 2 * g + 2; ++j) {
+                const v2i32 r = lds_read_tr4(vl, tok * 64 + 8 * (2 * j + (n16 >> 3)));
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const int nb = 2 * j + h2;
+                    const u32x4 bv = u4_to_bf16x8((uint32_t)r[h2]);
+                    acc2[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Aw),
+                                                                       __builtin_bit_cast(bf16x8, bv), acc2[nb], 0, 0, 0);
+                    acc2[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Aw),
+                                                                       __builtin_bit_cast(bf16x8, mones), acc2[nb], 0, 0,
+                                                                       0);
+                }
+            }
+        }
+        wave_lds_sync();    // the next stage rewrites both tiles
+      }
+    };
+    // W = p * scale of both V groups of one (head h, stage token t): two
+    // bf16 terms each (hi, lo = the rest) into rows 2 h and 2 h + 1 of the
+    // weights, one dword per group
+    auto pv_put2 = [&](int h, int t, float w0, float w1) {
+      if constexpr (PVM) {
+        const uint32_t hi = pack_bf16(w0, w1);
+        const uint32_t lo = pack_bf16(w0 - __uint_as_float(hi << 16), w1 - __uint_as_float(hi & 0xFFFF0000u));
+        *(uint32_t *)&pvp_all[wave][t * 16 + 2 * h] = __builtin_amdgcn_perm(lo, hi, 0x05040100u);
+        *(uint32_t *)&pvp_all[wave][(kTile + t) * 16 + 2 * h] = __builtin_amdgcn_perm(lo, hi, 0x07060302u);
+      }
+    };
+    // rescale the P.V accumulators of this lane's rows (heads 2 g4, 2 g4 + 1)
+    auto pv_rescale = [&](const float *alpha) {
+      if constexpr (PVM) {
+        float aA = 1.f, aB = 1.f;
+#pragma unroll
+        for (int h2 = 0; h2 < G; ++h2) {
+            if (h2 == 2 * g4) aA = alpha[h2];
+            if (h2 == 2 * g4 + 1) aB = alpha[h2];
+        }
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            acc2[nb][0] *= aA;
+            acc2[nb][1] *= aA;
+            acc2[nb][2] *= aB;
+            acc2[nb][3] *= aB;
+        }
+      }
+    };
 
     const float sl2 = a.scale_log2;
 
@@ -445,11 +603,13 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
             m_run[h] = mn;
         }
         if (changed) {
+            if constexpr (PVM) {
+                pv_rescale(alpha);
+            } else {
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                amin[h] *= alpha[h];
+                for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) acc[h][c] *= alpha[h];
+                    for (int c = 0; c < CPL; ++c) acc[h][c] *= alpha[h];
             }
 #pragma unroll
             for (int hh = 0; hh < HPL; ++hh) {
@@ -458,11 +618,26 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
 #pragma unroll
                 for (int h2 = 0; h2 < G; ++h2) if (h2 == h) al = alpha[h2];
                 l_part[hh] *= al;
+                if constexpr (PVM) {
+                    amg[hh][0] *= al;
+                    amg[hh][1] *= al;
+                }
             }
         }
         // G == 1: head 0's p of token (ts, n16) stays in lane n16 and the P.V
-        // lanes fetch it with a lane shuffle; otherwise p goes through LDS
+        // lanes fetch it with a lane shuffle; otherwise p goes through LDS.
+        // uint4: each lane turns its p into the P.V weights of both V groups
+        // (the token's V scale and minimum fetched from the lane that loaded
+        // them)
         float p0[kTS];
+        uint32_t sv2[kTS], mv2[kTS];
+        if constexpr (PVM) {
+#pragma unroll
+            for (int ts = 0; ts < kTS; ++ts) {
+                sv2[ts] = __shfl(st.sv, ts * kSub + n16, 64);
+                mv2[ts] = __shfl(st.mv, ts * kSub + n16, 64);
+            }
+        }
 #pragma unroll
         for (int hh = 0; hh < HPL; ++hh) {
             const int h = g4 * HPL + hh;
@@ -473,16 +648,28 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
             for (int ts = 0; ts < kTS; ++ts) {
                 const float p = (sc[ts][hh] == neg_inf()) ? 0.f : fast_exp2(sc[ts][hh] - mh);
                 l_part[hh] += p;
-                if constexpr (G == 1) {
+                if constexpr (PVM) {
+                    if (h < G) {
+                        pv_put2(h, ts * kSub + n16, p * f16_to_f32(sv2[ts] & 0xFFFFu), p * f16_to_f32(sv2[ts] >> 16));
+#pragma unroll
+                        for (int g = 0; g < 2; ++g)
+                            amg[hh][g] = fmaf(p, f16_to_f32((mv2[ts] >> (16 * g)) & 0xFFFFu), amg[hh][g]);
+                    }
+                } else if constexpr (G == 1) {
                     if (hh == 0) p0[ts] = p;
                 } else {
                     if (h < G) p_lds[(ts * kSub + n16) * G + h] = p;
                 }
             }
         }
+        if constexpr (PVM) {
+            pv_stage(st);
+            return;
+        }
         if constexpr (G > 1) wave_lds_sync();
 
         // P.V on the VALU
+        if constexpr (!PVM) {
 #pragma unroll
         for (int ts = 0; ts < kTS; ++ts) {
 #pragma unroll
@@ -502,35 +689,6 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
                         const float xv = __uint_as_float(x[e]);
 #pragma unroll
                         for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pv[h], xv, acc[h][e]);
-                    }
-                } else if constexpr (C::U4) {
-                    // even channels: low nibbles -> c; odd channels: high
-                    // nibbles left in place -> 16 c, so their weight is w / 16
-                    // this lane's V token (ts, vtok), group vcol / 32
-                    const int gsh = 16 * (vcol / 32);
-                    const float vmn1 = f16_to_f32((__shfl(st.mv, ts * kSub + vtok, 64) >> gsh) & 0xFFFFu);
-                    const float vsc1 = f16_to_f32((__shfl(st.sv, ts * kSub + vtok, 64) >> gsh) & 0xFFFFu);
-                    float wv[G], wv16[G];
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        wv[h] = pv[h] * vsc1;
-                        wv16[h] = wv[h] * 0.0625f;
-                        amin[h] = fmaf(pv[h], vmn1, amin[h]);
-                    }
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const uint32_t lo = opaque(x[u] & 0x0F0F0F0Fu);
-                        const uint32_t hi = opaque(x[u] & 0xF0F0F0F0u);
-#pragma unroll
-                        for (int bb = 0; bb < 4; ++bb) {
-                            const float c0 = ubyte_f32(lo, bb);
-                            const float c1 = ubyte_f32(hi, bb);
-#pragma unroll
-                            for (int h = 0; h < G; ++h) {
-                                acc[h][8 * u + 2 * bb] = fmaf(wv[h], c0, acc[h][8 * u + 2 * bb]);
-                                acc[h][8 * u + 2 * bb + 1] = fmaf(wv16[h], c1, acc[h][8 * u + 2 * bb + 1]);
-                            }
-                        }
                     }
                 } else {
 #pragma unroll
@@ -553,6 +711,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
             }
         }
         if constexpr (G > 1) wave_lds_sync();
+        }
     };
 
     // ---- uint4, one query head: each lane scores stage token lane mod 32 ----
@@ -642,19 +801,42 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         for (int o = 1; o < (SOLO ? 32 : 16); o <<= 1) x += shfl_xor(x, o);
         l_part[hh] = x;
     }
+    // uint4: the minimum term of each (head, V group), for the lanes whose
+    // P.V rows hold that head: amr[a][g] for head 2 g4 + a
+    float amr[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
     if constexpr (SOLO) {
-        // per V group: lanes 0..31 sum group 0, lanes 32..63 group 1
+        // per V group: lanes 0..31 sum group 0, lanes 32..63 group 1; the V
+        // lanes of channel group vcol / 32 add it to their channels
 #pragma unroll
         for (int o = 1; o < 32; o <<= 1) am += shfl_xor(am, o);
         amin[0] = __shfl(am, 32 * (vcol / 32), 64);
+    } else if constexpr (PVM) {
+#pragma unroll
+        for (int hh = 0; hh < HPL; ++hh)
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                float x = amg[hh][g];
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) x += shfl_xor(x, o);
+                amg[hh][g] = x;
+            }
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const float x = readlane_f(amg[h % HPL][g], 16 * (h / HPL));
+                if (h == 2 * g4) amr[0][g] = x;
+                if (h == 2 * g4 + 1) amr[1][g] = x;
+            }
     }
+    if constexpr (!PVM) {
 #pragma unroll
-    for (int mask = C::CH_LANES; mask < 64; mask <<= 1) {
+        for (int mask = C::CH_LANES; mask < 64; mask <<= 1) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            if constexpr (C::U4 && !SOLO) amin[h] += shfl_xor(amin[h], mask);
+            for (int h = 0; h < G; ++h) {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) acc[h][c] += shfl_xor(acc[h][c], mask);
+                for (int c = 0; c < CPL; ++c) acc[h][c] += shfl_xor(acc[h][c], mask);
+            }
         }
     }
     // to the workspace, or to this wave's LDS slot [G][PSTR] for the merge
@@ -672,7 +854,19 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
                 if (h < G) dst0[h * hstride + D + 1] = l_part[hh];
             }
         }
-        if (lane < C::CH_LANES) {
+        if constexpr (PVM) {
+            // u = min term + sum W c = am + 16 (C_hi + C_lo), channel 16 nb + n16
+#pragma unroll
+            for (int a2 = 0; a2 < 2; ++a2) {
+                const int h = 2 * g4 + a2;
+                if (h < G) {
+#pragma unroll
+                    for (int nb = 0; nb < 8; ++nb)
+                        dst0[h * hstride + 16 * nb + n16] =
+                            fmaf(16.f, acc2[nb][2 * a2] + acc2[nb][2 * a2 + 1], amr[a2][nb >> 2]);
+                }
+            }
+        } else if (lane < C::CH_LANES) {
             const int c0 = KF == FMT_F32 ? vcol / 4 : (C::U4 ? vcol * 2 : vcol / 2);
 #pragma unroll
             for (int h = 0; h < G; ++h) {

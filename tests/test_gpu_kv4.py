@@ -106,6 +106,12 @@ KV4_CASES = [
     (3, 5, 5, 333, "f16", 512),       # one ragged split per head, written without a merge
     (2, 3, 3, 45, "f32", 1024),       # one split shorter than a stage
     (1, 2, 2, 1, "f16", 0),           # a single token: o = its dequantized value row
+    # grouped query heads (P.V on the matrix cores)
+    (2, 16, 2, 700, "f16", 0),        # G = 8, several splits and the merge kernel
+    (3, 12, 3, 333, "f32", 512),      # G = 4, fp32 q, one ragged split per head
+    (1, 8, 2, 45, "f16", 0),          # G = 4, fewer tokens than a stage
+    (2, 4, 2, 1, "f16", 0),           # G = 2, a single token
+    (2, 8, 4, 600, "f32", 64),        # G = 2, fp32 q, 10 splits
 ]
 
 
@@ -134,6 +140,47 @@ def test_kv4_integer_data_equals_dense(da):
     o, _, _ = run_kv4(da, c)
     ref = decode_attention(as_f64(q, "f16"), k.astype(np.float64), v.astype(np.float64), 0.05)
     assert_close(o, ref, atol=1e-5, rel_rms=1e-5, what="kv4 integer data")
+
+
+@pytest.mark.parametrize("G", [2, 4, 8])
+def test_kv4_integer_data_grouped_query_heads(da, G):
+    """Integer data under grouped query heads, where P.V runs on the matrix
+    cores: each weight p * scale enters as two bf16 terms (hi, and the rest
+    rounded again), so it carries a relative error of at most 2^-9 * 2^-9 =
+    2^-18; with values of magnitude <= 8 the output may differ from the exact
+    result by at most 2^-18 * 8 = 3.1e-5 (plus fp32 accumulation, ~1e-6).
+    Bar: 4e-5 absolute.  (One query head per KV head keeps fp32 weights on
+    the VALU and holds 1e-5: test_kv4_integer_data_equals_dense.)"""
+    rng = np.random.default_rng(23 + G)
+    B, Hkv, N, D = 2, 2, 700, 128
+    k = rng.integers(0, 16, size=(B, Hkv, N, D)).astype(np.float16)
+    v = rng.integers(-7, 9, size=(B, Hkv, N, D)).astype(np.float16)
+    k[..., 0::64] = 0
+    k[..., 1::64] = 15
+    v[..., 0::64] = -7
+    v[..., 1::64] = 8
+    q = rng.standard_normal((B, G * Hkv, D)).astype(np.float16)
+    c = synth.DenseCase(q=q, k=k, v=v, q_dtype="f16", kv_dtype="f16", scale=0.05)
+    o, _, _ = run_kv4(da, c)
+    ref = decode_attention(as_f64(q, "f16"), k.astype(np.float64), v.astype(np.float64), 0.05)
+    assert_close(o, ref, atol=4e-5, what=f"kv4 integer data G{G}")
+
+
+@pytest.mark.parametrize("G,qd", [(2, "f16"), (4, "f16"), (8, "f16"), (4, "f32")])
+def test_kv4_grouped_query_heads_long_context(da, G, qd):
+    """Grouped query heads over a long uint4 cache (B2, 8 KV heads, 32768
+    tokens: 32 splits of 1024 and the merge kernel, the launch of the
+    grouped-query sweep in bench.py), every row against the oracle and the
+    unrounded fold."""
+    c = synth.dense_case([303, G, 0 if qd == "f16" else 1], 2, 8 * G, 8, 128, 32768, qd, "f16")
+    o, kq, vq = run_kv4(da, c)
+    q64 = as_f64(c.q, qd)
+    for b in range(2):
+        sel = lambda t: [x[b:b + 1] for x in t]
+        ref = kv4_attention(q64[b:b + 1], *sel(kq), *sel(vq), c.scale)
+        assert_close(o[b:b + 1], ref, atol=1e-3, rel_rms=3e-3, what=f"kv4 G{G} {qd} row {b}")
+        fold = decode_attention(q64[b:b + 1], unrounded(*sel(kq)), unrounded(*sel(vq)), c.scale)
+        assert_close(o[b:b + 1], fold, atol=1e-5, rel_rms=1e-4, what="  vs unrounded dequant")
 
 
 def test_workload4_full_size_every_row(da):
