@@ -3,6 +3,9 @@ into calibrated HBM bytes per launch, keyed by kernel, for bench.py.
 
     python pmc_traffic.py FETCH_DB WRITE_DB OUT_JSON
 
+(FETCH_DB / WRITE_DB: rocprofv3 result databases, or the
+pmc_counter_collection.csv files of --output-format csv runs.)
+
 Both runs must include the 512 MiB device-to-device copies that
 `bench.py --copy-calibration` performs first (`__amd_rocclr_copyBuffer`):
 each counter is scaled by (true bytes of that copy) / (what the counter read
@@ -11,6 +14,7 @@ figures can be recognised.
 """
 from __future__ import annotations
 
+import csv
 import hashlib
 import json
 import os
@@ -44,9 +48,16 @@ def source_hash() -> str:
 
 
 def _per_kernel(db: str, counter: str) -> dict:
-    con = sqlite3.connect(db)
-    rows = con.execute("select name, counter_value from pmc_events where counter_name = ?",
-                       (counter,)).fetchall()
+    """Counter values per kernel name, from a rocprofv3 result database or
+    from its CSV output (pmc_counter_collection.csv, one row per dispatch)."""
+    if db.endswith(".csv"):
+        with open(db, newline="") as fh:
+            rows = [(r["Kernel_Name"], r["Counter_Value"]) for r in csv.DictReader(fh)
+                    if r["Counter_Name"] == counter]
+    else:
+        con = sqlite3.connect(db)
+        rows = con.execute("select name, counter_value from pmc_events where counter_name = ?",
+                           (counter,)).fetchall()
     out: dict = {}
     for name, v in rows:
         out.setdefault(name, []).append(float(v))
