@@ -40,8 +40,8 @@ KERNELS = {                    # short name -> substring of the mangled kernel n
 def source_hash() -> str:
     h = hashlib.sha256()
     # the sources of the kernels in KERNELS (and what they include)
-    for rel in ("csrc/kernels/attn.hip", "csrc/kernels/page.hip", "csrc/kernels/kv4.hip", "csrc/kernels/common.h",
-                "csrc/internal.h"):
+    for rel in ("csrc/kernels/attn.hip", "csrc/kernels/attn_split.h", "csrc/kernels/attn_u4.hip",
+                "csrc/kernels/page.hip", "csrc/kernels/kv4.hip", "csrc/kernels/common.h", "csrc/internal.h"):
         with open(os.path.join(PKG, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()

@@ -24,6 +24,7 @@ SOURCES = [
     "csrc/api.cpp",
     "csrc/stream.cpp",
     "csrc/kernels/attn.hip",
+    "csrc/kernels/attn_u4.hip",
     "csrc/kernels/page.hip",
     "csrc/kernels/kv4.hip",
     "csrc/kernels/prefill.hip",
@@ -51,10 +52,17 @@ def common_flags() -> list[str]:
     ]
 
 
+# Per-source compiler options on top of common_flags().
+EXTRA_FLAGS = {
+    # uint4 partial pass: MFMA accumulators in VGPRs (no AGPR copies per stage)
+    "csrc/kernels/attn_u4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str, verbose: bool, out_dir: str = BUILD) -> str:
     path = os.path.join(PKG, src)
     obj = os.path.join(out_dir, src.replace("/", "_") + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", path, "-o", obj]
+    cmd = [hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), "-c", path, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
