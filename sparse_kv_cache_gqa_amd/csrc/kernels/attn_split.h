@@ -245,8 +245,9 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     static_assert(!SOLO || (kTS == 2 && kTile == 32), "one-head uint4 layout");
 
     // uint4 with grouped query heads: P.V runs on the matrix cores (see
-    // pv_stage below); with one query head per KV head it stays on the VALU,
-    // where the one-head layout needs fewer registers (measured on MI355X)
+    // pv_store and pv_mma below); with one query head per KV head it stays on
+    // the VALU, where the one-head layout needs fewer registers (measured on
+    // MI355X)
     constexpr bool PVM = C::U4 && G > 1;
     __shared__ float p_all[kMaxWavesPerBlock][(G > 1 && !PVM) ? kTile * G : 1];   // p exchange
     __shared__ int32_t pg_all[kMaxWavesPerBlock][PAGED ? kMaxPagesPerSplit : 1];  // page lists
@@ -459,13 +460,22 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     // the offset back out right away, so the fp32 accumulator never carries
     // it and C = sum W c / 16.  The codes reach the B layout (8 tokens of one
     // channel per lane) through LDS: stored as loaded, read back transposed.
-    auto pv_stage = [&](St &st) {
+    // The products of a stage run one stage late, after the next stage's
+    // scores (pv_store at the end of a stage, pv_mma in the next): the LDS
+    // round trip of the weights and codes then overlaps independent work.
+    bool pv_pend = false;    // a stage's weights and codes wait in LDS for their products
+    auto pv_store = [&](St &st) {
       if constexpr (PVM) {
         uint32_t *vl = pvv_all[wave];
 #pragma unroll
         for (int ts = 0; ts < kTS; ++ts)
             *(u32x4 *)&vl[(ts * kSub + vtok) * 16 + 4 * (lane & 3)] = st.V[ts][0];
-        wave_lds_sync();
+      }
+    };
+    auto pv_mma = [&]() {
+      if constexpr (PVM) {
+        const uint32_t *vl = pvv_all[wave];
+        wave_lds_sync();    // this wave's weights and codes of the stage are written
         // A operands, rows = (head, term), in the B operand's token order:
         // k-slots 0..7 of lane group g4 hold tokens 8 g4 + {0,4,1,5,2,6,3,7};
         // source lane 4 j + r of a transposed read supplies token slot j, rows
@@ -497,7 +507,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
                 }
             }
         }
-        wave_lds_sync();    // the next stage rewrites both tiles
+        wave_lds_sync();    // read before the next stage rewrites both tiles
       }
     };
     // W = p * scale of both V groups of one (head h, stage token t): two
@@ -584,6 +594,11 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
             }
         }
 
+        // the previous stage's products, before its accumulators are rescaled below
+        if constexpr (PVM) {
+            if (pv_pend) pv_mma();
+        }
+
         // online softmax (base 2): per-head tile max over the 16 lanes of a group
         float mt[HPL];
 #pragma unroll
@@ -668,7 +683,8 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
             }
         }
         if constexpr (PVM) {
-            pv_stage(st);
+            pv_store(st);
+            pv_pend = true;
             return;
         }
         if constexpr (G > 1) wave_lds_sync();
@@ -796,6 +812,10 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         if (!more) break;
         if (t0 + 2 * kTile < ntok) load_tile(sa, t0 + 2 * kTile);
         compute(sb);
+    }
+
+    if constexpr (PVM) {
+        if (pv_pend) pv_mma();     // the last stage's products
     }
 
     // ---- partial of this split ------------------------------------------------
