@@ -33,6 +33,7 @@ KERNELS = {                    # short name -> substring of the mangled kernel n
     "topk_attention_flexgen": "select_kernel<1, 1, 128, 2>",
     "select_tokens_flexgen": "select_kernel<1, 1, 128, 1>",
     "attn_reduce": "attn_reduce_kernel",
+    "attn_reduce_mid": "attn_reduce_mid_kernel",
     "attn_reduce_small": "attn_reduce_small_kernel",
 }
 
