@@ -369,6 +369,44 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         }
     };
 
+    // The two halves of load_tile (fp32 / fp16 / bf16 caches): the keys of a
+    // tile, which the scores consume first, and its values.
+    auto load_k = [&](St &st, int t0) {
+#pragma unroll
+        for (int ts = 0; ts < kTS; ++ts) {
+            if constexpr (!PAGED) {
+                const int rk = t0 + ts * kSub + n16;
+                st.kok[ts] = rk < ntok;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c)
+                    st.K[ts][c] = buf_load16(krs, (uint32_t)rk * R + 16 * g4 + 64 * c);
+            } else {
+                bool ok;
+                const int64_t r = row_of(t0 + ts * kSub + n16, ok);
+                st.kok[ts] = ok;
+                const char *p = kbase + r * R + 16 * g4;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c)
+                    st.K[ts][c] = ok ? ld_stream(p + 64 * c) : (u32x4){0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto load_v = [&](St &st, int t0) {
+#pragma unroll
+        for (int ts = 0; ts < kTS; ++ts) {
+#pragma unroll
+            for (int p2 = 0; p2 < VP; ++p2) {
+                if constexpr (!PAGED) {
+                    st.V[ts][p2] = buf_load16(vrs, (uint32_t)(t0 + ts * kSub + p2 * TPP + vtok) * R + vcol);
+                } else {
+                    bool okv;
+                    const int64_t rv = row_of(t0 + ts * kSub + p2 * TPP + vtok, okv);
+                    st.V[ts][p2] = okv ? ld_stream(vbase + rv * R + vcol) : (u32x4){0u, 0u, 0u, 0u};
+                }
+            }
+        }
+    };
+
     // issue the first tile before the q set-up below, so its latency overlaps
     St sa, sb;
     if (ntok > 0) load_tile(sa, 0);
@@ -543,7 +581,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     const float sl2 = a.scale_log2;
 
     // ---- scores, online softmax and P.V of one loaded tile ---------------------
-    auto compute_tile = [&](St &st) {
+    auto compute_tile = [&](St &st, auto &&after_scores) {
         float sc[kTS][HPL];
 
 #pragma unroll
@@ -593,6 +631,9 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
                 sc[ts][hh] = (h < G && st.kok[ts]) ? raw * sl2 : neg_inf();
             }
         }
+
+        // the scores are done with st.K (and st.kok)
+        after_scores();
 
         // the previous stage's products, before its accumulators are rescaled below
         if constexpr (PVM) {
@@ -801,17 +842,40 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     };
     auto compute = [&](St &st) {
         if constexpr (SOLO) compute_tile_solo(st);
-        else compute_tile(st);
+        else compute_tile(st, [] {});
     };
 
     // ---- main loop: two register stages -------------------------------------
-    for (int t0 = 0; t0 < ntok; t0 += 2 * kTile) {
-        const bool more = t0 + kTile < ntok;
-        if (more) load_tile(sb, t0 + kTile);
-        compute(sa);
-        if (!more) break;
-        if (t0 + 2 * kTile < ntok) load_tile(sa, t0 + 2 * kTile);
-        compute(sb);
+    // Early refill (below) on dense fp16 / bf16 caches with up to 4 query
+    // heads per KV head; elsewhere it raised the register count past the
+    // file (spills, AGPR copies) or measured no faster (paged gather).
+    constexpr bool EARLYK = !C::U4 && !PAGED && KF != FMT_F32 && G <= 4;
+    if constexpr (!EARLYK) {
+        for (int t0 = 0; t0 < ntok; t0 += 2 * kTile) {
+            const bool more = t0 + kTile < ntok;
+            if (more) load_tile(sb, t0 + kTile);
+            compute(sa);
+            if (!more) break;
+            if (t0 + 2 * kTile < ntok) load_tile(sa, t0 + 2 * kTile);
+            compute(sb);
+        }
+    } else {
+        // a stage's registers are refilled with the tile two ahead as soon as
+        // they are free: its keys right after the scores, its values after
+        // the P.V, so more loads stay in flight while a stage computes
+        if (kTile < ntok) load_tile(sb, kTile);
+        for (int t0 = 0; t0 < ntok; t0 += 2 * kTile) {
+            const int n2 = t0 + 2 * kTile, n3 = t0 + 3 * kTile;
+            compute_tile(sa, [&] {
+                if (n2 < ntok) load_k(sa, n2);
+            });
+            if (n2 < ntok) load_v(sa, n2);
+            if (t0 + kTile >= ntok) break;
+            compute_tile(sb, [&] {
+                if (n3 < ntok) load_k(sb, n3);
+            });
+            if (n3 < ntok) load_v(sb, n3);
+        }
     }
 
     if constexpr (PVM) {
