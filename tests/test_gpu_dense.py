@@ -140,7 +140,7 @@ def test_partials_match_oracle(da, B, Hq, Hkv, D, N, qd, kd, st):
     assert_close(ws[..., :D], u, atol=2e-6 * np.abs(u).max(), what=f"partials u split {st}")
 
 
-@pytest.mark.parametrize("ns,D", [(1, 64), (3, 128), (16, 128), (7, 64), (20, 64), (100, 128)])
+@pytest.mark.parametrize("ns,D", [(1, 64), (3, 128), (16, 128), (7, 64), (20, 64), (32, 128), (33, 64), (100, 128)])
 def test_merge_matches_oracle(da, ns, D):
     """The cross-split merge on its own, on seeded partials with empty splits
     (m = -inf) and a wide spread of maxima."""
@@ -166,6 +166,26 @@ def test_merge_matches_oracle(da, ns, D):
     p64 = part.astype(np.float64)
     ref = merge_partials(p64[..., :D], p64[..., D] * np.log(2.0), p64[..., D + 1])
     assert_close(got.cpu().numpy(), ref, atol=2e-6 * np.abs(ref).max(), what=f"merge ns{ns} D{D}")
+
+
+@pytest.mark.parametrize("ns,D", [(4, 128), (32, 128), (32, 64)])
+def test_merge_kernels_agree_bitwise(da, ns, D):
+    """The merge kernels for up to 4, up to 32 and more splits do the same
+    arithmetic in the same order: merging ns splits, and the same splits
+    followed by one empty split (m = -inf, l = 0, u = 0; it crosses into the
+    next kernel), must give the same bits."""
+    import torch
+    rng = np.random.default_rng([108, ns, D])
+    rows = 29
+    part = np.zeros((rows, ns + 1, D + 4), dtype=np.float32)
+    part[:, :ns, :D] = rng.standard_normal((rows, ns, D))
+    part[:, :ns, D] = rng.uniform(-20.0, 20.0, (rows, ns))
+    part[:, :ns, D + 1] = rng.uniform(1.0, 50.0, (rows, ns))
+    part[:, ns, D] = -np.inf
+    a = da.da_merge_partials(torch.from_numpy(np.ascontiguousarray(part[:, :ns])).cuda())
+    b = da.da_merge_partials(torch.from_numpy(part).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,D,N,qd,kd", [
