@@ -847,8 +847,10 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
 
     // ---- main loop: two register stages -------------------------------------
     // Early refill (below) on dense fp16 / bf16 caches with up to 4 query
-    // heads per KV head; elsewhere it raised the register count past the
-    // file (spills, AGPR copies) or measured no faster (paged gather).
+    // heads per KV head (measured on MI355X: the Llama-3-8B step about 0.5%
+    // faster).  Elsewhere it needed more registers than the file holds
+    // (spills, AGPR copies), cost occupancy, or measured slower (the paged
+    // gather, uint4 with grouped query heads).
     constexpr bool EARLYK = !C::U4 && !PAGED && KF != FMT_F32 && G <= 4;
     if constexpr (!EARLYK) {
         for (int t0 = 0; t0 < ntok; t0 += 2 * kTile) {
