@@ -356,7 +356,13 @@ hipError_t launch_split(const AttnLaunch &a, hipStream_t stream) {
     if (!k) return hipErrorInvalidValue;
     if (a.wpb < 1 || a.wpb > kMaxWavesPerBlock || a.n_split < 1) return hipErrorInvalidValue;
     if (a.fused && a.n_split > a.wpb) return hipErrorInvalidValue;
-    const size_t lds = a.fused ? merge_lds_bytes(a.wpb, a.G, a.D) : 0;
+    // uint4 with grouped query heads (P.V on the matrix cores): each wave's
+    // LDS tiles follow the merge slots
+    constexpr int kU4Tile = Cfg<FMT_U4, FMT_F16, 128, 2>::TILE;
+    static_assert(Cfg<FMT_U4, FMT_F16, 128, 8>::TILE == kU4Tile && Cfg<FMT_U4, FMT_F32, 128, 4>::TILE == kU4Tile,
+                  "one stage size for every grouped-query uint4 instance");
+    const bool pvm = a.kv_fmt == FMT_U4 && a.G > 1;
+    const size_t lds = (a.fused ? merge_lds_bytes(a.wpb, a.G, a.D) : 0) + (pvm ? a.wpb * kPvmWaveBytes<kU4Tile> : 0);
     dim3 grid((a.n_split + a.wpb - 1) / a.wpb, a.B * a.Hkv);
     hipLaunchKernelGGL(k.fn, grid, dim3(64 * a.wpb), lds, stream, a);
     return hipGetLastError();

@@ -61,6 +61,10 @@ __host__ __device__ inline int pages_per_split(int split_tokens, int log2_page) 
 __host__ __device__ inline size_t merge_lds_bytes(int wpb, int G, int D) {
     return (size_t)wpb * G * (D + 4) * sizeof(float);
 }
+// Dynamic LDS per wave of uint4 P.V on the matrix cores (stage of TILE
+// tokens): the V codes (TILE x 64 B), then the bf16 weights (2 x 16 x TILE).
+template <int TILE> constexpr size_t kPvvBytes = (size_t)TILE * 64;
+template <int TILE> constexpr size_t kPvmWaveBytes = kPvvBytes<TILE> + (size_t)2 * 16 * TILE * 2;
 
 // Compile-time layout of one kernel instance.
 template <int KF, int QF, int D, int G>
@@ -84,9 +88,11 @@ struct Cfg {
     static constexpr int TPP = 1024 / R;                // token stride between V pieces
     static constexpr int CPL = KF == FMT_F32 ? 4 : (U4 ? 32 : 8);   // V channels per lane
     static constexpr int CH_LANES = R / 16;             // lanes covering one row (V side)
-    // sub-tiles per pipeline stage (measured on MI355X): 4 for 128-byte rows;
-    // 2 otherwise -- uint4 rows are VALU-heavy and deeper stages cost occupancy
-    static constexpr int TS = R == 128 ? 4 : 2;
+    // sub-tiles per pipeline stage (measured on MI355X): 4 for 128-byte rows
+    // and for uint4 with grouped query heads (half the per-stage fixed work);
+    // 2 otherwise -- the one-head uint4 layout assumes 32-token stages, and
+    // deeper stages cost the other layouts occupancy
+    static constexpr int TS = (R == 128 || (U4 && G > 1)) ? 4 : 2;
     static constexpr int TILE = kSub * TS;              // tokens per stage
     // 16 MFMA rows must hold every (head, group, split term); rows fit 64..1024 bytes
     static constexpr bool ok = RPH0 <= 4 && G * RPH <= 16 && R >= 64 && R <= 1024;
@@ -251,11 +257,12 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     constexpr bool PVM = C::U4 && G > 1;
     __shared__ float p_all[kMaxWavesPerBlock][(G > 1 && !PVM) ? kTile * G : 1];   // p exchange
     __shared__ int32_t pg_all[kMaxWavesPerBlock][PAGED ? kMaxPagesPerSplit : 1];  // page lists
-    // uint4: a stage's V codes [32 tokens][64 B], and its P.V weights as bf16
-    // [V group][32 tokens][A row = 2 head + term]
-    __shared__ __attribute__((aligned(16))) uint32_t pvv_all[PVM ? kMaxWavesPerBlock : 1][PVM ? kTile * 16 : 1];
-    __shared__ __attribute__((aligned(16))) uint16_t pvp_all[PVM ? kMaxWavesPerBlock : 1][PVM ? 2 * 16 * kTile : 1];
-    extern __shared__ float mrg_lds[];                                            // merge slots
+    // Dynamic LDS: the merge slots (fused launches), then, for uint4 with
+    // grouped query heads, per wave a stage's V codes [32 tokens][64 B] and
+    // its P.V weights as bf16 [V group][32 tokens][A row = 2 head + term].
+    // Sized per launch (pvm_lds_bytes), so single-wave workgroups hold only
+    // their own wave's tiles and more of them fit on a CU.
+    extern __shared__ float mrg_lds[];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -269,6 +276,14 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
 
     float *const p_lds = p_all[wave];
     int32_t *const pg_lds = pg_all[wave];
+    uint32_t *pvv = nullptr;
+    uint16_t *pvp = nullptr;
+    if constexpr (PVM) {
+        char *const dyn = (char *)mrg_lds + (a.fused ? merge_lds_bytes(a.wpb, G, D) : 0) +
+                          (size_t)wave * kPvmWaveBytes<kTile>;
+        pvv = (uint32_t *)dyn;
+        pvp = (uint16_t *)(dyn + kPvvBytes<kTile>);
+    }
 
     // ---- token range of this split (empty past the last split) ----------
     int64_t s0 = 0;
@@ -486,7 +501,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     for (int hh = 0; hh < HPL; ++hh) amg[hh][0] = amg[hh][1] = 0.f;
     if constexpr (PVM) {
         // rows of the weights that no head writes stay zero for the whole call
-        u32x4 *z = (u32x4 *)pvp_all[wave];
+        u32x4 *z = (u32x4 *)pvp;
         for (int i = lane; i < 2 * 16 * kTile / 8; i += 64) z[i] = (u32x4){0u, 0u, 0u, 0u};
         wave_lds_sync();
     }
@@ -504,7 +519,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     bool pv_pend = false;    // a stage's weights and codes wait in LDS for their products
     auto pv_store = [&](St &st) {
       if constexpr (PVM) {
-        uint32_t *vl = pvv_all[wave];
+        uint32_t *vl = pvv;
 #pragma unroll
         for (int ts = 0; ts < kTS; ++ts)
             *(u32x4 *)&vl[(ts * kSub + vtok) * 16 + 4 * (lane & 3)] = st.V[ts][0];
@@ -512,23 +527,25 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     };
     auto pv_mma = [&]() {
       if constexpr (PVM) {
-        const uint32_t *vl = pvv_all[wave];
+        const uint32_t *vl = pvv;
         wave_lds_sync();    // this wave's weights and codes of the stage are written
         // A operands, rows = (head, term), in the B operand's token order:
         // k-slots 0..7 of lane group g4 hold tokens 8 g4 + {0,4,1,5,2,6,3,7};
         // source lane 4 j + r of a transposed read supplies token slot j, rows
         // 4 r .. 4 r + 3
-        const uint16_t *pl = pvp_all[wave];
+        const uint16_t *pl = pvp;
         const int jr = n16 >> 2, rr = n16 & 3;
         const int t_lo = 8 * g4 + (jr >> 1) + 4 * (jr & 1);       // slots 0..3: tokens 0, 4, 1, 5
         const u32x4 mones = {0xBF80BF80u, 0xBF80BF80u, 0xBF80BF80u, 0xBF80BF80u};   // bf16 -1
         // source lane (g4, s) of a code read: token 8 g4 + s mod 8, 16-channel
         // chunk 2 j + s / 8 (blocks 2 j and 2 j + 1, V group j / 2)
-        const int tok = 8 * g4 + (n16 & 7);
+#pragma unroll
+        for (int hf = 0; hf < kTile / 32; ++hf) {      // 32-token halves of the stage
+        const int tok = 32 * hf + 8 * g4 + (n16 & 7);
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-            const uint2 x0 = lds_read_tr16(pl, (g * kTile + t_lo) * 16 + 4 * rr);
-            const uint2 x1 = lds_read_tr16(pl, (g * kTile + t_lo + 2) * 16 + 4 * rr);   // 2, 6, 3, 7
+            const uint2 x0 = lds_read_tr16(pl, (g * kTile + 32 * hf + t_lo) * 16 + 4 * rr);
+            const uint2 x1 = lds_read_tr16(pl, (g * kTile + 32 * hf + t_lo + 2) * 16 + 4 * rr);   // 2, 6, 3, 7
             const u32x4 Aw = {x0.x, x0.y, x1.x, x1.y};
 #pragma unroll
             for (int j = 2 * g; j < 2 * g + 2; ++j) {
@@ -545,6 +562,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
                 }
             }
         }
+        }
         wave_lds_sync();    // read before the next stage rewrites both tiles
       }
     };
@@ -555,8 +573,8 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
       if constexpr (PVM) {
         const uint32_t hi = pack_bf16(w0, w1);
         const uint32_t lo = pack_bf16(w0 - __uint_as_float(hi << 16), w1 - __uint_as_float(hi & 0xFFFF0000u));
-        *(uint32_t *)&pvp_all[wave][t * 16 + 2 * h] = __builtin_amdgcn_perm(lo, hi, 0x05040100u);
-        *(uint32_t *)&pvp_all[wave][(kTile + t) * 16 + 2 * h] = __builtin_amdgcn_perm(lo, hi, 0x07060302u);
+        *(uint32_t *)&pvp[t * 16 + 2 * h] = __builtin_amdgcn_perm(lo, hi, 0x05040100u);
+        *(uint32_t *)&pvp[(kTile + t) * 16 + 2 * h] = __builtin_amdgcn_perm(lo, hi, 0x07060302u);
       }
     };
     // rescale the P.V accumulators of this lane's rows (heads 2 g4, 2 g4 + 1)
