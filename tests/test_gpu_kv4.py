@@ -112,6 +112,8 @@ KV4_CASES = [
     (1, 8, 2, 45, "f16", 0),          # G = 4, fewer tokens than a stage
     (2, 4, 2, 1, "f16", 0),           # G = 2, a single token
     (2, 8, 4, 600, "f32", 64),        # G = 2, fp32 q, 10 splits
+    (2, 8, 2, 500, "f16", 96),        # G = 4, splits of one and a half 64-token stages
+    (1, 16, 2, 250, "f16", 32),       # G = 8, splits of half a stage
 ]
 
 
