@@ -114,6 +114,8 @@ KV4_CASES = [
     (2, 8, 4, 600, "f32", 64),        # G = 2, fp32 q, 10 splits
     (2, 8, 2, 500, "f16", 96),        # G = 4, splits of one and a half 64-token stages
     (1, 16, 2, 250, "f16", 32),       # G = 8, splits of half a stage
+    (32, 32, 8, 1000, "f16", 0),      # G = 4, 256 units x 4 splits merged in the workgroup
+    (32, 64, 8, 900, "f16", 0),       # G = 8, merged in the workgroup
 ]
 
 
