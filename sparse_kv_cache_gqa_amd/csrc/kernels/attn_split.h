@@ -30,7 +30,8 @@
 //   * Online softmax per 32-token tile in base 2 (exp2 with log2(e) folded
 //     into the scale); the per-head tile max is reduced with lane shuffles
 //     and broadcast with readlane; accumulators are rescaled only when a max
-//     changes.
+//     changes (uint4 with grouped query heads: only when it grows by more
+//     than 2^8, kLazyMax).
 //   * A workgroup holds 1..4 waves, one split each.  Partials go to the
 //     workspace and attn_reduce combines the splits of each query head; or,
 //     when the workgroup holds every split of its (b, h), the partials go to
@@ -49,6 +50,10 @@ using namespace dev;
 
 
 constexpr int kSub = 16;               // tokens per MFMA (its N dimension)
+// uint4 with grouped query heads: a head's running max moves only when a
+// tile's max passes it by more than this (base-2 logits), so p <= 2^8 and
+// most tiles skip the accumulator rescale
+constexpr float kLazyMax = 8.f;
 constexpr int kMaxPagesPerSplit = 1024;
 
 // Pages per split of a paged launch.
@@ -496,6 +501,10 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     f32x4 acc2[PVM ? 8 : 1];
 #pragma unroll
     for (int nb = 0; nb < (PVM ? 8 : 1); ++nb) acc2[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    // and -sum W per V group (the same for all 16-channel blocks of a group)
+    f32x4 accn[PVM ? 2 : 1];
+#pragma unroll
+    for (int g = 0; g < (PVM ? 2 : 1); ++g) accn[g] = (f32x4){0.f, 0.f, 0.f, 0.f};
     float amg[HPL][2];
 #pragma unroll
     for (int hh = 0; hh < HPL; ++hh) amg[hh][0] = amg[hh][1] = 0.f;
@@ -505,14 +514,16 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         for (int i = lane; i < 2 * 16 * kTile / 8; i += 64) z[i] = (u32x4){0u, 0u, 0u, 0u};
         wave_lds_sync();
     }
-    // P.V of one stage on the matrix cores: O += P V over the stage's 32
+    // P.V of one stage on the matrix cores: O += P V over the stage's
     // tokens, per 16-channel block nb (V group nb / 4), as
-    //   C += W (1 + c/16)  then  C += W (-1),
+    //   C += W (1 + c/16)  and, once per V group,  N += W (-1),
     // W = p * (V group scale) as two bf16 terms (A rows 2 h, 2 h + 1), the
-    // codes as the exact bf16 values 1 + c/16 (B); the second product takes
-    // the offset back out right away, so the fp32 accumulator never carries
-    // it and C = sum W c / 16.  The codes reach the B layout (8 tokens of one
-    // channel per lane) through LDS: stored as loaded, read back transposed.
+    // codes as the exact bf16 values 1 + c/16 (B); the offset product is
+    // the same for every channel of a group, so one product per group
+    // carries it and C + N = sum W c / 16 at the end (measured on MI355X:
+    // 4-5% faster at G = 8 than taking it out per block and stage).  The
+    // codes reach the B layout (8 tokens of one channel per lane) through
+    // LDS: stored as loaded, read back transposed.
     // The products of a stage run one stage late, after the next stage's
     // scores (pv_store at the end of a stage, pv_mma in the next): the LDS
     // round trip of the weights and codes then overlaps independent work.
@@ -556,11 +567,10 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
                     const u32x4 bv = u4_to_bf16x8((uint32_t)r[h2]);
                     acc2[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Aw),
                                                                        __builtin_bit_cast(bf16x8, bv), acc2[nb], 0, 0, 0);
-                    acc2[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Aw),
-                                                                       __builtin_bit_cast(bf16x8, mones), acc2[nb], 0, 0,
-                                                                       0);
                 }
             }
+            accn[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Aw),
+                                                              __builtin_bit_cast(bf16x8, mones), accn[g], 0, 0, 0);
         }
         }
         wave_lds_sync();    // read before the next stage rewrites both tiles
@@ -592,6 +602,13 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
             acc2[nb][1] *= aA;
             acc2[nb][2] *= aB;
             acc2[nb][3] *= aB;
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            accn[g][0] *= aA;
+            accn[g][1] *= aA;
+            accn[g][2] *= aB;
+            accn[g][3] *= aB;
         }
       }
     };
@@ -676,7 +693,8 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const float tmax = readlane_f(mt[h % HPL], (h / HPL) * 16);
-            const float mn = fmaxf(m_run[h], tmax);
+            float mn = fmaxf(m_run[h], tmax);
+            if constexpr (PVM) mn = (tmax > m_run[h] + kLazyMax) ? tmax : m_run[h];
             alpha[h] = (mn == m_run[h]) ? 1.f : fast_exp2(m_run[h] - mn);
             changed |= (mn != m_run[h]);
             m_run[h] = mn;
@@ -964,7 +982,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
             }
         }
         if constexpr (PVM) {
-            // u = min term + sum W c = am + 16 (C_hi + C_lo), channel 16 nb + n16
+            // u = min term + sum W c = am + 16 (C + N) over both terms, channel 16 nb + n16
 #pragma unroll
             for (int a2 = 0; a2 < 2; ++a2) {
                 const int h = 2 * g4 + a2;
@@ -972,7 +990,9 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
 #pragma unroll
                     for (int nb = 0; nb < 8; ++nb)
                         dst0[h * hstride + 16 * nb + n16] =
-                            fmaf(16.f, acc2[nb][2 * a2] + acc2[nb][2 * a2 + 1], amr[a2][nb >> 2]);
+                            fmaf(16.f, (acc2[nb][2 * a2] + accn[nb >> 2][2 * a2]) +
+                                           (acc2[nb][2 * a2 + 1] + accn[nb >> 2][2 * a2 + 1]),
+                                 amr[a2][nb >> 2]);
                 }
             }
         } else if (lane < C::CH_LANES) {

@@ -6,12 +6,16 @@ may carry either sign).  Dequantization is bit-exact.  Attention folds the
 dequantization into fp32 arithmetic (min * sum(q) + scale * sum(q * code)),
 which differs from the oracle's fp16-rounded values by at most half an fp16
 ulp (2^-11 relative) per element.  Against the oracle the bar is the
-required 1e-3 absolute and max|err|/rms <= 3e-3 (random per-element
-differences of up to 2^-11 |x| give a typical output error near
-2^-11 / sqrt(3) of rms, about 3e-4, and a maximum over a head a few times
-that; measured maxima are near 1.3e-3).  A second, tight check compares the
-kernel with attention over the exact unrounded values min + code * scale,
-which is what the fold computes, at 1e-5 absolute and 1e-4 of rms."""
+required 1e-3 absolute and max|err|/rms <= 5e-3 (ORACLE_REL_RMS): random
+per-element differences of up to 2^-11 |x| give a typical output error near
+2^-11 / sqrt(3) of rms, about 2e-4, and the largest error grows with the
+number of outputs and with how peaked a head's weights are.  Attention over
+the exact unrounded values itself (fp64, CPU) sits 2.96e-3 of rms from the
+oracle on the 262,144 outputs of the largest case here (B32, 64 query heads),
+so 5e-3 holds that plus the kernel's own error.  A second, tight check
+compares the kernel with attention over the exact unrounded values
+min + code * scale, which is what the fold computes, at 1e-5 absolute and
+1e-4 of rms."""
 import numpy as np
 import pytest
 
@@ -20,6 +24,8 @@ from oracle import dequantize_kv4, kv4_attention, quantize_kv4, decode_attention
 from oracle.kv4 import unpack_codes
 from oracle.numerics import as_f64
 from gpu_util import assert_close, each_row, to_dev
+
+ORACLE_REL_RMS = 5e-3
 
 pytestmark = pytest.mark.gpu
 
@@ -125,7 +131,7 @@ def test_kv4_attention(da, B, Hq, Hkv, N, qd, st):
     o, kq, vq = run_kv4(da, c, st)
     assert_quant_equal(kq, quantize_kv4(c.k))
     ref = kv4_attention(as_f64(c.q, qd), *kq, *vq, c.scale)
-    assert_close(o, ref, atol=1e-3, rel_rms=3e-3, what=f"kv4 B{B} Hq{Hq} Hkv{Hkv} N{N} {qd}")
+    assert_close(o, ref, atol=1e-3, rel_rms=ORACLE_REL_RMS, what=f"kv4 B{B} Hq{Hq} Hkv{Hkv} N{N} {qd}")
     fold = decode_attention(as_f64(c.q, qd), unrounded(*kq), unrounded(*vq), c.scale)
     assert_close(o, fold, atol=1e-5, rel_rms=1e-4, what="  vs unrounded dequant")
 
@@ -182,7 +188,7 @@ def test_kv4_grouped_query_heads_long_context(da, G, qd):
     for b in range(2):
         sel = lambda t: [x[b:b + 1] for x in t]
         ref = kv4_attention(q64[b:b + 1], *sel(kq), *sel(vq), c.scale)
-        assert_close(o[b:b + 1], ref, atol=1e-3, rel_rms=3e-3, what=f"kv4 G{G} {qd} row {b}")
+        assert_close(o[b:b + 1], ref, atol=1e-3, rel_rms=ORACLE_REL_RMS, what=f"kv4 G{G} {qd} row {b}")
         fold = decode_attention(q64[b:b + 1], unrounded(*sel(kq)), unrounded(*sel(vq)), c.scale)
         assert_close(o[b:b + 1], fold, atol=1e-5, rel_rms=1e-4, what="  vs unrounded dequant")
 
@@ -203,7 +209,7 @@ def test_workload4_full_size_every_row(da):
         q64 = as_f64(c.q[b:b + 1], "f16")
         ref = kv4_attention(q64, *want_k, *want_v, c.scale)
         fold = decode_attention(q64, unrounded(*want_k), unrounded(*want_v), c.scale)
-        e1 = max(assert_close(o[b, h], ref[0, h], atol=1e-3, rel_rms=3e-3, what=f"w4 b{b} h{h}", quiet=True)
+        e1 = max(assert_close(o[b, h], ref[0, h], atol=1e-3, rel_rms=ORACLE_REL_RMS, what=f"w4 b{b} h{h}", quiet=True)
                  ["max_abs"] for h in range(ref.shape[1]))
         e2 = max(assert_close(o[b, h], fold[0, h], atol=1e-5, rel_rms=1e-4, what=f"w4 fold b{b} h{h}",
                               quiet=True)["max_abs"] for h in range(ref.shape[1]))
