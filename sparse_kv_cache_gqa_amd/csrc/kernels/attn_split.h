@@ -21,7 +21,10 @@
 //     (hi + mid + lo) when q is fp32, so the products are exact and the sum is
 //     fp32-accurate; for a uint4 cache the rows also separate the two
 //     64-channel quantization groups so their scales can be applied after,
-//     and the codes enter as the exact fp16 values 1 + c/16.  With one query
+//     and the codes enter as the exact fp16 values 1 + c/16.  With grouped
+//     query heads and a uint4 cache the products are int8 instead: the codes
+//     as bytes, q of each (head, group) as a 22-bit fixed-point integer in
+//     three int8 digits (A rows), so q . c comes out exact per digit.  With one query
 //     head per KV head (uint4, MHA) q fills all 16 rows, so every lane group
 //     receives scores and each lane scores the token whose min/scale words it
 //     loaded itself (no metadata shuffles; the tile max by DPP).
@@ -99,9 +102,17 @@ struct Cfg {
     // deeper stages cost the other layouts occupancy
     static constexpr int TS = (R == 128 || (U4 && G > 1)) ? 4 : 2;
     static constexpr int TILE = kSub * TS;              // tokens per stage
+    // uint4 with grouped query heads: q.K^T on the int8 matrix cores
+    // (measured on MI355X, uint4 K/V of 8 rows x 8 KV heads x 32768 tokens:
+    // G = 4 / 8 took 60.5-60.9 / 72.5 us against 63.3-63.7 / 75.6 us with
+    // the fp16 products, G = 2 unchanged at 61.9; the codes need 3 VALU
+    // instructions per 8 instead of 9)
+    static constexpr bool I8S = U4 && G > 1;
     // 16 MFMA rows must hold every (head, group, split term); rows fit 64..1024 bytes
     static constexpr bool ok = RPH0 <= 4 && G * RPH <= 16 && R >= 64 && R <= 1024;
 };
+
+typedef int i32x4v __attribute__((ext_vector_type(4)));
 
 // K/V rows are read once per call: load them non-temporally (streaming).
 __device__ __forceinline__ u32x4 ld_stream(const char *p) {
@@ -278,6 +289,12 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     const int b = unit / a.Hkv;
     const int hkv = unit - b * a.Hkv;
     const int pps = PAGED ? pages_per_split(a.split_tokens, a.log2_page) : 0;
+
+    // the score lanes: lane group g4 holds heads hd(g4, 0..HPL-1); with int8
+    // scores (I8S) A-row block hh carries heads 4 hh .. 4 hh + 3
+    auto hd = [](int g, int hh) { return C::I8S ? g + 4 * hh : g * HPL + hh; };
+    auto grp_of = [](int h) { return C::I8S ? h % 4 : h / HPL; };
+    auto slot_of = [](int h) { return C::I8S ? h / 4 : h % HPL; };
 
     float *const p_lds = p_all[wave];
     int32_t *const pg_lds = pg_all[wave];
@@ -459,6 +476,61 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         }
     }
 
+    // uint4 with grouped query heads: q of (head h, group gr) as the integer
+    // rint(q * 2^e), e from the group's largest |q| so that |q| 2^e < 2^22,
+    // in three signed int8 digits d0 2^16 + d1 2^8 + d2 (A row 4 (h mod 4) +
+    // digit of block h / 4; row 4 h' + 3 stays zero).  After the key codes
+    // are regrouped (see the scores), k-slot byte j of lane group g4 is
+    // channel 64 gr + base(g4) + 8 (j / 8) + 2 (j mod 4) + (j / 4) mod 2,
+    // base = 0, 32, 16, 48 for g4 = 0..3: the order in which a dword of
+    // codes splits into its low and high nibbles.  The rounding of q to 22
+    // bits of its group's largest value is below fp32 accumulation error.
+    u32x4 Aq8[C::I8S ? 2 : 1][C::I8S ? HPL : 1];
+    float ek[C::I8S ? 2 : 1][C::I8S ? HPL : 1][3];
+    if constexpr (C::I8S) {
+#pragma unroll
+        for (int hb = 0; hb < HPL; ++hb) {
+        const int m = n16, h = 4 * hb + (m >> 2), t = m & 3;
+#pragma unroll
+        for (int gr = 0; gr < 2; ++gr) {
+            float qv[16];
+            float mx = 0.f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int ch = 64 * gr + 32 * (g4 & 1) + 16 * (g4 >> 1) + 8 * (j >> 3) + 2 * (j & 3) + ((j >> 2) & 1);
+                qv[j] = h < G ? load_scalar<QF>(a.q, qoff + h * D + ch) : 0.f;
+                mx = fmaxf(mx, fabsf(qv[j]));
+            }
+            mx = fmaxf(mx, shfl_xor(mx, 16));
+            mx = fmaxf(mx, shfl_xor(mx, 32));
+            int ex;
+            (void)frexpf(mx, &ex);
+            const int e = 22 - ex;               // |q| 2^e < 2^22
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                uint32_t dw = 0;
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const int qi = (int)rintf(ldexpf(qv[4 * w + bb], e));
+                    const int d2 = (int)(int8_t)(qi & 0xFF);
+                    const int q1 = (qi - d2) >> 8;
+                    const int d1 = (int)(int8_t)(q1 & 0xFF);
+                    const int d0 = (q1 - d1) >> 8;
+                    const int dig = (h >= G || t == 3) ? 0 : (t == 0 ? d0 : (t == 1 ? d1 : d2));
+                    dw |= (uint32_t)(dig & 0xFF) << (8 * bb);
+                }
+                Aq8[gr][hb][w] = dw;
+            }
+            // the score lanes of head hd(g4, hb) take its exponent from row 4 g4
+            const int es = __shfl(e, 4 * g4, 64);
+            const float sc = ldexpf(1.f, -es);
+            ek[gr][hb][0] = 65536.f * sc;
+            ek[gr][hb][1] = 256.f * sc;
+            ek[gr][hb][2] = sc;
+        }
+        }
+    }
+
     // uint4: per (head, group) sum of q, for the min term of the folded dequantization
     float qs[HPL][NGRP];
 #pragma unroll
@@ -473,7 +545,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
                 float x = load_scalar<QF>(a.q, qoff + h * D + gr * 64 + lane);
 #pragma unroll
                 for (int o = 1; o < 64; o <<= 1) x += shfl_xor(x, o);
-                if (SOLO || h / HPL == g4) qs[h % HPL][gr] = x;
+                if (SOLO || grp_of(h) == g4) qs[slot_of(h)][gr] = x;
             }
     }
 
@@ -621,6 +693,40 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
 
 #pragma unroll
         for (int ts = 0; ts < kTS; ++ts) {
+          if constexpr (C::I8S) {
+            // q . c per group, exact in int32 per digit, then
+            // raw = sum_gr min sum(q) + scale (q . c)
+            const uint32_t kmn2 = __shfl(st.mk, ts * kSub + n16, 64);
+            const uint32_t ksc2 = __shfl(st.sk, ts * kSub + n16, 64);
+            float raw[HPL];
+#pragma unroll
+            for (int hb = 0; hb < HPL; ++hb) raw[hb] = 0.f;
+            // lanes 0..31 keep their first 16 codes (group 0) and take the
+            // first 16 of lane + 32 (group 1); lanes 32..63 take the last 16
+            // of lane - 32 (group 0) and keep their last 16 (group 1)
+            const auto s0 = __builtin_amdgcn_permlane32_swap(st.K[ts][0][0], st.K[ts][0][2], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(st.K[ts][0][1], st.K[ts][0][3], false, false);
+            const uint32_t kw[4] = {s0[0], s1[0], s0[1], s1[1]};
+#pragma unroll
+            for (int gr = 0; gr < 2; ++gr) {
+                const uint32_t x0 = kw[2 * gr], x1 = kw[2 * gr + 1];
+                const u32x4 bv = {x0 & 0x0F0F0F0Fu, (x0 >> 4) & 0x0F0F0F0Fu, x1 & 0x0F0F0F0Fu, (x1 >> 4) & 0x0F0F0F0Fu};
+                const i32x4v z = {0, 0, 0, 0};
+                const float mn = f16_to_f32((kmn2 >> (16 * gr)) & 0xFFFFu);
+                const float sg = f16_to_f32((ksc2 >> (16 * gr)) & 0xFFFFu);
+#pragma unroll
+                for (int hb = 0; hb < HPL; ++hb) {
+                    const i32x4v tt = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4v, Aq8[gr][hb]),
+                                                                            __builtin_bit_cast(i32x4v, bv), z, 0, 0, 0);
+                    const float dq = fmaf((float)tt[0], ek[gr][hb][0],
+                                          fmaf((float)tt[1], ek[gr][hb][1], (float)tt[2] * ek[gr][hb][2]));
+                    raw[hb] += fmaf(mn, qs[hb][gr], sg * dq);
+                }
+            }
+#pragma unroll
+            for (int hb = 0; hb < HPL; ++hb)
+                sc[ts][hb] = (hd(g4, hb) < G && st.kok[ts]) ? raw[hb] * sl2 : neg_inf();
+          } else {
             f32x4 cc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
@@ -643,7 +749,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
             }
 #pragma unroll
             for (int hh = 0; hh < HPL; ++hh) {
-                const int h = g4 * HPL + hh;
+                const int h = hd(g4, hh);
                 float raw = 0.f;
                 if constexpr (C::U4) {
                     // this lane's K token (ts, n16): its (min, min) and (scale, scale) pairs
@@ -665,6 +771,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
                 }
                 sc[ts][hh] = (h < G && st.kok[ts]) ? raw * sl2 : neg_inf();
             }
+          }
         }
 
         // the scores are done with st.K (and st.kok)
@@ -692,7 +799,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         bool changed = false;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const float tmax = readlane_f(mt[h % HPL], (h / HPL) * 16);
+            const float tmax = readlane_f(mt[slot_of(h)], grp_of(h) * 16);
             float mn = fmaxf(m_run[h], tmax);
             if constexpr (PVM) mn = (tmax > m_run[h] + kLazyMax) ? tmax : m_run[h];
             alpha[h] = (mn == m_run[h]) ? 1.f : fast_exp2(m_run[h] - mn);
@@ -710,7 +817,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
             }
 #pragma unroll
             for (int hh = 0; hh < HPL; ++hh) {
-                const int h = g4 * HPL + hh;
+                const int h = hd(g4, hh);
                 float al = 1.f;
 #pragma unroll
                 for (int h2 = 0; h2 < G; ++h2) if (h2 == h) al = alpha[h2];
@@ -737,7 +844,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         }
 #pragma unroll
         for (int hh = 0; hh < HPL; ++hh) {
-            const int h = g4 * HPL + hh;
+            const int h = hd(g4, hh);
             float mh = 0.f;
 #pragma unroll
             for (int h2 = 0; h2 < G; ++h2) if (h2 == h) mh = m_run[h2];
@@ -951,7 +1058,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
-                const float x = readlane_f(amg[h % HPL][g], 16 * (h / HPL));
+                const float x = readlane_f(amg[slot_of(h)][g], 16 * grp_of(h));
                 if (h == 2 * g4) amr[0][g] = x;
                 if (h == 2 * g4 + 1) amr[1][g] = x;
             }
@@ -977,7 +1084,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         if (n16 == 0) {
 #pragma unroll
             for (int hh = 0; hh < HPL; ++hh) {
-                const int h = g4 * HPL + hh;
+                const int h = hd(g4, hh);
                 if (h < G) dst0[h * hstride + D + 1] = l_part[hh];
             }
         }
