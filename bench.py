@@ -511,6 +511,7 @@ def bench_kv4(args, torch, np, da, synth):
 
     ms_eager = time_events(torch, step, args.steps, args.warmup)
     ms = ms_eager if args.no_graph else time_graph(torch, step, args.steps, args.warmup)
+    ms_kernel = time_each(torch, step, args.steps)
     code_bytes = 2 * B * H * N * D // 2
     ms_bytes = 2 * 2 * B * H * N * (D // 64) * 2
     step_bytes = code_bytes + ms_bytes + B * H * D * 2 + B * H * D * 4
@@ -519,6 +520,7 @@ def bench_kv4(args, torch, np, da, synth):
     res = {"workload": "flexgen-uint4 B64 H56 D128 N1024 groups of 64", "ms_per_step": ms,
            "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "step_bytes": step_bytes,
            "tokens_per_s": B / (ms * 1e-3), "quantize_k_ms": ms_quant, "eager_ms_per_step": ms_eager,
+           "avg_launch_ms": ms_kernel, "kernel_gbs": step_bytes / (ms_kernel * 1e-3) / 1e9,
            "traffic": measured_traffic("attn_split_uint4_flexgen", code_bytes + ms_bytes + B * H * D * 2)}
     log(f"kv4: {ms * 1e3:.1f} us/step ({gbs:.0f} GB/s)")
     del copies
