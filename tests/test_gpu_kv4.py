@@ -220,12 +220,14 @@ def test_workload4_full_size_every_row(da):
           f"{max(r[1] for r in rs):.2e} vs unrounded dequantization", flush=True)
 
 
-@pytest.mark.parametrize("qd", ["f16", "f32"])
-def test_kv4_query_with_wide_dynamic_range(da, qd):
+@pytest.mark.parametrize("qd,G", [("f16", 1), ("f32", 1), ("f16", 2), ("f16", 4), ("f32", 4), ("f16", 8)])
+def test_kv4_query_with_wide_dynamic_range(da, qd, G):
     """One query channel per group far larger than the rest, one group all
-    zero, one head with tiny values: the query's integer digits (one scale
-    per 64-channel group) must still give fp32-accurate scores."""
-    c = synth.dense_case([301, 0 if qd == "f16" else 1], 2, 3, 3, 128, 400, qd, "f16")
+    zero, one head with tiny values: the scores must stay fp32-accurate.
+    With grouped query heads q enters the int8 products as integer digits
+    with one power-of-two scale per (head, 64-channel group); with one head
+    it enters the fp16 products as one or two fp16 terms."""
+    c = synth.dense_case([301, 0 if qd == "f16" else 1, G], 2, 3 * G, 3, 128, 400, qd, "f16")
     q = c.q.astype(np.float64)
     q[0, 0, 5] = 90.0                   # group 0 of head 0 dominated by one channel
     q[0, 0, 64:] = 0.0                  # group 1 of head 0 all zero
@@ -239,6 +241,6 @@ def test_kv4_query_with_wide_dynamic_range(da, qd):
     # dequantized keys, so against the oracle only the 1e-3 bar applies here;
     # the fold itself is held to the tight bar
     ref = kv4_attention(as_f64(c.q, qd), *kq, *vq, c.scale)
-    assert_close(o, ref, atol=1e-3, what=f"kv4 wide q {qd}")
+    assert_close(o, ref, atol=1e-3, what=f"kv4 wide q {qd} G{G}")
     fold = decode_attention(as_f64(c.q, qd), unrounded(*kq), unrounded(*vq), c.scale)
     assert_close(o, fold, atol=1e-5, rel_rms=1e-4, what="  vs unrounded dequant")
