@@ -85,9 +85,11 @@ struct Cfg {
                              : (QF == KF || (U4 && QF == FMT_F16)) ? 1
                              : (KF == FMT_BF16 ? (G <= 4 ? 3 : 2) : 2);
     static constexpr int RPH0 = SPL * NGRP;            // A rows used per head
-    // uint4 with 2 or 4 query heads: four rows per head (two of them zero),
-    // so each lane group scores one head and the per-head work after the
-    // scores (softmax, P.V weights) spreads over the lane groups
+    // uint4 with 2 or 4 query heads: four rows per head (the int8 scores'
+    // three digits and a zero row), so each lane group scores one head and
+    // the per-head work after the scores (softmax, P.V weights) spreads over
+    // the lane groups; with 8 heads, two blocks of A rows, and lane group g
+    // scores heads g and g + 4 (HPL = 2)
     static constexpr int RPH = RPH0 <= 1 ? 1 : (RPH0 <= 2 ? ((U4 && G > 1 && G <= 4) ? 4 : 2) : 4);
     static constexpr int HPL = 4 / RPH;                 // heads per 16-lane group
     static constexpr int NCH = R / 64;                  // 16-byte K chunks per lane per sub-tile
@@ -569,7 +571,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     // uint4: P.V accumulators, one 16x16 MFMA output per 16-channel block:
     // lane (g4, n) holds rows 4 g4 + i = (head 2 g4 + i / 2, bf16 term i mod 2)
     // of channel 16 nb + n; amg[hh][g]: sum of p * (V group minimum) of head
-    // g4 * HPL + hh over this lane's tokens (one-head layout: am below)
+    // hd(g4, hh) over this lane's tokens (one-head layout: am below)
     f32x4 acc2[PVM ? 8 : 1];
 #pragma unroll
     for (int nb = 0; nb < (PVM ? 8 : 1); ++nb) acc2[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
