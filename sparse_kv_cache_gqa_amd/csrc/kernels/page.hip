@@ -20,9 +20,10 @@
 //      11 and 10 bits) over an order-preserving uint32 image of the fp32
 //      scores, one shared LDS histogram per pass (two buffers, so the next
 //      pass's is cleared while the current one counts: two barriers a
-//      pass).  Ties at the K-th score go to the lower page index: the equal
-//      keys are ranked by a block-wide prefix count in index order (skipped
-//      when every key equal to the K-th is kept).  The kept indices are
+//      pass; the passes stop once every key left in the chosen bin is kept,
+//      usually after the second).  Ties at the K-th score go to the lower
+//      page index: the equal keys are ranked by a block-wide prefix count in
+//      index order (skipped when every key equal to the K-th is kept).  The kept indices are
 //      compacted in index order, so they come out ascending.
 //   3. Attend modes continue in the same workgroup: token mode weights the
 //      kept tokens' value rows by the softmax of their exact scores, still in
@@ -438,8 +439,13 @@ __global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args)
         pmask |= dmask << shift;
         need = pick_need;
         eq_count = pick_count;
+        // every key left in the chosen bin is kept: the later digits would
+        // only order keys that are all selected anyway
+        if (need == eq_count) break;
     }
-    const uint32_t T = prefix;              // key of the top_k-th largest score
+    // the leading digits (pmask) of the top_k-th largest key; all 32 bits
+    // unless the passes stopped early
+    const uint32_t T = prefix;
 
     // ---- 3. ties by lower index; compact in index order --------------------
     // Keep every key > T and the `need` lowest-indexed keys == T.  When all
@@ -451,14 +457,14 @@ __global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args)
     const bool all_ties = need == eq_count;
     if (!all_ties) {
         uint32_t n_eq = 0;
-        for (int64_t i = i0; i < i1; ++i) n_eq += order_key(sc_lds[i]) == T;
+        for (int64_t i = i0; i < i1; ++i) n_eq += (order_key(sc_lds[i]) & pmask) == T;
         eq_before = block_exscan<kSelWaves>(n_eq, scan_buf, &tot);
     }
     uint32_t n_sel = 0;
     {
         uint32_t r = eq_before;
         for (int64_t i = i0; i < i1; ++i) {
-            const uint32_t key = order_key(sc_lds[i]);
+            const uint32_t key = order_key(sc_lds[i]) & pmask;
             if (key > T) ++n_sel;
             else if (key == T) { if (all_ties || r < need) ++n_sel; ++r; }
         }
@@ -469,7 +475,7 @@ __global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args)
     {
         uint32_t r = eq_before;
         for (int64_t i = i0; i < i1; ++i) {
-            const uint32_t key = order_key(sc_lds[i]);
+            const uint32_t key = order_key(sc_lds[i]) & pmask;
             bool sel = key > T;
             if (key == T) { sel = all_ties || r < need; ++r; }
             if (sel && pos < (uint32_t)top_k) {
