@@ -342,7 +342,9 @@ da_status da_dequantize_kv4(int64_t n_rows, int32_t row_len,
  *   k_min, k_scale, v_min, v_scale
  *                     [batch][n_kv_heads][n_ctx][head_dim/64] fp16, device
  *   o                 [batch][n_q_heads][head_dim] fp32, device (written)
- * head_dim must be 128; kv_dtype is ignored; ws as reported.
+ * head_dim must be 128; kv_dtype is ignored; ws as reported.  A query head
+ * holding a NaN or an infinity gets an unspecified row of o; the other rows
+ * are unaffected.
  * ------------------------------------------------------------------------ */
 size_t da_decode_attention_kv4_workspace(const da_attn_shape *s);
 da_status da_decode_attention_kv4(const da_attn_shape *s, const void *q,

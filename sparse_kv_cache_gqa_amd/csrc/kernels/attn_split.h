@@ -497,14 +497,18 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         for (int gr = 0; gr < 2; ++gr) {
             float qv[16];
             float mx = 0.f;
+            int bad = 0;                         // a NaN or an infinity in the group
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int ch = 64 * gr + 32 * (g4 & 1) + 16 * (g4 >> 1) + 8 * (j >> 3) + 2 * (j & 3) + ((j >> 2) & 1);
                 qv[j] = h < G ? load_scalar<QF>(a.q, qoff + h * D + ch) : 0.f;
                 mx = fmaxf(mx, fabsf(qv[j]));
+                bad |= !(fabsf(qv[j]) <= 3.402823466e38f);
             }
             mx = fmaxf(mx, shfl_xor(mx, 16));
             mx = fmaxf(mx, shfl_xor(mx, 32));
+            bad |= shfl_xor(bad, 16);
+            bad |= shfl_xor(bad, 32);
             int ex;
             (void)frexpf(mx, &ex);
             const int e = 22 - ex;               // |q| 2^e < 2^22
@@ -523,9 +527,12 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
                 }
                 Aq8[gr][hb][w] = dw;
             }
-            // the score lanes of head hd(g4, hb) take its exponent from row 4 g4
+            // the score lanes of head hd(g4, hb) take its exponent from row 4 g4;
+            // a group holding a NaN or an infinity gets NaN scales, so that
+            // head's scores and output are NaN, as the arithmetic would give
             const int es = __shfl(e, 4 * g4, 64);
-            const float sc = ldexpf(1.f, -es);
+            const int bs = __shfl(bad, 4 * g4, 64);
+            const float sc = bs ? __builtin_nanf("") : ldexpf(1.f, -es);
             ek[gr][hb][0] = 65536.f * sc;
             ek[gr][hb][1] = 256.f * sc;
             ek[gr][hb][2] = sc;

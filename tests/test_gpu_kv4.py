@@ -244,3 +244,23 @@ def test_kv4_query_with_wide_dynamic_range(da, qd, G):
     assert_close(o, ref, atol=1e-3, what=f"kv4 wide q {qd} G{G}")
     fold = decode_attention(as_f64(c.q, qd), unrounded(*kq), unrounded(*vq), c.scale)
     assert_close(o, fold, atol=1e-5, rel_rms=1e-4, what="  vs unrounded dequant")
+
+
+@pytest.mark.parametrize("G,qd,val", [(1, "f16", np.nan), (2, "f16", np.nan), (4, "f32", np.nan), (8, "f16", np.nan),
+                                      (4, "f16", np.inf)])
+def test_kv4_nonfinite_query_head_is_isolated(da, G, qd, val):
+    """A NaN (or an infinity) in one channel of one query head leaves every
+    other row bitwise as in the run without it: the heads of a KV head share
+    a wave, its A rows and its running state arrays, not their arithmetic.
+    (The affected row itself is not specified: its scores are all NaN, so no
+    running max ever becomes finite and the split counts as empty.)"""
+    c = synth.dense_case([304, G], 2, 2 * G, 2, 128, 300, qd, "f16")
+    o0, _, _ = run_kv4(da, c)
+    q = c.q.copy()
+    q[1, 1, 70] = val
+    c2 = synth.DenseCase(q=q, k=c.k, v=c.v, q_dtype=qd, kv_dtype="f16", scale=c.scale)
+    o1, _, _ = run_kv4(da, c2)
+    keep = np.ones(o0.shape[:2], dtype=bool)
+    keep[1, 1] = False
+    assert np.array_equal(o1[keep], o0[keep]), f"G{G}: other rows changed"
+    assert not np.array_equal(o1[1, 1], o0[1, 1]), f"G{G}: the non-finite query left its row unchanged"
