@@ -24,13 +24,17 @@
 //     and the codes enter as the exact fp16 values 1 + c/16.  With grouped
 //     query heads and a uint4 cache the products are int8 instead: the codes
 //     as bytes, q of each (head, group) as a 22-bit fixed-point integer in
-//     three int8 digits (A rows), so q . c comes out exact per digit.  With one query
-//     head per KV head (uint4, MHA) q fills all 16 rows, so every lane group
-//     receives scores and each lane scores the token whose min/scale words it
-//     loaded itself (no metadata shuffles; the tile max by DPP).
+//     three int8 digits (A rows), so q . c comes out exact per digit.  With
+//     one query head per KV head (uint4, MHA) q fills all 16 rows, so every
+//     lane group receives scores and each lane scores the token whose
+//     min/scale words it loaded itself (no metadata shuffles; the tile max by
+//     DPP).
 //   * P.V runs on the VALU in fp32: each lane owns a fixed set of channels and
 //     accumulates them over the tokens it loads (16-byte coalesced loads).
-//   * Online softmax per 32-token tile in base 2 (exp2 with log2(e) folded
+//     For a uint4 cache with grouped query heads it runs on the matrix cores
+//     instead (bf16 weights in two terms, the codes as bf16 1 + c/16, staged
+//     through LDS; see pv_mma).
+//   * Online softmax per 32- or 64-token tile in base 2 (exp2 with log2(e) folded
 //     into the scale); the per-head tile max is reduced with lane shuffles
 //     and broadcast with readlane; accumulators are rescaled only when a max
 //     changes (uint4 with grouped query heads: only when it grows by more
