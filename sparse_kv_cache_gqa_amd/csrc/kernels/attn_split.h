@@ -84,9 +84,10 @@ struct Cfg {
     static constexpr bool U4 = KF == FMT_U4;
     static constexpr int R = KF == FMT_F32 ? 4 * D : (U4 ? D / 2 : 2 * D);   // row bytes
     static constexpr int NGRP = U4 ? D / 64 : 1;        // quantization groups per row
-    // number of terms q is split into for the MFMA input type
+    // number of terms q is split into for the MFMA input type (uint4 with
+    // grouped query heads: one, q enters the int8 products as digits)
     static constexpr int SPL = (KF == FMT_F32) ? 1
-                             : (QF == KF || (U4 && QF == FMT_F16)) ? 1
+                             : (QF == KF || (U4 && (QF == FMT_F16 || G > 1))) ? 1
                              : (KF == FMT_BF16 ? (G <= 4 ? 3 : 2) : 2);
     static constexpr int RPH0 = SPL * NGRP;            // A rows used per head
     // uint4 with 2 or 4 query heads: four rows per head (the int8 scores'

@@ -122,6 +122,8 @@ KV4_CASES = [
     (1, 16, 2, 250, "f16", 32),       # G = 8, splits of half a stage
     (32, 32, 8, 1000, "f16", 0),      # G = 4, 256 units x 4 splits merged in the workgroup
     (32, 64, 8, 900, "f16", 0),       # G = 8, merged in the workgroup
+    (2, 16, 2, 1500, "f32", 0),       # G = 8, fp32 q (digits of the int8 products)
+    (3, 24, 3, 200, "f32", 64),       # G = 8, fp32 q, ragged splits
 ]
 
 
@@ -176,7 +178,7 @@ def test_kv4_integer_data_grouped_query_heads(da, G):
     assert_close(o, ref, atol=4e-5, what=f"kv4 integer data G{G}")
 
 
-@pytest.mark.parametrize("G,qd", [(2, "f16"), (4, "f16"), (8, "f16"), (4, "f32")])
+@pytest.mark.parametrize("G,qd", [(2, "f16"), (4, "f16"), (8, "f16"), (4, "f32"), (8, "f32")])
 def test_kv4_grouped_query_heads_long_context(da, G, qd):
     """Grouped query heads over a long uint4 cache (B2, 8 KV heads, 32768
     tokens: 32 splits of 1024 and the merge kernel, the launch of the
@@ -220,7 +222,7 @@ def test_workload4_full_size_every_row(da):
           f"{max(r[1] for r in rs):.2e} vs unrounded dequantization", flush=True)
 
 
-@pytest.mark.parametrize("qd,G", [("f16", 1), ("f32", 1), ("f16", 2), ("f16", 4), ("f32", 4), ("f16", 8)])
+@pytest.mark.parametrize("qd,G", [("f16", 1), ("f32", 1), ("f16", 2), ("f16", 4), ("f32", 4), ("f16", 8), ("f32", 8)])
 def test_kv4_query_with_wide_dynamic_range(da, qd, G):
     """One query channel per group far larger than the rest, one group all
     zero, one head with tiny values: the scores must stay fp32-accurate.
