@@ -1,7 +1,11 @@
-"""Seeded random shapes for decode attention over dense and uint4 caches,
-each against the fp64 oracle: batch 1-3, 1-4 KV heads, G in {1, 2, 4, 8},
+"""Seeded random shapes for decode attention, each against the fp64 oracle.
+Dense and uint4 caches: batch 1-3, 1-4 KV heads, G in {1, 2, 4, 8},
 head_dim 64 or 128 (uint4: 128), 1-3000 tokens, every supported pair of q
 and cache formats, the default split or a random multiple of 16 tokens.
+Page-sparse (both routes) and token top-k (one call and two): random page
+sizes, kept counts, context lengths and grouped query heads, with the
+selection checked by the near-tie rule and the attention on the GPU's own
+set.
 The cases are drawn once from a fixed seed, so every run checks the same
 shapes (their parameters are in the test ids); they complement the chosen
 edge cases of test_gpu_dense.py and test_gpu_kv4.py with combinations
@@ -22,10 +26,10 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import decode_attention, kv4_attention
+from oracle import bound_scores, decode_attention, kv4_attention, page_meta, sparse_attention, token_scores
 from oracle.kv4 import unpack_codes
 from oracle.numerics import as_f64
-from gpu_util import assert_close, to_dev
+from gpu_util import assert_close, check_selection, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -103,3 +107,89 @@ def test_random_uint4(da, B, Hq, Hkv, N, qd, st):
     assert_close(o, decode_attention(q64, _unrounded(*kq), _unrounded(*vq), c.scale), atol=1e-5, rel_rms=rel,
                  what=what + " vs unrounded dequant")
     assert_close(o, kv4_attention(q64, *kq, *vq, c.scale), atol=1e-3, rel_rms=5e-3, what=what + " vs oracle")
+
+
+def _draw_sparse(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B, Hkv = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        G = int(rng.choice([1, 2, 4]))
+        D = int(rng.choice([64, 128]))
+        dt = "f16" if rng.random() < 0.6 else "bf16"
+        S = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        N = int(rng.integers(1, 6001))
+        P = -(-N // S)
+        # the one-kernel route's LDS: P + K + 2 K S + 16 D floats <= 16384
+        kmax = min(P, (16384 - P - 16 * D) // (1 + 2 * S))
+        K = int(rng.integers(1, kmax + 1))
+        out.append((B, G * Hkv, Hkv, D, N, S, K, dt))
+    return out
+
+
+SPARSE_CASES = _draw_sparse(16, 2028)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,N,S,K,dt", SPARSE_CASES, ids=_ids(SPARSE_CASES))
+def test_random_page_sparse(da, B, Hq, Hkv, D, N, S, K, dt):
+    import torch
+    G = Hq // Hkv
+    c = synth.dense_case([702, B, Hq, Hkv, D, N], B, Hq, Hkv, D, N, dt, dt)
+    q, k, v = to_dev(c.q, dt), to_dev(c.k, dt), to_dev(c.v, dt)
+    kmin, kmax = da.da_build_page_meta(k, S)
+    idx2 = da.da_select_pages(q, kmin, kmax, S, K, N)
+    o2 = da.da_decode_attention_paged(q, k, v, idx2, S, scale=c.scale)
+    o1, idx1 = da.da_decode_attention_sparse(q, kmin, kmax, k, v, S, K, scale=c.scale, want_idx=True)
+    torch.cuda.synchronize()
+    idx1, idx2 = idx1.cpu().numpy(), idx2.cpu().numpy()
+    assert np.array_equal(idx1, idx2), "the two routes keep different pages"
+    q64 = as_f64(c.q, dt)
+    k64 = np.repeat(as_f64(c.k, dt), G, axis=1)
+    v64 = np.repeat(as_f64(c.v, dt), G, axis=1)
+    check_selection(idx1, bound_scores(q64, *page_meta(k64, S)), K)
+    ref = sparse_attention(q64, k64, v64, idx1, S, c.scale)
+    what = f"pages B{B} Hq{Hq} Hkv{Hkv} D{D} N{N} S{S} K{K} {dt}"
+    assert_close(o1.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what=what + " one kernel")
+    assert_close(o2.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what=what + " two calls")
+
+
+_TOKEN_FORMATS = [("f16", "f16"), ("bf16", "bf16"), ("f32", "f32"), ("f32", "bf16"), ("f32", "f16")]
+
+
+def _draw_tokens(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B, Hkv = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        G = int(rng.choice([1, 2, 4]))
+        D = int(rng.choice([64, 128]))
+        N = int(rng.integers(1, 4001))
+        qd, kd = _TOKEN_FORMATS[int(rng.integers(len(_TOKEN_FORMATS)))]
+        K = int(rng.integers(1, N + 1))
+        out.append((B, G * Hkv, Hkv, D, N, K, qd, kd))
+    return out
+
+
+TOKEN_CASES = _draw_tokens(12, 2029)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,N,K,qd,kd", TOKEN_CASES, ids=_ids(TOKEN_CASES))
+def test_random_token_topk(da, B, Hq, Hkv, D, N, K, qd, kd):
+    import torch
+    G = Hq // Hkv
+    c = synth.dense_case([703, B, Hq, Hkv, D, N], B, Hq, Hkv, D, N, qd, kd)
+    q, k, v = to_dev(c.q, qd), to_dev(c.k, kd), to_dev(c.v, kd)
+    o1, idx1 = da.da_decode_attention_topk(q, k, v, K, scale=c.scale, want_idx=True)
+    idx2 = da.da_select_tokens(q, k, K)
+    o2 = da.da_decode_attention_paged(q, k, v, idx2, 1, scale=c.scale)
+    torch.cuda.synchronize()
+    idx1, idx2 = idx1.cpu().numpy(), idx2.cpu().numpy()
+    assert np.array_equal(idx1, idx2), "the two routes keep different tokens"
+    q64 = as_f64(c.q, qd)
+    k64 = np.repeat(as_f64(c.k, kd), G, axis=1)
+    v64 = np.repeat(as_f64(c.v, kd), G, axis=1)
+    check_selection(idx1, token_scores(q64, k64), K)
+    ref = sparse_attention(q64, k64, v64, idx1, 1, c.scale)
+    what = f"tokens B{B} Hq{Hq} Hkv{Hkv} D{D} N{N} K{K} {qd}/{kd}"
+    assert_close(o1.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what=what + " one kernel")
+    assert_close(o2.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what=what + " two calls")
