@@ -5,7 +5,8 @@ and cache formats, the default split or a random multiple of 16 tokens.
 Page-sparse (both routes) and token top-k (one call and two): random page
 sizes, kept counts, context lengths and grouped query heads, with the
 selection checked by the near-tie rule and the attention on the GPU's own
-set.
+set.  Chunked prefill: random chunk lengths, prefixes, head counts and
+head_dim.
 The cases are drawn once from a fixed seed, so every run checks the same
 shapes (their parameters are in the test ids); they complement the chosen
 edge cases of test_gpu_dense.py and test_gpu_kv4.py with combinations
@@ -26,7 +27,8 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import bound_scores, decode_attention, kv4_attention, page_meta, sparse_attention, token_scores
+from oracle import (bound_scores, chunk_prefill_attention, decode_attention, kv4_attention, page_meta,
+                    sparse_attention, token_scores)
 from oracle.kv4 import unpack_codes
 from oracle.numerics import as_f64
 from gpu_util import assert_close, check_selection, to_dev
@@ -193,3 +195,33 @@ def test_random_token_topk(da, B, Hq, Hkv, D, N, K, qd, kd):
     what = f"tokens B{B} Hq{Hq} Hkv{Hkv} D{D} N{N} K{K} {qd}/{kd}"
     assert_close(o1.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what=what + " one kernel")
     assert_close(o2.cpu().numpy(), ref, atol=1e-5, rel_rms=1e-4, what=what + " two calls")
+
+
+def _draw_prefill(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B, Hkv = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        G = int(rng.choice([1, 2, 4]))
+        D = int(rng.choice([64, 128]))
+        C = int(rng.integers(1, 600))
+        P = int(rng.choice([0, int(rng.integers(1, 1500))]))
+        dt = "bf16" if rng.random() < 0.6 else "f16"
+        out.append((B, G * Hkv, Hkv, C, P, D, dt))
+    return out
+
+
+PREFILL_CASES = _draw_prefill(10, 2030)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,C,P,D,dt", PREFILL_CASES, ids=_ids(PREFILL_CASES))
+def test_random_prefill(da, B, Hq, Hkv, C, P, D, dt):
+    """Bars of test_gpu_prefill.py: 1e-4 absolute and 1e-4 of rms (each
+    probability enters the second product as two 16-bit terms)."""
+    import torch
+    c = synth.prefill_case([704, B, Hq, Hkv, C, P, D], B, Hq, Hkv, C, P, D, dt)
+    o = da.da_prefill_attention(to_dev(c.q, dt), to_dev(c.k, dt), to_dev(c.v, dt), scale=c.scale)
+    torch.cuda.synchronize()
+    ref = chunk_prefill_attention(as_f64(c.q, dt), as_f64(c.k, dt), as_f64(c.v, dt), c.scale, P)
+    assert_close(o.cpu().numpy(), ref, atol=1e-4, rel_rms=1e-4,
+                 what=f"prefill B{B} Hq{Hq} Hkv{Hkv} C{C} P{P} D{D} {dt}")
