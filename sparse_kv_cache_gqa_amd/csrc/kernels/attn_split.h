@@ -213,6 +213,13 @@ struct Stage {
     // with several query heads the lanes that use a token's pair fetch it
     // with a lane shuffle, with one head each lane scores its own token
     uint32_t mk, sk, mv, sv;
+    // uint4 with 2 or 4 query heads: the pairs of the tokens this lane
+    // scores (ts * 16 + lane mod 16), loaded directly instead of fetched
+    // with lane shuffles (measured on MI355X, uint4 K/V of 8 rows x 8 KV
+    // heads x 32768 tokens: G = 2 / 4 59.9-60.5 / 61.5-61.7 us against
+    // 62.1-62.2 / 61.9-62.6; 24 more VGPRs, so G = 8 keeps the shuffles)
+    static constexpr bool DM = C::I8S && G <= 4;
+    uint32_t mk4[DM ? C::TS : 1], sk4[DM ? C::TS : 1], mv4[DM ? C::TS : 1], sv4[DM ? C::TS : 1];
 };
 
 // In-workgroup merge of the n_split (<= waves) partials in `mrg` ([wave][G]
@@ -387,11 +394,22 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
                     st.V[ts][p] = buf_load16(vrs, (uint32_t)(t0 + ts * kSub + p * TPP + vtok) * R + vcol);
             }
             if constexpr (C::U4) {
+                if constexpr (St::DM) {
+#pragma unroll
+                    for (int ts = 0; ts < kTS; ++ts) {
+                        const uint32_t o4 = (uint32_t)(t0 + ts * kSub + n16) * NGRP * 2;
+                        st.mk4[ts] = buf_load4(kmrs, o4);
+                        st.sk4[ts] = buf_load4(ksrs, o4);
+                        st.mv4[ts] = buf_load4(vmrs, o4);
+                        st.sv4[ts] = buf_load4(vsrs, o4);
+                    }
+                } else {
                 const uint32_t off = (uint32_t)(t0 + lane % kTile) * NGRP * 2;
                 st.mk = buf_load4(kmrs, off);
                 st.sk = buf_load4(ksrs, off);
                 st.mv = buf_load4(vmrs, off);
                 st.sv = buf_load4(vsrs, off);
+                }
             }
             return;
         }
@@ -710,8 +728,14 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
           if constexpr (C::I8S) {
             // q . c per group, exact in int32 per digit, then
             // raw = sum_gr min sum(q) + scale (q . c)
-            const uint32_t kmn2 = __shfl(st.mk, ts * kSub + n16, 64);
-            const uint32_t ksc2 = __shfl(st.sk, ts * kSub + n16, 64);
+            uint32_t kmn2, ksc2;
+            if constexpr (St::DM) {
+                kmn2 = st.mk4[ts];
+                ksc2 = st.sk4[ts];
+            } else {
+                kmn2 = __shfl(st.mk, ts * kSub + n16, 64);
+                ksc2 = __shfl(st.sk, ts * kSub + n16, 64);
+            }
             float raw[HPL];
 #pragma unroll
             for (int hb = 0; hb < HPL; ++hb) raw[hb] = 0.f;
@@ -852,8 +876,13 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         if constexpr (PVM) {
 #pragma unroll
             for (int ts = 0; ts < kTS; ++ts) {
-                sv2[ts] = __shfl(st.sv, ts * kSub + n16, 64);
-                mv2[ts] = __shfl(st.mv, ts * kSub + n16, 64);
+                if constexpr (St::DM) {
+                    sv2[ts] = st.sv4[ts];
+                    mv2[ts] = st.mv4[ts];
+                } else {
+                    sv2[ts] = __shfl(st.sv, ts * kSub + n16, 64);
+                    mv2[ts] = __shfl(st.mv, ts * kSub + n16, 64);
+                }
             }
         }
 #pragma unroll
