@@ -41,8 +41,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(const float *__restric
     float M = neg_inf();
     if (live)
         for (int s = tid; s < n_split; s += nt) M = fmaxf(M, p[(int64_t)s * PSTR + D]);
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, shfl_xor(M, off));
+    M = xor_reduce<1, 64>(M, OpMax{});
     if ((tid & 63) == 0) red[wv] = M;
     __syncthreads();
     M = red[0];
@@ -58,8 +57,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(const float *__restric
             if (use_lds) w_lds[s] = f;
             L = fmaf(f, p[(int64_t)s * PSTR + D + 1], L);
         }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) L += shfl_xor(L, off);
+    L = xor_reduce<1, 64>(L, OpAdd{});
     if ((tid & 63) == 0) red[wv] = L;
     __syncthreads();
     L = red[0];

@@ -474,6 +474,11 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     if (ntok > 0) load_tile(sa, 0);
 
     // ---- A operand: query rows, split into MFMA-type terms -------------------
+    // Every lane issues every q load (a row or channel that holds no value
+    // reads head 0 and drops it): with no load behind a branch they all go
+    // out before the first wait, where conditional loads had cost one
+    // memory round trip each (measured on MI355X, see the uint4 one-head
+    // pass).
     u32x4 Aq[KF == FMT_F32 ? 1 : NMF];
     float Af[KF == FMT_F32 ? NMF : 1];
     {
@@ -485,14 +490,16 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         for (int mf = 0; mf < NMF; ++mf) {
             if constexpr (KF == FMT_F32) {
                 const int d = qk_dim<KF>(mf, g4, 0);
-                Af[mf] = rowok ? load_scalar<QF>(a.q, qoff + h * D + d) : 0.f;
+                const float v = load_scalar<QF>(a.q, qoff + (rowok ? h : 0) * D + d);
+                Af[mf] = rowok ? v : 0.f;
             } else {
                 uint32_t hv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int d = qk_dim<KF>(mf, g4, e);
-                    float x = 0.f;
-                    if (rowok && (!C::U4 || d / 64 == grp)) x = load_scalar<QF>(a.q, qoff + h * D + d);
+                    const bool ok = rowok && (!C::U4 || d / 64 == grp);
+                    const float v = load_scalar<QF>(a.q, qoff + (ok ? h : 0) * D + d);
+                    const float x = ok ? v : 0.f;
                     hv[e] = split_term<MT>(x, s);
                 }
 #pragma unroll
@@ -524,14 +531,13 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int ch = 64 * gr + 32 * (g4 & 1) + 16 * (g4 >> 1) + 8 * (j >> 3) + 2 * (j & 3) + ((j >> 2) & 1);
-                qv[j] = h < G ? load_scalar<QF>(a.q, qoff + h * D + ch) : 0.f;
+                const float v = load_scalar<QF>(a.q, qoff + (h < G ? h : 0) * D + ch);
+                qv[j] = h < G ? v : 0.f;
                 mx = fmaxf(mx, fabsf(qv[j]));
                 bad |= !(fabsf(qv[j]) <= 3.402823466e38f);
             }
-            mx = fmaxf(mx, shfl_xor(mx, 16));
-            mx = fmaxf(mx, shfl_xor(mx, 32));
-            bad |= shfl_xor(bad, 16);
-            bad |= shfl_xor(bad, 32);
+            mx = xor_reduce<16, 64>(mx, OpMax{});
+            bad = xor_reduce<16, 64>(bad, OpOr{});
             int ex;
             (void)frexpf(mx, &ex);
             const int e = 22 - ex;               // |q| 2^e < 2^22
@@ -575,8 +581,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
 #pragma unroll
             for (int gr = 0; gr < NGRP; ++gr) {
                 float x = load_scalar<QF>(a.q, qoff + h * D + gr * 64 + lane);
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) x += shfl_xor(x, o);
+                x = xor_reduce<1, 64>(x, OpAdd{});
                 if (SOLO || grp_of(h) == g4) qs[slot_of(h)][gr] = x;
             }
     }
@@ -827,10 +832,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
             float x = sc[0][hh];
 #pragma unroll
             for (int ts = 1; ts < kTS; ++ts) x = fmaxf(x, sc[ts][hh]);
-            x = fmaxf(x, shfl_xor(x, 1));
-            x = fmaxf(x, shfl_xor(x, 2));
-            x = fmaxf(x, shfl_xor(x, 4));
-            x = fmaxf(x, shfl_xor(x, 8));
+            x = xor_reduce<1, 16>(x, OpMax{});
             mt[hh] = x;
         }
         float alpha[G];
@@ -1074,8 +1076,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
 #pragma unroll
     for (int hh = 0; hh < HPL; ++hh) {
         float x = l_part[hh];
-#pragma unroll
-        for (int o = 1; o < (SOLO ? 32 : 16); o <<= 1) x += shfl_xor(x, o);
+        x = xor_reduce<1, SOLO ? 32 : 16>(x, OpAdd{});
         l_part[hh] = x;
     }
     // uint4: the minimum term of each (head, V group), for the lanes whose
@@ -1084,8 +1085,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     if constexpr (SOLO) {
         // per V group: lanes 0..31 sum group 0, lanes 32..63 group 1; the V
         // lanes of channel group vcol / 32 add it to their channels
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) am += shfl_xor(am, o);
+        am = xor_reduce<1, 32>(am, OpAdd{});
         amin[0] = __shfl(am, 32 * (vcol / 32), 64);
     } else if constexpr (PVM) {
 #pragma unroll
@@ -1093,8 +1093,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
                 float x = amg[hh][g];
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) x += shfl_xor(x, o);
+                x = xor_reduce<1, 16>(x, OpAdd{});
                 amg[hh][g] = x;
             }
 #pragma unroll
@@ -1108,12 +1107,9 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     }
     if constexpr (!PVM) {
 #pragma unroll
-        for (int mask = C::CH_LANES; mask < 64; mask <<= 1) {
+        for (int h = 0; h < G; ++h) {
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) acc[h][c] += shfl_xor(acc[h][c], mask);
-            }
+            for (int c = 0; c < CPL; ++c) acc[h][c] = xor_reduce<C::CH_LANES, 64>(acc[h][c], OpAdd{});
         }
     }
     // to the workspace, or to this wave's LDS slot [G][PSTR] for the merge

@@ -36,17 +36,65 @@ __device__ __forceinline__ float load_scalar(const void *p, int64_t i) {
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <typename T>
-__device__ __forceinline__ T shfl_xor(T v, int mask) {
-    return __shfl_xor(v, mask, 64);
-}
-
 // One data-parallel-primitive move: lane i takes `v` of the lane that the
 // row-local pattern CTRL names (VALU, no LDS round trip).
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
+// One butterfly step of a lane reduction on the VALU: op(x, x of lane
+// i ^ MASK) in every lane i, for a commutative op on a 32-bit value.
+// Masks 1, 2 and 8 are single row moves (quad_perm [1,0,3,2], [2,3,0,1],
+// row_ror:8); mask 4 is a mirror within 8 lanes followed by a reversal
+// within 4 (lane i ends with lane i ^ 4); masks 16 and 32 use
+// v_permlane16_swap / v_permlane32_swap of x with itself, whose two
+// outputs then hold, in every lane, x of the lane and of its partner, in
+// some order.  Each lane gets exactly op(x, __shfl_xor(x, MASK)), without
+// the LDS round trip of ds_bpermute.
+template <int MASK, typename T, typename Op>
+__device__ __forceinline__ T xor_step(T x, Op op) {
+    static_assert(sizeof(T) == 4, "32-bit lanes");
+    static_assert(MASK == 1 || MASK == 2 || MASK == 4 || MASK == 8 || MASK == 16 || MASK == 32, "lane mask");
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    if constexpr (MASK >= 16) {
+        const auto pr = MASK == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                                   : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return op(__builtin_bit_cast(T, (uint32_t)pr[0]), __builtin_bit_cast(T, (uint32_t)pr[1]));
+    } else {
+        int v = (int)u;
+        if constexpr (MASK == 1) v = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+        if constexpr (MASK == 2) v = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+        if constexpr (MASK == 4) {
+            v = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+            v = __builtin_amdgcn_mov_dpp(v, 0x1B, 0xF, 0xF, false);    // quad_perm [3,2,1,0]
+        }
+        if constexpr (MASK == 8) v = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);
+        return op(x, __builtin_bit_cast(T, v));
+    }
+}
+// Butterfly steps for masks FIRST, 2 FIRST, ... below END (powers of two).
+template <int FIRST, int END, typename T, typename Op>
+__device__ __forceinline__ T xor_reduce(T x, Op op) {
+    if constexpr (FIRST < END) {
+        x = xor_step<FIRST>(x, op);
+        return xor_reduce<2 * FIRST, END>(x, op);
+    } else {
+        return x;
+    }
+}
+struct OpAdd {
+    __device__ float operator()(float a, float b) const { return a + b; }
+};
+struct OpMax {
+    __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct OpMin {
+    __device__ float operator()(float a, float b) const { return fminf(a, b); }
+};
+struct OpOr {
+    __device__ int operator()(int a, int b) const { return a | b; }
+};
+
 // Maximum over the 16 lanes of each row, left in every lane of the row: swap
 // neighbours, swap pairs, mirror within 8 lanes, mirror within 16 lanes.
 // Maximum is exact, so the result equals that of any reduction order.

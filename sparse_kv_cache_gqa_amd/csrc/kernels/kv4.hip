@@ -35,11 +35,8 @@ __global__ __launch_bounds__(256) void quantize_kv4_kernel(int64_t n_groups, con
     float mn = f[0], mx = f[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) { mn = fminf(mn, f[e]); mx = fmaxf(mx, f[e]); }
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-        mn = fminf(mn, shfl_xor(mn, o));
-        mx = fmaxf(mx, shfl_xor(mx, o));
-    }
+    mn = xor_reduce<1, 8>(mn, OpMin{});
+    mx = xor_reduce<1, 8>(mx, OpMax{});
     const double dmn = (double)mn;
     const uint16_t s16 = f64_to_f16_rne(((double)mx - dmn) / 15.0);
     const double s = (double)f16_to_f32(s16);

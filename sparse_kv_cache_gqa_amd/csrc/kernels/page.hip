@@ -196,11 +196,8 @@ __device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t *buf, uint
 template <int NW, bool MAX>
 __device__ __forceinline__ float block_reduce(float x, float *buf) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const float y = __shfl_xor(x, o, 64);
-        x = MAX ? fmaxf(x, y) : x + y;
-    }
+    if constexpr (MAX) x = xor_reduce<1, 64>(x, OpMax{});
+    else x = xor_reduce<1, 64>(x, OpAdd{});
     if (lane == 0) buf[w] = x;
     __syncthreads();
     float r = buf[0];
@@ -272,9 +269,7 @@ __device__ __forceinline__ void attend_items(const SelArgs &args, int64_t bh, in
     }
     // sum the slots of each wave (lanes with the same chunk), then the waves
 #pragma unroll
-    for (int o = CH; o < 64; o <<= 1)
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+    for (int e = 0; e < EPC; ++e) acc[e] = xor_reduce<CH, 64>(acc[e], OpAdd{});
     const int lane = tid & 63, w = tid >> 6;
     if (lane < CH) {
 #pragma unroll
@@ -365,6 +360,8 @@ __global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args)
                     for (int e = 0; e < EPC; ++e) sn = fmaf(qn[e], fn[e], sn);
                 }
                 float s = EXACT ? sp : sp + sn;
+                // LDS lane shuffles in this VALU-heavy scan: the VALU
+                // butterfly measured slower here
 #pragma unroll
                 for (int o = 1; o < PCS; o <<= 1) s += __shfl_xor(s, o, 64);
                 const int64_t row = base + i * TPI + rin;
@@ -532,8 +529,7 @@ __global__ __launch_bounds__(sel_threads(MODE)) void select_kernel(SelArgs args)
                 float s = 0.f;
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) s = fmaf(qe[e], fx[e], s);
-#pragma unroll
-                for (int o = 1; o < PCS; o <<= 1) s += __shfl_xor(s, o, 64);
+                s = xor_reduce<1, PCS>(s, OpAdd{});
                 const int t = base + i * TPI + rin;
                 if (piece == 0 && t < T) tsc[t] = rr[i] >= 0 ? s : -__builtin_inff();
             }

@@ -291,8 +291,10 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) m = fmaxf(m, st[qb][kb][i]);
-            m = fmaxf(m, shfl_xor(m, 16));
-            mx[qb] = fmaxf(m, shfl_xor(m, 32));
+            // LDS lane shuffles here: this loop is bound by its VALU issue,
+            // and the VALU butterfly (permlane swaps) measured slower
+            m = fmaxf(m, __shfl_xor(m, 16, 64));
+            mx[qb] = fmaxf(m, __shfl_xor(m, 32, 64));
             up |= mx[qb] * sl2 > m_run[qb] + kLazy;
         }
         if (__builtin_amdgcn_ballot_w64(up) != 0) {
@@ -371,8 +373,8 @@ __global__ __launch_bounds__(pre_threads<QB>()) void prefill_kernel(PrefillArgs 
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         float l = l_run[qb];
-        l += shfl_xor(l, 16);
-        l += shfl_xor(l, 32);
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
         const int64_t qi = qw + 16 * qb + n;
         if (qi < a.C) {
             float *dst = a.o + (bh * a.C + qi) * D;
