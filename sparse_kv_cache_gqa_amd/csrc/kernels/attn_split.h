@@ -1105,7 +1105,36 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
                 if (h == 2 * g4 + 1) amr[1][g] = x;
             }
     }
-    if constexpr (!PVM) {
+    if constexpr (SOLO) {
+        // one-head uint4: lane l holds 32 channels 32 (l mod 4) + k summed
+        // over token slot l / 4; reduce over the slots as a reduce-scatter:
+        // at each step over lane bit b a lane keeps half of its values, adds
+        // its partner's copies of them and passes on the other half, so the
+        // lane ends with the two channels 32 (l mod 4) + 2 (l / 4) + {0, 1}
+        // (30 exchanges and 30 additions instead of 128 each)
+        float *v = acc[0];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {       // bit 5: keep j (bit clear) or j + 16
+            const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[j]), __float_as_uint(v[j + 16]), false, false);
+            v[j] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {        // bit 4: keep j or j + 8
+            const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[j]), __float_as_uint(v[j + 8]), false, false);
+            v[j] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+        }
+        const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {        // bit 3: keep j or j + 4
+            const float send = b3 ? v[j] : v[j + 4], keep = b3 ? v[j + 4] : v[j];
+            v[j] = keep + lane_xor<8>(send);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {        // bit 2: keep j or j + 2
+            const float send = b2 ? v[j] : v[j + 2], keep = b2 ? v[j + 2] : v[j];
+            v[j] = keep + lane_xor<4>(send);
+        }
+    } else if constexpr (!PVM) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -1141,6 +1170,9 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
                                  amr[a2][nb >> 2]);
                 }
             }
+        } else if constexpr (SOLO) {
+            const int ch = 32 * (lane & 3) + 2 * (lane >> 2);
+            *(float2 *)(dst0 + ch) = make_float2(acc[0][0] + amin[0], acc[0][1] + amin[0]);
         } else if (lane < C::CH_LANES) {
             const int c0 = KF == FMT_F32 ? vcol / 4 : (C::U4 ? vcol * 2 : vcol / 2);
 #pragma unroll

@@ -51,6 +51,21 @@ __device__ __forceinline__ float dpp_mov(float v) {
 // outputs then hold, in every lane, x of the lane and of its partner, in
 // some order.  Each lane gets exactly op(x, __shfl_xor(x, MASK)), without
 // the LDS round trip of ds_bpermute.
+// x of lane i ^ MASK, for MASK 1, 2, 4 or 8 (row moves, as in xor_step).
+template <int MASK>
+__device__ __forceinline__ float lane_xor(float x) {
+    static_assert(MASK == 1 || MASK == 2 || MASK == 4 || MASK == 8, "row-local lane mask");
+    int v = __float_as_int(x);
+    if constexpr (MASK == 1) v = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    if constexpr (MASK == 2) v = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    if constexpr (MASK == 4) {
+        v = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+        v = __builtin_amdgcn_mov_dpp(v, 0x1B, 0xF, 0xF, false);    // quad_perm [3,2,1,0]
+    }
+    if constexpr (MASK == 8) v = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);  // row_ror:8
+    return __int_as_float(v);
+}
+
 template <int MASK, typename T, typename Op>
 __device__ __forceinline__ T xor_step(T x, Op op) {
     static_assert(sizeof(T) == 4, "32-bit lanes");
@@ -61,15 +76,7 @@ __device__ __forceinline__ T xor_step(T x, Op op) {
                                    : __builtin_amdgcn_permlane32_swap(u, u, false, false);
         return op(__builtin_bit_cast(T, (uint32_t)pr[0]), __builtin_bit_cast(T, (uint32_t)pr[1]));
     } else {
-        int v = (int)u;
-        if constexpr (MASK == 1) v = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
-        if constexpr (MASK == 2) v = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
-        if constexpr (MASK == 4) {
-            v = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);   // row_half_mirror
-            v = __builtin_amdgcn_mov_dpp(v, 0x1B, 0xF, 0xF, false);    // quad_perm [3,2,1,0]
-        }
-        if constexpr (MASK == 8) v = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);
-        return op(x, __builtin_bit_cast(T, v));
+        return op(x, __builtin_bit_cast(T, __float_as_uint(lane_xor<MASK>(__uint_as_float(u)))));
     }
 }
 // Butterfly steps for masks FIRST, 2 FIRST, ... below END (powers of two).
