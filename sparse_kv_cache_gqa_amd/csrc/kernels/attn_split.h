@@ -115,6 +115,10 @@ struct Cfg {
     // the fp16 products, G = 2 unchanged at 61.9; the codes need 3 VALU
     // instructions per 8 instead of 9)
     static constexpr bool I8S = U4 && G > 1;
+    // minimum waves per SIMD the register allocation must leave room for:
+    // four for the one-head uint4 layout (its 3584-wave grid at the FlexGen
+    // shape then runs in one round), no constraint otherwise
+    static constexpr int WPE = (U4 && G == 1) ? 4 : 1;
     // 16 MFMA rows must hold every (head, group, split term); rows fit 64..1024 bytes
     static constexpr bool ok = RPH0 <= 4 && G * RPH <= 16 && R >= 64 && R <= 1024;
 };
@@ -263,7 +267,7 @@ __device__ __forceinline__ void merge_in_workgroup(const AttnLaunch &a, const fl
 // query head.  Loads of the next tile are issued before the current tile is
 // computed (two register stages).
 template <int KF, int QF, int D, int G, bool PAGED>
-__global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(AttnLaunch a) {
+__global__ __launch_bounds__(64 * kMaxWavesPerBlock) __attribute__((amdgpu_waves_per_eu(Cfg<KF, QF, D, G>::WPE))) void attn_split_kernel(AttnLaunch a) {
     using C = Cfg<KF, QF, D, G>;
     static_assert(C::ok, "unsupported layout");
     static_assert(!(PAGED && C::U4), "no paged uint4 cache");
@@ -431,9 +435,15 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         }
     };
 
-    // The two halves of load_tile (fp32 / fp16 / bf16 caches): the keys of a
+    // The two halves of load_tile (fp16 / bf16 caches, and uint4 with one
+    // query head, with the minima and scales of each side): the keys of a
     // tile, which the scores consume first, and its values.
     auto load_k = [&](St &st, int t0) {
+        if constexpr (SOLO && !PAGED) {
+            const uint32_t off = (uint32_t)(t0 + lane % kTile) * NGRP * 2;
+            st.mk = buf_load4(kmrs, off);
+            st.sk = buf_load4(ksrs, off);
+        }
 #pragma unroll
         for (int ts = 0; ts < kTS; ++ts) {
             if constexpr (!PAGED) {
@@ -454,6 +464,11 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         }
     };
     auto load_v = [&](St &st, int t0) {
+        if constexpr (SOLO && !PAGED) {
+            const uint32_t off = (uint32_t)(t0 + lane % kTile) * NGRP * 2;
+            st.mv = buf_load4(vmrs, off);
+            st.sv = buf_load4(vsrs, off);
+        }
 #pragma unroll
         for (int ts = 0; ts < kTS; ++ts) {
 #pragma unroll
@@ -968,7 +983,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
     // am: sum of p * (V group minimum) over this lane's tokens, for V group
     // lane / 32 (lanes 32..63 repeat the tokens of lanes 0..31)
     float am = 0.f;
-    auto compute_tile_solo = [&](St &st) {
+    auto compute_tile_solo = [&](St &st, auto &&after_scores) {
         f32x4 cc[kTS];
 #pragma unroll
         for (int ts = 0; ts < kTS; ++ts) {
@@ -991,6 +1006,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
             raw += mn * qs[0][gr] + (16.f * sg) * (dot - qs[0][gr]);
         }
         const float sc = (odd ? st.kok[1] : st.kok[0]) ? raw * sl2 : neg_inf();
+        after_scores();
         const float rmax = row16_max(sc);
         const float mn = fmaxf(m_run[0], fmaxf(readlane_f(rmax, 0), readlane_f(rmax, 16)));
         if (mn != m_run[0]) {
@@ -1029,17 +1045,20 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         }
     };
     auto compute = [&](St &st) {
-        if constexpr (SOLO) compute_tile_solo(st);
+        if constexpr (SOLO) compute_tile_solo(st, [] {});
         else compute_tile(st, [] {});
     };
 
     // ---- main loop: two register stages -------------------------------------
     // Early refill (below) on dense fp16 / bf16 caches with up to 4 query
     // heads per KV head (measured on MI355X: the Llama-3-8B step about 0.5%
+    // faster) and in the one-head uint4 layout (the key codes and their
+    // minima and scales refilled after the scores, the value side after the
+    // P.V; 128 VGPRs at four waves per SIMD; the FlexGen step about 1.2 us
     // faster).  Elsewhere it needed more registers than the file holds
     // (spills, AGPR copies), cost occupancy, or measured slower (the paged
     // gather, uint4 with grouped query heads).
-    constexpr bool EARLYK = !C::U4 && !PAGED && KF != FMT_F32 && G <= 4;
+    constexpr bool EARLYK = (!C::U4 && !PAGED && KF != FMT_F32 && G <= 4) || (SOLO && !PAGED);
     if constexpr (!EARLYK) {
         for (int t0 = 0; t0 < ntok; t0 += 2 * kTile) {
             const bool more = t0 + kTile < ntok;
@@ -1056,14 +1075,18 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) void attn_split_kernel(Attn
         if (kTile < ntok) load_tile(sb, kTile);
         for (int t0 = 0; t0 < ntok; t0 += 2 * kTile) {
             const int n2 = t0 + 2 * kTile, n3 = t0 + 3 * kTile;
-            compute_tile(sa, [&] {
+            auto hook_a = [&] {
                 if (n2 < ntok) load_k(sa, n2);
-            });
+            };
+            if constexpr (SOLO) compute_tile_solo(sa, hook_a);
+            else compute_tile(sa, hook_a);
             if (n2 < ntok) load_v(sa, n2);
             if (t0 + kTile >= ntok) break;
-            compute_tile(sb, [&] {
+            auto hook_b = [&] {
                 if (n3 < ntok) load_k(sb, n3);
-            });
+            };
+            if constexpr (SOLO) compute_tile_solo(sb, hook_b);
+            else compute_tile(sb, hook_b);
             if (n3 < ntok) load_v(sb, n3);
         }
     }
