@@ -435,10 +435,18 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) __attribute__((amdgpu_waves
         }
     };
 
-    // The two halves of load_tile (fp16 / bf16 caches, and uint4 with one
-    // query head, with the minima and scales of each side): the keys of a
-    // tile, which the scores consume first, and its values.
+    // The two halves of load_tile (fp16 / bf16 caches, and uint4 with up to
+    // 4 query heads per KV head, with the minima and scales of each side):
+    // the keys of a tile, which the scores consume first, and its values.
     auto load_k = [&](St &st, int t0) {
+        if constexpr (St::DM && !PAGED) {
+#pragma unroll
+            for (int ts = 0; ts < kTS; ++ts) {
+                const uint32_t o4 = (uint32_t)(t0 + ts * kSub + n16) * NGRP * 2;
+                st.mk4[ts] = buf_load4(kmrs, o4);
+                st.sk4[ts] = buf_load4(ksrs, o4);
+            }
+        }
         if constexpr (SOLO && !PAGED) {
             const uint32_t off = (uint32_t)(t0 + lane % kTile) * NGRP * 2;
             st.mk = buf_load4(kmrs, off);
@@ -464,6 +472,14 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) __attribute__((amdgpu_waves
         }
     };
     auto load_v = [&](St &st, int t0) {
+        if constexpr (St::DM && !PAGED) {
+#pragma unroll
+            for (int ts = 0; ts < kTS; ++ts) {
+                const uint32_t o4 = (uint32_t)(t0 + ts * kSub + n16) * NGRP * 2;
+                st.mv4[ts] = buf_load4(vmrs, o4);
+                st.sv4[ts] = buf_load4(vsrs, o4);
+            }
+        }
         if constexpr (SOLO && !PAGED) {
             const uint32_t off = (uint32_t)(t0 + lane % kTile) * NGRP * 2;
             st.mv = buf_load4(vmrs, off);
@@ -1052,13 +1068,15 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) __attribute__((amdgpu_waves
     // ---- main loop: two register stages -------------------------------------
     // Early refill (below) on dense fp16 / bf16 caches with up to 4 query
     // heads per KV head (measured on MI355X: the Llama-3-8B step about 0.5%
-    // faster) and in the one-head uint4 layout (the key codes and their
-    // minima and scales refilled after the scores, the value side after the
-    // P.V; 128 VGPRs at four waves per SIMD; the FlexGen step about 1.2 us
-    // faster).  Elsewhere it needed more registers than the file holds
-    // (spills, AGPR copies), cost occupancy, or measured slower (the paged
-    // gather, uint4 with grouped query heads).
-    constexpr bool EARLYK = (!C::U4 && !PAGED && KF != FMT_F32 && G <= 4) || (SOLO && !PAGED);
+    // faster), in the one-head uint4 layout (the key codes and their minima
+    // and scales refilled after the scores, the value side after the P.V;
+    // 128 VGPRs at four waves per SIMD; the FlexGen step about 1.2 us
+    // faster) and for uint4 with 2 or 4 query heads per KV head (each lane's
+    // own metadata words; 8 x 8 KV heads x 32768 tokens: G = 4 61.6 -> 58.4
+    // us, G = 2 58.9 -> 57.4 us).  Elsewhere it needed more registers than
+    // the file holds (spills, AGPR copies), cost occupancy, or measured
+    // slower (the paged gather; uint4 with 8 query heads, 72.6 -> 74.4 us).
+    constexpr bool EARLYK = (!C::U4 && !PAGED && KF != FMT_F32 && G <= 4) || (SOLO && !PAGED) || (St::DM && !PAGED);
     if constexpr (!EARLYK) {
         for (int t0 = 0; t0 < ntok; t0 += 2 * kTile) {
             const bool more = t0 + kTile < ntok;
