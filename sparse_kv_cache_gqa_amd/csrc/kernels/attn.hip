@@ -213,10 +213,10 @@ struct SplitKernel {
     explicit operator bool() const { return fn != nullptr; }
 };
 
-template <int KF, int QF, int D, int G, bool PAGED>
+template <int KF, int QF, int D, int G, bool PAGED, int SV = 0>
 SplitKernel pick_one() {
     using C = Cfg<KF, QF, D, G>;
-    if constexpr (C::ok) return {attn_split_kernel<KF, QF, D, G, PAGED>};
+    if constexpr (C::ok) return {attn_split_kernel<KF, QF, D, G, PAGED, SV>};
     else return {};
 }
 
@@ -242,7 +242,9 @@ SplitKernel pick_d(int D, int G) {
     return {};
 }
 
-SplitKernel pick(int kv, int qf, int D, int G, bool paged) {
+// `waves`: the launch's wave count (0 when only asking whether a kernel
+// exists); it picks between the two one-head uint4 forms.
+SplitKernel pick(int kv, int qf, int D, int G, bool paged, int64_t waves = 0) {
     if (paged) {
         if (G != 1) return {};
         switch (kv) {
@@ -273,8 +275,16 @@ SplitKernel pick(int kv, int qf, int D, int G, bool paged) {
         // grouped query heads: attn_u4.hip
         if (G != 1) return {pick_split_u4(qf, D, G)};
         if (D != 128) return {};
-        if (qf == FMT_F16) return pick_one<FMT_U4, FMT_F16, 128, 1, false>();
-        if (qf == FMT_F32) return pick_one<FMT_U4, FMT_F32, 128, 1, false>();
+        {
+            // int8 score products for grids of three or more waves per SIMD
+            // (MI355X: 256 CUs x 4 SIMDs), where more waves cover their
+            // longer chain; fp16 products below that
+            const bool q8 = waves >= 3 * 1024;
+            if (qf == FMT_F16) return q8 ? pick_one<FMT_U4, FMT_F16, 128, 1, false, 1>()
+                                         : pick_one<FMT_U4, FMT_F16, 128, 1, false>();
+            if (qf == FMT_F32) return q8 ? pick_one<FMT_U4, FMT_F32, 128, 1, false, 1>()
+                                         : pick_one<FMT_U4, FMT_F32, 128, 1, false>();
+        }
         return {};
     default: return {};
     }
@@ -350,7 +360,7 @@ bool attn_supported(int kv_fmt, int q_fmt, int D, int G, bool paged) {
 
 hipError_t launch_split(const AttnLaunch &a, hipStream_t stream) {
     const bool paged = a.page_idx != nullptr;
-    const SplitKernel k = pick(a.kv_fmt, a.q_fmt, a.D, a.G, paged);
+    const SplitKernel k = pick(a.kv_fmt, a.q_fmt, a.D, a.G, paged, (int64_t)a.B * a.Hkv * a.n_split);
     if (!k) return hipErrorInvalidValue;
     if (a.wpb < 1 || a.wpb > kMaxWavesPerBlock || a.n_split < 1) return hipErrorInvalidValue;
     if (a.fused && a.n_split > a.wpb) return hipErrorInvalidValue;

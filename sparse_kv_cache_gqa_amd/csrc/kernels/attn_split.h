@@ -265,8 +265,9 @@ __device__ __forceinline__ void merge_in_workgroup(const AttnLaunch &a, const fl
 
 // Each wave reduces one split of one (batch row, KV head) to a partial per
 // query head.  Loads of the next tile are issued before the current tile is
-// computed (two register stages).
-template <int KF, int QF, int D, int G, bool PAGED>
+// computed (two register stages).  SV = 1 selects int8 score products for the
+// one-head uint4 layout (see compute_tile_solo); 0 everywhere else.
+template <int KF, int QF, int D, int G, bool PAGED, int SV = 0>
 __global__ __launch_bounds__(64 * kMaxWavesPerBlock) __attribute__((amdgpu_waves_per_eu(Cfg<KF, QF, D, G>::WPE))) void attn_split_kernel(AttnLaunch a) {
     using C = Cfg<KF, QF, D, G>;
     static_assert(C::ok, "unsupported layout");
@@ -283,6 +284,8 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) __attribute__((amdgpu_waves
     // holds stage token l mod 32, whose metadata it loaded itself
     constexpr bool SOLO = C::U4 && G == 1;
     static_assert(!SOLO || (kTS == 2 && kTile == 32), "one-head uint4 layout");
+    constexpr bool SOLO8 = SOLO && SV == 1;      // one head, int8 score products
+    static_assert(SV == 0 || SOLO, "int8 one-head scores are a one-head uint4 form");
 
     // uint4 with grouped query heads: P.V runs on the matrix cores (see
     // pv_store and pv_mma below); with one query head per KV head it stays on
@@ -548,12 +551,15 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) __attribute__((amdgpu_waves
     // base = 0, 32, 16, 48 for g4 = 0..3: the order in which a dword of
     // codes splits into its low and high nibbles.  The rounding of q to 22
     // bits of its group's largest value is below fp32 accumulation error.
-    u32x4 Aq8[C::I8S ? 2 : 1][C::I8S ? HPL : 1];
-    float ek[C::I8S ? 2 : 1][C::I8S ? HPL : 1][3];
-    if constexpr (C::I8S) {
+    // (one-head layout with SOLO8: head 0's digits in all four row blocks)
+    constexpr bool Q8 = C::I8S || SOLO8;
+    constexpr int NB8 = C::I8S ? HPL : 1;
+    u32x4 Aq8[Q8 ? 2 : 1][NB8];
+    float ek[Q8 ? 2 : 1][NB8][3];
+    if constexpr (Q8) {
 #pragma unroll
-        for (int hb = 0; hb < HPL; ++hb) {
-        const int m = n16, h = 4 * hb + (m >> 2), t = m & 3;
+        for (int hb = 0; hb < NB8; ++hb) {
+        const int m = n16, h = SOLO ? 0 : 4 * hb + (m >> 2), t = m & 3;
 #pragma unroll
         for (int gr = 0; gr < 2; ++gr) {
             float qv[16];
@@ -590,8 +596,8 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) __attribute__((amdgpu_waves
             // the score lanes of head hd(g4, hb) take its exponent from row 4 g4;
             // a group holding a NaN or an infinity gets NaN scales, so that
             // head's scores and output are NaN, as the arithmetic would give
-            const int es = __shfl(e, 4 * g4, 64);
-            const int bs = __shfl(bad, 4 * g4, 64);
+            const int es = SOLO ? e : __shfl(e, 4 * g4, 64);
+            const int bs = SOLO ? bad : __shfl(bad, 4 * g4, 64);
             const float sc = bs ? __builtin_nanf("") : ldexpf(1.f, -es);
             ek[gr][hb][0] = 65536.f * sc;
             ek[gr][hb][1] = 256.f * sc;
@@ -1000,6 +1006,46 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) __attribute__((amdgpu_waves
     // lane / 32 (lanes 32..63 repeat the tokens of lanes 0..31)
     float am = 0.f;
     auto compute_tile_solo = [&](St &st, auto &&after_scores) {
+        const bool odd = (g4 & 1) != 0;          // this lane group's sub-tile
+        float raw = 0.f;
+        if constexpr (SOLO8) {
+            // int8 products as with grouped heads (the A rows repeat head 0's
+            // three digits four times, so every lane group receives them):
+            // fewer VALU instructions and products, a longer chain per stage
+            // (measured on MI355X: 86.1 against 86.9 us at the FlexGen shape,
+            // 3584 waves; 56.5 against 55.0 us with 8 rows x 8 KV heads x
+            // 32768 tokens, 2048 waves); the host picks it for grids of three
+            // or more waves per SIMD
+            uint32_t kw[kTS][4];
+#pragma unroll
+            for (int ts = 0; ts < kTS; ++ts) {
+                const auto s0 = __builtin_amdgcn_permlane32_swap(st.K[ts][0][0], st.K[ts][0][2], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(st.K[ts][0][1], st.K[ts][0][3], false, false);
+                kw[ts][0] = s0[0];
+                kw[ts][1] = s1[0];
+                kw[ts][2] = s0[1];
+                kw[ts][3] = s1[1];
+            }
+#pragma unroll
+            for (int gr = 0; gr < NGRP; ++gr) {
+                i32x4v tt[kTS];
+#pragma unroll
+                for (int ts = 0; ts < kTS; ++ts) {
+                    const uint32_t x0 = kw[ts][2 * gr], x1 = kw[ts][2 * gr + 1];
+                    const u32x4 bv = {x0 & 0x0F0F0F0Fu, (x0 >> 4) & 0x0F0F0F0Fu, x1 & 0x0F0F0F0Fu, (x1 >> 4) & 0x0F0F0F0Fu};
+                    const i32x4v z = {0, 0, 0, 0};
+                    tt[ts] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4v, Aq8[gr][0]),
+                                                                   __builtin_bit_cast(i32x4v, bv), z, 0, 0, 0);
+                }
+                const int d0 = odd ? tt[1][0] : tt[0][0];
+                const int d1 = odd ? tt[1][1] : tt[0][1];
+                const int d2 = odd ? tt[1][2] : tt[0][2];
+                const float dq = fmaf((float)d0, ek[gr][0][0], fmaf((float)d1, ek[gr][0][1], (float)d2 * ek[gr][0][2]));
+                const float mn = f16_to_f32((st.mk >> (16 * gr)) & 0xFFFFu);
+                const float sg = f16_to_f32((st.sk >> (16 * gr)) & 0xFFFFu);
+                raw += fmaf(mn, qs[0][gr], sg * dq);
+            }
+        } else {
         f32x4 cc[kTS];
 #pragma unroll
         for (int ts = 0; ts < kTS; ++ts) {
@@ -1010,8 +1056,6 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) __attribute__((amdgpu_waves
                                                                 __builtin_bit_cast(f16x8, u4_to_f16x8(st.K[ts][0][u])),
                                                                 cc[ts], 0, 0, 0);
         }
-        const bool odd = (g4 & 1) != 0;          // this lane group's sub-tile
-        float raw = 0.f;
 #pragma unroll
         for (int gr = 0; gr < NGRP; ++gr) {
             float dot = 0.f;
@@ -1020,6 +1064,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerBlock) __attribute__((amdgpu_waves
             const float mn = f16_to_f32((st.mk >> (16 * gr)) & 0xFFFFu);
             const float sg = f16_to_f32((st.sk >> (16 * gr)) & 0xFFFFu);
             raw += mn * qs[0][gr] + (16.f * sg) * (dot - qs[0][gr]);
+        }
         }
         const float sc = (odd ? st.kok[1] : st.kok[0]) ? raw * sl2 : neg_inf();
         after_scores();

@@ -112,6 +112,10 @@ KV4_CASES = [
     (3, 5, 5, 333, "f16", 512),       # one ragged split per head, written without a merge
     (2, 3, 3, 45, "f32", 1024),       # one split shorter than a stage
     (1, 2, 2, 1, "f16", 0),           # a single token: o = its dequantized value row
+    # grids of 3072 or more waves take the int8 score products of the one-head layout
+    (32, 96, 96, 77, "f16", 0),       # 3072 waves, one ragged split each
+    (16, 200, 200, 300, "f32", 0),    # 3200 waves, fp32 q
+    (4, 128, 128, 5000, "f16", 512),  # 5120 waves: 10 splits per head and the merge
     # grouped query heads (P.V on the matrix cores)
     (2, 16, 2, 700, "f16", 0),        # G = 8, several splits and the merge kernel
     (3, 12, 3, 333, "f32", 512),      # G = 4, fp32 q, one ragged split per head
