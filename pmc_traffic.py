@@ -25,11 +25,11 @@ import sys
 PKG = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_kv_cache_gqa_amd")
 COPY_KIB = 512 * 1024          # one calibration copy reads and writes 512 MiB
 KERNELS = {                    # short name -> substring of the mangled kernel name
-    "attn_split_llama3_8b_32k": "attn_split_kernel<2, 0, 128, 4, false>",
+    "attn_split_llama3_8b_32k": "attn_split_kernel<2, 0, 128, 4, false, 0>",
     "select_tinyserve_32k": "select_kernel<1, 1, 64, 0>",
     "page_attention_tinyserve_32k": "select_kernel<1, 1, 64, 3>",
-    "attn_split_paged_tinyserve_32k": "attn_split_kernel<1, 1, 64, 1, true>",
-    "attn_split_uint4_flexgen": "attn_split_kernel<3, 1, 128, 1, false>",
+    "attn_split_paged_tinyserve_32k": "attn_split_kernel<1, 1, 64, 1, true, 0>",
+    "attn_split_uint4_flexgen": "attn_split_kernel<3, 1, 128, 1, false, 1>",
     "topk_attention_flexgen": "select_kernel<1, 1, 128, 2>",
     "select_tokens_flexgen": "select_kernel<1, 1, 128, 1>",
     "attn_reduce": "attn_reduce_kernel",
