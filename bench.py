@@ -102,13 +102,16 @@ def capture(torch, fn, n: int = 2):
 
 
 def graph_size(steps: int) -> int:
-    """Steps captured per HIP graph: the largest even divisor of `steps` up to
-    10, so exactly `steps` steps are timed (2 when none divides it).  A
-    serving loop captures a whole decode step, many kernels, in one graph;
-    with only 2 steps per graph each step also carries half a graph launch
-    (measured on MI355X: the Llama-3-8B step 169.7 / 167.6 / 166.7 /
-    166.2-166.9 us at 1 / 2 / 4 / 8 steps per graph)."""
-    return next((d for d in (10, 8, 6, 4, 2) if steps % d == 0), 2)
+    """Steps captured per HIP graph, a divisor of `steps` so that exactly
+    `steps` steps are timed: the largest even one up to 10 (steps alternate
+    between two KV copies, so consecutive replays keep alternating), else the
+    largest odd one up to 9.  A serving loop captures a whole decode step,
+    many kernels, in one graph; with only 2 steps per graph each step also
+    carries half a graph launch (measured on MI355X: the Llama-3-8B step
+    169.7 / 167.6 / 166.7 / 166.2-166.9 us at 1 / 2 / 4 / 8 steps per
+    graph)."""
+    even = next((d for d in (10, 8, 6, 4, 2) if steps % d == 0), 0)
+    return even or max(d for d in range(1, 10) if steps % d == 0)
 
 
 def time_graph(torch, fn, steps: int, warmup: int, per_graph: int = 0) -> float:
