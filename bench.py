@@ -263,7 +263,7 @@ def bench_dense(args, torch, np, da, synth):
         "step_bytes": step_bytes, "partial_ms": ms_partial, "partial_bytes": part_bytes,
         "partial_gbs": part_gbs, "partial_isolated_ms": ms_partial_isolated,
         "eager_in_step_ms_per_step": ms_in_step, "merge_ms": ms_merge, "n_split": ns,
-        "eager_ms_per_step": ms_eager, "launch": "eager" if args.no_graph else "hip-graph, 2 steps per replay",
+        "eager_ms_per_step": ms_eager, "launch": "eager" if args.no_graph else f"hip-graph, {graph_size(args.steps)} steps per replay",
         "measured_read_peak_gbs": read_gbs,
     }
     log(f"dense: {ms * 1e3:.1f} us/step (eager {ms_eager * 1e3:.1f}), {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s); "
